@@ -1,0 +1,189 @@
+/*
+ * mgs.h -- C ABI of the MI355X (gfx950) library for the fused MoE expert-MLP hot path:
+ * per-row scaled activation + grouped block quantization (MXFP8 / NVFP4) + grouped MX GEMM.
+ *
+ * Sources (web pages the method is described on):
+ *   [P1] "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU" (TransformerEngine PR 3473)
+ *   [P2] "Activation + GroupedLinear Fusion for MOE" (TransformerEngine PR 3238)
+ *   [P3] "[PyTorch] Preserve FP8 recompute state for inner autocast" (TransformerEngine PR 3284)
+ *
+ * General conventions (all entry points):
+ *   - Every pointer argument named *_bf16, probs, dprobs, group_amax, data, scales, group_scale, c and
+ *     bias is a DEVICE pointer; mgs_groups.split_sizes and the mgs_* structs themselves are HOST memory.
+ *   - The caller owns every buffer.  The library allocates no memory and keeps no state between calls.
+ *   - Every call validates its arguments on the host, then enqueues its kernels on `stream` (a
+ *     hipStream_t; NULL = the null stream) and returns without synchronizing.
+ *   - A NULL output pointer (or an mgs_qbuf with data == NULL) means "not requested": it is not computed.
+ *   - Return value: MGS_OK (0) or a negative MGS_ERR_* code; nothing is enqueued when validation
+ *     fails.  mgs_last_error() returns a thread-local message describing the last failure.
+ *   - Row groups: `groups->split_sizes[g]` rows belong to group (expert) g, stored contiguously in
+ *     group order ([P2] sequence diagram: split_sizes).  M = sum of split sizes.
+ *   - Quantized widths (the quantized, contiguous dimension) must be multiples of 32.
+ *   - Arithmetic follows IEEE FP32 with round-to-nearest-even; results are deterministic (no float
+ *     atomics, fixed reduction orders).
+ *
+ * Quantized tensor layouts (mgs_qbuf), for a logical [M x W] tensor quantized along W:
+ *   MXFP8 (E4M3 elements, E8M0 scale per 32):
+ *     rowwise : data u8 [M, W]                      scales u8 [M, W/32]
+ *     colwise : group g at data + W*coff[g]:        data [W, mp_g]   (tokens contiguous)
+ *               group g at scales + W*coff[g]/32:   scales [W, mp_g/32]
+ *   NVFP4 (E2M1 elements two per byte, element 2i in the low nibble; E4M3 scale per 16; FP32 per group):
+ *     rowwise : data u8 [M, W/2]                    scales u8 [M, W/16]   group_scale f32 [E]
+ *     colwise : group g at data + W*coff[g]/2:      data [W, mp_g/2]
+ *               group g at scales + W*coff[g]/16:   scales [W, mp_g/16]   group_scale f32 [E]
+ *   where mp_g = roundup(m_g, 32) and coff[g] = sum_{h<g} mp_h; padding tokens are written as zeros.
+ *   MXFP8 scale of a block with maximum magnitude amax: E8M0 code clamp(floor(log2 amax) - 8 + 127, 0, 254)
+ *   (0 for an all-zero block), element = E4M3(y / 2^(code-127)) rounded to nearest-even, saturated at 448.
+ *   NVFP4 (per group g, FP32): S_enc = 2688 / amax_g (1 if amax_g == 0, FLT_MAX on overflow);
+ *   block scale s_b = E4M3((amax_b / 6) * S_enc); element = E2M1(y * (S_enc / s_b)) (0 if s_b == 0);
+ *   group_scale[g] = S_dec = 1 / S_enc; dequantized value = e2m1 * s_b * S_dec.
+ */
+#ifndef MGS_H
+#define MGS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MGS_ABI_VERSION 1
+#define MGS_MAX_GROUPS 256
+
+enum mgs_status {
+  MGS_OK = 0,
+  MGS_ERR_INVALID_ARG = -1, /* NULL required pointer, unknown enum value, bad group count      */
+  MGS_ERR_SHAPE = -2,       /* width not a multiple of 32, negative split, split sum mismatch   */
+  MGS_ERR_UNSUPPORTED = -3, /* a valid but unsupported combination (e.g. NVFP4 recompute
+                               without the forward's group amax)                                 */
+  MGS_ERR_HIP = -4          /* a HIP launch error                                                */
+};
+
+/* Activation kinds.  [P2] Greptile summary (first bullet) and Important Files Changed
+ * (csrc/extensions/activation.cpp): scaled SwiGLU, clamped SwiGLU and SReLU; [P1] title:
+ * ScaledTanhSReLU.  With x the BF16 FC1 output row and p the row's routing probability:
+ *   IDENTITY        a = x                                       (plain grouped quantize)
+ *   SRELU           a = relu(x)^2
+ *   TANH_SRELU      a = (s * tanh(relu(x) / s))^2               (bounded at s^2, [P1] reviewer comment)
+ *   SWIGLU          x = [gate | up], a = silu(gate) * up        (output width = width_in / 2)
+ *   CLAMPED_SWIGLU  g = min(gate, limit), u = clamp(up, -limit, limit), a = g * sigmoid(alpha g) * (u + beta)
+ * and the forward output is y = a * p, kept in FP32 until it is quantized. */
+typedef enum {
+  MGS_ACT_IDENTITY = 0,
+  MGS_ACT_SRELU = 1,
+  MGS_ACT_TANH_SRELU = 2,
+  MGS_ACT_SWIGLU = 3,
+  MGS_ACT_CLAMPED_SWIGLU = 4
+} mgs_act_kind;
+
+typedef enum { MGS_FMT_MXFP8 = 0, MGS_FMT_NVFP4 = 1 } mgs_fmt;
+
+typedef enum { MGS_DTYPE_BF16 = 0, MGS_DTYPE_F32 = 1 } mgs_dtype;
+
+typedef enum {
+  MGS_GEMM_FPROP = 0, /* grouped over M: C[M x N] = A[M x K] . B_g^T, B = [E x N x K]          */
+  MGS_GEMM_DGRAD = 1, /* same contraction as FPROP; B is the columnwise copy of the weight     */
+  MGS_GEMM_WGRAD = 2  /* grouped over K: C_g[Mc x N] = A_g[Mc x mp_g] . B_g[N x mp_g]^T          */
+} mgs_gemm_mode;
+
+typedef enum { MGS_NBYTES_DATA = 0, MGS_NBYTES_SCALES = 1, MGS_NBYTES_GROUP_SCALE = 2 } mgs_nbytes_which;
+
+typedef struct {
+  int32_t kind;  /* mgs_act_kind */
+  float s;       /* TANH_SRELU bound parameter (> 0) */
+  float limit;   /* CLAMPED_SWIGLU clamp (> 0) */
+  float alpha;   /* CLAMPED_SWIGLU sigmoid slope (default 1) */
+  float beta;    /* CLAMPED_SWIGLU up-projection offset (default 0) */
+} mgs_act_params;
+
+typedef struct {
+  int32_t num_groups;         /* 1 .. MGS_MAX_GROUPS */
+  const int64_t* split_sizes; /* host array [num_groups], each >= 0 */
+} mgs_groups;
+
+/* One orientation (rowwise or columnwise) of a grouped quantized tensor; see the layouts above. */
+typedef struct {
+  void* data;
+  void* scales;
+  float* group_scale; /* NVFP4 only: S_dec per group [E]; ignored for MXFP8 */
+} mgs_qbuf;
+
+/* Library ABI version (MGS_ABI_VERSION). */
+int mgs_abi_version(void);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* mgs_last_error(void);
+
+/* Byte size of one buffer of a grouped quantized tensor of width `width`:
+ * which = DATA, SCALES or GROUP_SCALE (4 * E for NVFP4, 0 for MXFP8).  Negative MGS_ERR_* on error. */
+int64_t mgs_qtensor_nbytes(int32_t fmt, int32_t colwise, const mgs_groups* groups, int64_t width,
+                           int32_t which);
+
+/* Fused forward: y = act(x) * p, quantized rowwise and/or columnwise in one pass over x.
+ * [P2] Greptile summary, first bullet ("fuse per-row scale multiplication with activation and grouped
+ * quantization into one pass") and sequence diagram (grouped_scaled_{swiglu,srelu}(x, scales,
+ * quantizer, split_sizes) -> grouped_x).
+ *   x_bf16     [M x width_in] BF16, row-major (required)
+ *   probs      [M] FP32 per-row scale; NULL means 1 for every row
+ *   out_row    rowwise qtensor of y [M x W_a] (W_a = width_in, or width_in/2 for gated kinds); nullable
+ *   out_col    columnwise qtensor of y; nullable (NULL in the recompute forward, [P1] Description)
+ *   group_amax [E] FP32: NVFP4 only, required there; receives max|y| per group (the per-tensor
+ *              amax of each expert slice) and must be kept for a later recompute.  Ignored for MXFP8.
+ * NVFP4 runs two passes over x (group amax, then quantize). */
+int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                               int64_t width_in, const void* x_bf16, const float* probs,
+                               const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
+                               void* stream);
+
+/* Fused backward.  [P2] sequence diagram, backward half: grouped_scaled_d{swiglu,srelu}(grad, input_,
+ * scales, quantizer) -> (grouped_dy, dense_dy, grad_scales), where grad = dL/d(act_out * scales);
+ * [P1] Description: activation recompute regenerates FC2's input from the saved BF16 FC1 output.
+ *   x_bf16        [M x width_in] BF16 saved FC1 output (required)
+ *   dy_bf16       [M x W_a] BF16 dL/d(a * p) (required)
+ *   probs         [M] FP32; NULL means 1
+ *   dx_bf16       [M x width_in] BF16 dense dL/dx = dy * p * a'(x); nullable
+ *   dx_row/dx_col quantized dL/dx (rowwise / columnwise); nullable
+ *   dx_group_amax [E] FP32: required when dx is quantized to NVFP4 (receives max|dL/dx| per group)
+ *   dprobs        [M] FP32 dL/dp = sum_j dy * a(x); nullable
+ *   act_col       columnwise qtensor of y = a(x) * p regenerated from x (recompute); nullable.  Its bytes
+ *                 equal those the forward's out_col would have held.
+ *   saved_group_amax [E] FP32 group amax written by the forward; required for an NVFP4 act_col. */
+int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                               int64_t width_in, const void* x_bf16, const void* dy_bf16,
+                               const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
+                               const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
+                               const mgs_qbuf* act_col, const float* saved_group_amax, void* stream);
+
+/* Plain grouped quantization of a BF16 tensor (weights, upstream gradients, FC1 input): the forward
+ * above with act = IDENTITY and p = 1.  [P2] Greptile summary, second bullet (GroupedLinear consumes a
+ * pre-quantized grouped tensor); [P3] "A behaviour change worth calling out" (columnwise usage). */
+int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width, const void* x_bf16,
+                            const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
+                            void* stream);
+
+/* Grouped GEMM on quantized operands with FP32 accumulation.  [P2] Greptile summary, second bullet and
+ * sequence diagram (GroupedLinear forward / backward on a pre-built grouped tensor).
+ *   FPROP, DGRAD (grouped over M; m = M = sum of splits, n, k = reduction width, k % 32 == 0):
+ *     A = rowwise qtensor [M x k]; B = [E x n x k] block-quantized along k with per-group stride
+ *     (n*k data bytes) -- a rowwise weight for FPROP, the columnwise copy of the weight for DGRAD;
+ *     C [M x n] row-major; bias_bf16 [E x n] optional.
+ *   WGRAD (grouped over K; k = M = sum of splits; m, n = widths of A and B):
+ *     A = columnwise qtensor of width m, B = columnwise qtensor of width n, both over the same groups;
+ *     C [E x m x n] row-major (an empty group writes zeros, or leaves C unchanged if accumulating).
+ *   c_dtype BF16 or F32; accumulate != 0 adds into C (F32 only).
+ *   NVFP4 operands also scale each group's result by A.group_scale[g] * B.group_scale[g]. */
+int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int64_t m, int64_t n,
+                        int64_t k, const mgs_qbuf* a, const mgs_qbuf* b, void* c, int32_t c_dtype,
+                        const void* bias_bf16, int32_t accumulate, void* stream);
+
+/* Per-group column sums (bias gradient): out[g, j] = sum over group g's rows of x[r, j], FP32,
+ * fixed summation order.  [P1] Description, second paragraph: bias changes what wgrad consumes.
+ *   x_bf16 [M x width] BF16; out [E x width] FP32 (empty groups give zeros). */
+int mgs_grouped_col_sum(const mgs_groups* groups, int64_t width, const void* x_bf16, float* out,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGS_H */

@@ -1,0 +1,206 @@
+"""ctypes binding of the C ABI in include/mgs.h (libmgs.so, built in-tree for gfx950).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.  Tensors are
+torch tensors on the GPU (PyTorch provides device memory and streams); they are passed as raw device
+pointers together with the current HIP stream.  There is no fallback: if the library is missing or
+does not load, importing this module raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmgs.so")
+
+MGS_OK = 0
+ERRORS = {-1: "MGS_ERR_INVALID_ARG", -2: "MGS_ERR_SHAPE", -3: "MGS_ERR_UNSUPPORTED", -4: "MGS_ERR_HIP"}
+
+ACT = {"identity": 0, "srelu": 1, "tanh_srelu": 2, "swiglu": 3, "clamped_swiglu": 4}
+FMT = {"mxfp8": 0, "nvfp4": 1}
+GEMM_MODE = {"fprop": 0, "dgrad": 1, "wgrad": 2}
+DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+NBYTES = {"data": 0, "scales": 1, "group_scale": 2}
+MAX_GROUPS = 256
+
+
+class MgsError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (ERRORS.get(code, "?"), code, msg))
+        self.code = code
+
+
+class ActParams(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("s", ctypes.c_float), ("limit", ctypes.c_float),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float)]
+
+
+class Groups(ctypes.Structure):
+    _fields_ = [("num_groups", ctypes.c_int32), ("split_sizes", ctypes.POINTER(ctypes.c_int64))]
+
+
+class QBuf(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("group_scale", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmgs.so not found at %s: build it with __graft_entry__.build() "
+                          "(hipcc, gfx950)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    pact, pgr, pq = ctypes.POINTER(ActParams), ctypes.POINTER(Groups), ctypes.POINTER(QBuf)
+    sig = {
+        "mgs_abi_version": (ctypes.c_int, []),
+        "mgs_last_error": (ctypes.c_char_p, []),
+        "mgs_qtensor_nbytes": (i64, [i32, i32, pgr, i64, i32]),
+        "mgs_grouped_scaled_act_fwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, pq, pq, vp, vp]),
+        "mgs_grouped_scaled_act_bwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, vp, vp, pq, pq, vp,
+                                                      vp, pq, vp, vp]),
+        "mgs_grouped_mx_quantize": (ctypes.c_int, [i32, pgr, i64, vp, pq, pq, vp, vp]),
+        "mgs_grouped_gemm_mx": (ctypes.c_int, [i32, i32, pgr, i64, i64, i64, pq, pq, vp, i32, vp, i32,
+                                               vp]),
+        "mgs_grouped_col_sum": (ctypes.c_int, [pgr, i64, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
+            "mgs_grouped_scaled_act_bwd", "mgs_grouped_mx_quantize", "mgs_grouped_gemm_mx",
+            "mgs_grouped_col_sum")
+
+
+def _check(rc):
+    if rc != MGS_OK:
+        raise MgsError(rc, LIB.mgs_last_error().decode())
+    return rc
+
+
+def last_error():
+    return LIB.mgs_last_error().decode()
+
+
+def abi_version():
+    return LIB.mgs_abi_version()
+
+
+class _GroupsArg:
+    """Keeps the int64 split array alive for the duration of a call."""
+
+    def __init__(self, split_sizes):
+        self.arr = np.ascontiguousarray(np.asarray(split_sizes, dtype=np.int64))
+        self.struct = Groups(len(self.arr), self.arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    """HIP stream handle: an int passes through (0 = null stream), None = torch's current stream."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def act_params(kind, s=2.0, limit=7.0, alpha=1.0, beta=0.0):
+    return ActParams(ACT[kind], s, limit, alpha, beta)
+
+
+class QTensor:
+    """One orientation (rowwise or columnwise) of a grouped quantized tensor: three torch buffers."""
+
+    def __init__(self, fmt, colwise, split_sizes, width, device="cuda"):
+        self.fmt, self.colwise, self.width = fmt, bool(colwise), int(width)
+        self.split_sizes = np.asarray(split_sizes, dtype=np.int64)
+        nd = qtensor_nbytes(fmt, colwise, split_sizes, width, "data")
+        ns = qtensor_nbytes(fmt, colwise, split_sizes, width, "scales")
+        ng = qtensor_nbytes(fmt, colwise, split_sizes, width, "group_scale")
+        self.data = torch.empty(max(nd, 1), dtype=torch.uint8, device=device)[:nd]
+        self.scales = torch.empty(max(ns, 1), dtype=torch.uint8, device=device)[:ns]
+        self.group_scale = torch.empty(ng // 4, dtype=torch.float32, device=device) if ng else None
+
+    def qbuf(self):
+        return QBuf(self.data.data_ptr(), self.scales.data_ptr(), _ptr(self.group_scale))
+
+    def nbytes(self):
+        return self.data.numel() + self.scales.numel() + (self.group_scale.numel() * 4 if self.group_scale is not None else 0)
+
+
+def _qref(q):
+    if q is None:
+        return None, None
+    qb = q.qbuf() if isinstance(q, QTensor) else q
+    return qb, ctypes.byref(qb)
+
+
+def qtensor_nbytes(fmt, colwise, split_sizes, width, which):
+    g = _GroupsArg(split_sizes)
+    n = LIB.mgs_qtensor_nbytes(FMT[fmt], int(bool(colwise)), g.ref, int(width), NBYTES[which])
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def grouped_scaled_act_fwd(act, fmt, split_sizes, width_in, x, probs, out_row=None, out_col=None,
+                           group_amax=None, stream=None):
+    g = _GroupsArg(split_sizes)
+    _r, rref = _qref(out_row)
+    _c, cref = _qref(out_col)
+    _check(LIB.mgs_grouped_scaled_act_fwd(ctypes.byref(act), FMT[fmt], g.ref, int(width_in), _ptr(x),
+                                          _ptr(probs), rref, cref, _ptr(group_amax), _stream(stream)))
+
+
+def grouped_scaled_act_bwd(act, fmt, split_sizes, width_in, x, dy, probs, dx=None, dx_row=None,
+                           dx_col=None, dx_group_amax=None, dprobs=None, act_col=None,
+                           saved_group_amax=None, stream=None):
+    g = _GroupsArg(split_sizes)
+    _r, rref = _qref(dx_row)
+    _c, cref = _qref(dx_col)
+    _a, aref = _qref(act_col)
+    _check(LIB.mgs_grouped_scaled_act_bwd(ctypes.byref(act), FMT[fmt], g.ref, int(width_in), _ptr(x),
+                                          _ptr(dy), _ptr(probs), _ptr(dx), rref, cref,
+                                          _ptr(dx_group_amax), _ptr(dprobs), aref,
+                                          _ptr(saved_group_amax), _stream(stream)))
+
+
+def grouped_mx_quantize(fmt, split_sizes, width, x, out_row=None, out_col=None, group_amax=None,
+                        stream=None):
+    g = _GroupsArg(split_sizes)
+    _r, rref = _qref(out_row)
+    _c, cref = _qref(out_col)
+    _check(LIB.mgs_grouped_mx_quantize(FMT[fmt], g.ref, int(width), _ptr(x), rref, cref,
+                                       _ptr(group_amax), _stream(stream)))
+
+
+def grouped_gemm_mx(mode, fmt, split_sizes, m, n, k, a, b, c, bias=None, accumulate=False,
+                    stream=None):
+    g = _GroupsArg(split_sizes)
+    _a, aref = _qref(a)
+    _b, bref = _qref(b)
+    _check(LIB.mgs_grouped_gemm_mx(GEMM_MODE[mode], FMT[fmt], g.ref, int(m), int(n), int(k), aref, bref,
+                                   _ptr(c), DTYPE[c.dtype], _ptr(bias), int(bool(accumulate)),
+                                   _stream(stream)))
+
+
+def grouped_col_sum(split_sizes, width, x, out, stream=None):
+    g = _GroupsArg(split_sizes)
+    _check(LIB.mgs_grouped_col_sum(g.ref, int(width), _ptr(x), _ptr(out), _stream(stream)))

@@ -1,0 +1,296 @@
+// C-ABI entry points: argument validation, group bookkeeping and kernel dispatch.
+//
+// Group bookkeeping (page "Activation + GroupedLinear Fusion for MOE", sequence diagram: the fused
+// ops receive split_sizes and derive each group's rows from it): row offsets, padded columnwise
+// token offsets and the per-launch tile lists are computed here on the host and passed to the
+// kernels by value, so no device memory is allocated and nothing is synchronized.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "mgs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MGS_OK;
+}
+
+bool valid_fmt(int32_t fmt) { return fmt == MGS_FMT_MXFP8 || fmt == MGS_FMT_NVFP4; }
+
+bool is_gated(int kind) { return kind == MGS_ACT_SWIGLU || kind == MGS_ACT_CLAMPED_SWIGLU; }
+
+// Validates the groups and fills the panel table.  Returns MGS_OK or an error code.
+int build_groups(const mgs_groups* groups, mgs::GroupTable* gt, int64_t* total_rows) {
+  if (!groups) return fail(MGS_ERR_INVALID_ARG, "groups is NULL");
+  if (groups->num_groups < 1 || groups->num_groups > MGS_MAX_GROUPS)
+    return fail(MGS_ERR_INVALID_ARG, "num_groups %d outside [1, %d]", groups->num_groups, MGS_MAX_GROUPS);
+  if (!groups->split_sizes) return fail(MGS_ERR_INVALID_ARG, "split_sizes is NULL");
+  std::memset(gt, 0, sizeof *gt);
+  gt->num_groups = groups->num_groups;
+  int64_t rows = 0, panels = 0;
+  for (int g = 0; g < groups->num_groups; ++g) {
+    const int64_t m = groups->split_sizes[g];
+    if (m < 0) return fail(MGS_ERR_SHAPE, "split_sizes[%d] = %lld is negative", g, (long long)m);
+    gt->row_off[g] = (int32_t)rows;
+    gt->panel_off[g] = (int32_t)panels;
+    rows += m;
+    panels += (m + mgs::PANEL_ROWS - 1) / mgs::PANEL_ROWS;
+    if (rows > INT32_MAX - 64) return fail(MGS_ERR_SHAPE, "total rows exceed 2^31 - 64");
+  }
+  gt->row_off[groups->num_groups] = (int32_t)rows;
+  gt->panel_off[groups->num_groups] = (int32_t)panels;
+  gt->num_panels = (int32_t)panels;
+  *total_rows = rows;
+  return MGS_OK;
+}
+
+int check_width(int64_t w, const char* what) {
+  if (w <= 0 || w % 32 != 0)
+    return fail(MGS_ERR_SHAPE, "%s = %lld must be a positive multiple of 32", what, (long long)w);
+  if (w > (int64_t)1 << 24) return fail(MGS_ERR_SHAPE, "%s = %lld is too large", what, (long long)w);
+  return MGS_OK;
+}
+
+bool qbuf_requested(const mgs_qbuf* q) { return q && q->data; }
+
+int check_qbuf(const mgs_qbuf* q, int32_t fmt, const char* what) {
+  if (!qbuf_requested(q)) return MGS_OK;
+  if (!q->scales) return fail(MGS_ERR_INVALID_ARG, "%s.scales is NULL", what);
+  if (fmt == MGS_FMT_NVFP4 && !q->group_scale)
+    return fail(MGS_ERR_INVALID_ARG, "%s.group_scale is NULL (required for NVFP4)", what);
+  return MGS_OK;
+}
+
+int check_act(const mgs_act_params* act, mgs::ActHost* out) {
+  if (!act) return fail(MGS_ERR_INVALID_ARG, "act is NULL");
+  if (act->kind < MGS_ACT_IDENTITY || act->kind > MGS_ACT_CLAMPED_SWIGLU)
+    return fail(MGS_ERR_INVALID_ARG, "unknown activation kind %d", act->kind);
+  if (act->kind == MGS_ACT_TANH_SRELU && !(act->s > 0.0f && std::isfinite(act->s)))
+    return fail(MGS_ERR_INVALID_ARG, "TANH_SRELU needs a finite s > 0 (got %g)", (double)act->s);
+  if (act->kind == MGS_ACT_CLAMPED_SWIGLU &&
+      !(act->limit > 0.0f && std::isfinite(act->limit) && std::isfinite(act->alpha) && std::isfinite(act->beta)))
+    return fail(MGS_ERR_INVALID_ARG, "CLAMPED_SWIGLU needs a finite limit > 0 and finite alpha, beta");
+  out->kind = act->kind;
+  out->s = act->s;
+  out->inv_s = act->kind == MGS_ACT_TANH_SRELU ? 1.0f / act->s : 1.0f;
+  out->limit = act->limit;
+  out->alpha = act->alpha;
+  out->beta = act->beta;
+  return MGS_OK;
+}
+
+mgs::QOut make_qout(const mgs_qbuf* row, const mgs_qbuf* col, int64_t width) {
+  mgs::QOut q{};
+  if (qbuf_requested(row)) {
+    q.row_data = static_cast<uint8_t*>(row->data);
+    q.row_scales = static_cast<uint8_t*>(row->scales);
+    q.row_gscale = row->group_scale;
+  }
+  if (qbuf_requested(col)) {
+    q.col_data = static_cast<uint8_t*>(col->data);
+    q.col_scales = static_cast<uint8_t*>(col->scales);
+    q.col_gscale = col->group_scale;
+  }
+  q.width = width;
+  return q;
+}
+
+int hip_status(hipError_t e) {
+  if (e != hipSuccess) return fail(MGS_ERR_HIP, "HIP launch error: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mgs_abi_version(void) { return MGS_ABI_VERSION; }
+
+const char* mgs_last_error(void) { return g_err; }
+
+int64_t mgs_qtensor_nbytes(int32_t fmt, int32_t colwise, const mgs_groups* groups, int64_t width,
+                           int32_t which) {
+  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  int rc = build_groups(groups, &gt, &rows);
+  if (rc) return rc;
+  if ((rc = check_width(width, "width"))) return rc;
+  const int64_t r = colwise ? (int64_t)mgs::PANEL_ROWS * gt.num_panels : rows;
+  switch (which) {
+    case MGS_NBYTES_DATA: ok(); return fmt == MGS_FMT_MXFP8 ? r * width : r * width / 2;
+    case MGS_NBYTES_SCALES: ok(); return fmt == MGS_FMT_MXFP8 ? r * width / 32 : r * width / 16;
+    case MGS_NBYTES_GROUP_SCALE: ok(); return fmt == MGS_FMT_MXFP8 ? 0 : 4 * (int64_t)gt.num_groups;
+    default: return fail(MGS_ERR_INVALID_ARG, "unknown buffer selector %d", which);
+  }
+}
+
+int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                               int64_t width_in, const void* x_bf16, const float* probs,
+                               const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
+                               void* stream) {
+  mgs::ActHost ah;
+  int rc = check_act(act, &ah);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
+  const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
+  if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
+  if (!x_bf16) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
+  if (!qbuf_requested(out_row) && !qbuf_requested(out_col))
+    return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row and out_col are both empty)");
+  if ((rc = check_qbuf(out_row, fmt, "out_row"))) return rc;
+  if ((rc = check_qbuf(out_col, fmt, "out_col"))) return rc;
+  if (fmt == MGS_FMT_NVFP4 && !group_amax)
+    return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
+  const mgs::QOut q = make_qout(out_row, out_col, wa);
+  return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
+                                        probs, q, group_amax, static_cast<hipStream_t>(stream)));
+}
+
+int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                               int64_t width_in, const void* x_bf16, const void* dy_bf16,
+                               const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
+                               const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
+                               const mgs_qbuf* act_col, const float* saved_group_amax,
+                               void* stream) {
+  mgs::ActHost ah;
+  int rc = check_act(act, &ah);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
+  const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
+  if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
+  if (!x_bf16) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
+  if (!dy_bf16) return fail(MGS_ERR_INVALID_ARG, "dy_bf16 is NULL");
+  const bool want_dxq = qbuf_requested(dx_row) || qbuf_requested(dx_col);
+  if (!dx_bf16 && !want_dxq && !dprobs && !qbuf_requested(act_col))
+    return fail(MGS_ERR_INVALID_ARG, "no output requested");
+  if ((rc = check_qbuf(dx_row, fmt, "dx_row"))) return rc;
+  if ((rc = check_qbuf(dx_col, fmt, "dx_col"))) return rc;
+  if ((rc = check_qbuf(act_col, fmt, "act_col"))) return rc;
+  if (fmt == MGS_FMT_NVFP4 && want_dxq && !dx_group_amax)
+    return fail(MGS_ERR_INVALID_ARG, "dx_group_amax is required to quantize dx to NVFP4");
+  if (fmt == MGS_FMT_NVFP4 && qbuf_requested(act_col) && !saved_group_amax)
+    return fail(MGS_ERR_UNSUPPORTED,
+                "NVFP4 recompute (act_col) needs saved_group_amax, the group amax of the forward");
+  mgs::QOut dxq = make_qout(dx_row, dx_col, width_in);
+  mgs::QOut aq = make_qout(nullptr, act_col, wa);
+  aq.amax = saved_group_amax;
+  return hip_status(mgs::launch_act_bwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
+                                        static_cast<const uint16_t*>(dy_bf16), probs,
+                                        static_cast<uint16_t*>(dx_bf16), dxq, dx_group_amax, dprobs,
+                                        aq, static_cast<hipStream_t>(stream)));
+}
+
+int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width, const void* x_bf16,
+                            const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
+                            void* stream) {
+  mgs_act_params id{MGS_ACT_IDENTITY, 1.0f, 1.0f, 1.0f, 0.0f};
+  return mgs_grouped_scaled_act_fwd(&id, fmt, groups, width, x_bf16, nullptr, out_row, out_col,
+                                    group_amax, stream);
+}
+
+int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int64_t m, int64_t n,
+                        int64_t k, const mgs_qbuf* a, const mgs_qbuf* b, void* c, int32_t c_dtype,
+                        const void* bias_bf16, int32_t accumulate, void* stream) {
+  if (mode != MGS_GEMM_FPROP && mode != MGS_GEMM_DGRAD && mode != MGS_GEMM_WGRAD)
+    return fail(MGS_ERR_INVALID_ARG, "unknown GEMM mode %d", mode);
+  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
+  if (c_dtype != MGS_DTYPE_BF16 && c_dtype != MGS_DTYPE_F32)
+    return fail(MGS_ERR_INVALID_ARG, "unknown output dtype %d", c_dtype);
+  if (accumulate && c_dtype != MGS_DTYPE_F32)
+    return fail(MGS_ERR_UNSUPPORTED, "accumulate needs an FP32 output");
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  int rc = build_groups(groups, &gt, &rows);
+  if (rc) return rc;
+  if (!a || !a->data || !a->scales) return fail(MGS_ERR_INVALID_ARG, "operand A (data, scales) is NULL");
+  if (!b || !b->data || !b->scales) return fail(MGS_ERR_INVALID_ARG, "operand B (data, scales) is NULL");
+  if (fmt == MGS_FMT_NVFP4 && (!a->group_scale || !b->group_scale))
+    return fail(MGS_ERR_INVALID_ARG, "NVFP4 operands need group_scale");
+  if (!c) return fail(MGS_ERR_INVALID_ARG, "c is NULL");
+  if ((rc = check_width(n, "n"))) return rc;
+  mgs::GemmTable tt;
+  std::memset(&tt, 0, sizeof tt);
+  tt.num_groups = gt.num_groups;
+  const int64_t ntn = (n + 127) / 128;
+  int64_t tiles = 0;
+  if (mode == MGS_GEMM_WGRAD) {
+    if ((rc = check_width(m, "m"))) return rc;
+    if (k != rows) return fail(MGS_ERR_SHAPE, "WGRAD k = %lld must equal the split sum %lld", (long long)k, (long long)rows);
+    if (bias_bf16) return fail(MGS_ERR_INVALID_ARG, "bias is not defined for WGRAD");
+    const int64_t ntm = (m + 127) / 128;
+    for (int g = 0; g < gt.num_groups; ++g) {
+      tt.tile_off[g] = (int32_t)tiles;
+      tt.tok_off[g] = mgs::PANEL_ROWS * gt.panel_off[g];
+      tiles += ntm * ntn;
+      if (tiles > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
+    }
+    tt.tok_off[gt.num_groups] = mgs::PANEL_ROWS * gt.panel_off[gt.num_groups];
+  } else {
+    if ((rc = check_width(k, "k"))) return rc;
+    if (m != rows) return fail(MGS_ERR_SHAPE, "m = %lld must equal the split sum %lld", (long long)m, (long long)rows);
+    for (int g = 0; g < gt.num_groups; ++g) {
+      tt.tile_off[g] = (int32_t)tiles;
+      tt.tok_off[g] = gt.row_off[g];
+      const int64_t mg = gt.row_off[g + 1] - gt.row_off[g];
+      tiles += ((mg + 127) / 128) * ntn;
+      if (tiles > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
+    }
+    tt.tok_off[gt.num_groups] = gt.row_off[gt.num_groups];
+  }
+  tt.tile_off[gt.num_groups] = (int32_t)tiles;
+  tt.total_tiles = (int32_t)tiles;
+  mgs::GemmArgs ga{};
+  ga.mode = mode;
+  ga.fmt = fmt;
+  ga.m = m;
+  ga.n = n;
+  ga.k = k;
+  ga.a_data = static_cast<const uint8_t*>(a->data);
+  ga.a_scales = static_cast<const uint8_t*>(a->scales);
+  ga.a_gscale = a->group_scale;
+  ga.b_data = static_cast<const uint8_t*>(b->data);
+  ga.b_scales = static_cast<const uint8_t*>(b->scales);
+  ga.b_gscale = b->group_scale;
+  ga.c = c;
+  ga.c_f32 = c_dtype == MGS_DTYPE_F32;
+  ga.accumulate = accumulate != 0;
+  ga.bias = static_cast<const uint16_t*>(bias_bf16);
+  return hip_status(mgs::launch_gemm(ga, tt, static_cast<hipStream_t>(stream)));
+}
+
+int mgs_grouped_col_sum(const mgs_groups* groups, int64_t width, const void* x_bf16, float* out,
+                        void* stream) {
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  int rc = build_groups(groups, &gt, &rows);
+  if (rc) return rc;
+  if (width <= 0 || width % 8 != 0) return fail(MGS_ERR_SHAPE, "width must be a positive multiple of 8");
+  if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
+  if (!out) return fail(MGS_ERR_INVALID_ARG, "out is NULL");
+  return hip_status(mgs::launch_col_sum(gt, width, static_cast<const uint16_t*>(x_bf16), out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

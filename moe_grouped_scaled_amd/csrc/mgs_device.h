@@ -1,0 +1,216 @@
+// Device helpers shared by the gfx950 kernels: BF16 access, block codecs on hardware converts,
+// wavefront reductions over DPP, and the scaled activation functors.
+//
+// Everything here follows IEEE FP32 with round-to-nearest-even and is compiled with FP contraction
+// off, so a functor evaluated in two different kernels gives identical bits (the recompute path
+// regenerates the forward's quantized activation and must match it byte for byte).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mgs_internal.h"
+
+namespace mgs {
+
+// ------------------------------------------------------------------------------------------ BF16
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// FP32 -> BF16, round to nearest, ties to even (quiet NaN kept quiet).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ void unpack8(const uint4& w, float* v) {
+  v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+  v[4] = bf16lo(w.z); v[5] = bf16hi(w.z); v[6] = bf16lo(w.w); v[7] = bf16hi(w.w);
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float* v) {
+  uint4 r;
+  r.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+  r.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+  r.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
+  r.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+  return r;
+}
+
+// ------------------------------------------------------------------------------------------ DPP
+
+// quad_perm / row_ror controls of the DPP modifier (GCN3+ encoding)
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // [2,3,0,1]
+constexpr int DPP_ROW_ROR4 = 0x124;  // rotate right by 4 within each 16-lane row
+constexpr int DPP_ROW_ROR8 = 0x128;  // rotate right by 8 within each 16-lane row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// max over the 4 lanes of a quad
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  return fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+}
+// max over the 2 lanes (l, l^1)
+__device__ __forceinline__ float pair1_max(float v) { return fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v)); }
+// max over the 4 lanes {l mod 4 + 4k} of each 16-lane row
+__device__ __forceinline__ float row4_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_ROW_ROR4>(v));
+  return fmaxf(v, dpp_f<DPP_ROW_ROR8>(v));
+}
+// max over the 2 lanes (l, l^4)
+__device__ __forceinline__ float pair4_max(float v) { return fmaxf(v, __shfl_xor(v, 4)); }
+
+// ------------------------------------------------------------------------------------------ MXFP8
+
+// E8M0 scale code of a block with maximum magnitude `amax` (>= 0, finite):
+// clamp(floor(log2 amax) - 8 + 127, 0, 254), 0 for amax == 0.  For a normal FP32 amax the biased
+// exponent field is floor(log2 amax) + 127; a zero or subnormal amax has field 0 and clamps to 0.
+__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
+  int e = (int)(__float_as_uint(amax) >> 23);
+  return (uint32_t)(e > 8 ? e - 8 : 0);
+}
+
+// 2^(127 - code): the exact reciprocal of the block scale, for code in [0, 246]
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+
+// four FP32 values -> four E4M3 codes (byte i = value i), RNE, saturating at +-448.  The hardware
+// convert rounds to nearest-even but does not saturate, so values are clamped first.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// E4M3 code of one non-negative value (RNE, saturating)
+__device__ __forceinline__ uint32_t e4m3_pos(float a) {
+  a = __builtin_amdgcn_fmed3f(a, 0.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0, false) & 0xffu;
+}
+
+// exact value of a non-negative E4M3 code (0..126)
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// ------------------------------------------------------------------------------------------ NVFP4
+
+// eight FP32 values -> eight E2M1 codes packed in a dword (value 2i in the low nibble of byte i),
+// RNE, saturating at +-6 (the gfx950 convert with a unit scale).
+__device__ __forceinline__ uint32_t e2m1x8(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
+// per-group encode scale from the group amax: 2688 / amax (1 for amax == 0, FLT_MAX on overflow)
+__device__ __forceinline__ float nv_encode_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  float s = 2688.0f / amax;
+  return (__float_as_uint(s) & 0x7fffffffu) == 0x7f800000u ? 3.40282347e+38f : s;
+}
+
+struct NvBlock {
+  uint32_t code;  // E4M3 block scale code
+  float r;        // element multiplier S_enc / s_b (0 when s_b == 0)
+};
+
+__device__ __forceinline__ NvBlock nv_block(float amax_b, float s_enc) {
+  NvBlock b;
+  float sf = (amax_b / 6.0f) * s_enc;
+  b.code = e4m3_pos(sf);
+  float d = e4m3_value(b.code);
+  b.r = d != 0.0f ? s_enc / d : 0.0f;
+  return b;
+}
+
+// ------------------------------------------------------------------------------------------ acts
+
+struct ActArgs {
+  int kind;
+  float s, inv_s, limit, alpha, beta;
+};
+
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// a(x) for unary kinds
+template <int KIND>
+__device__ __forceinline__ float act_unary(float x, const ActArgs& aa) {
+  if constexpr (KIND == MGS_ACT_IDENTITY) {
+    return x;
+  } else if constexpr (KIND == MGS_ACT_SRELU) {
+    float r = fmaxf(x, 0.0f);
+    return r * r;
+  } else {
+    float r = fmaxf(x, 0.0f);
+    float t = aa.s * tanhf(r * aa.inv_s);
+    return t * t;
+  }
+}
+
+// a'(x) * dy for unary kinds (dy already multiplied by nothing); returns da/dx
+template <int KIND>
+__device__ __forceinline__ float dact_unary(float x, const ActArgs& aa) {
+  if constexpr (KIND == MGS_ACT_IDENTITY) {
+    return 1.0f;
+  } else if constexpr (KIND == MGS_ACT_SRELU) {
+    float r = fmaxf(x, 0.0f);
+    return r + r;
+  } else {
+    float r = fmaxf(x, 0.0f);
+    float t = tanhf(r * aa.inv_s);
+    float d = (aa.s + aa.s) * t * (1.0f - t * t);
+    return x > 0.0f ? d : 0.0f;
+  }
+}
+
+// a(gate, up) for gated kinds
+template <int KIND>
+__device__ __forceinline__ float act_gated(float g, float u, const ActArgs& aa) {
+  if constexpr (KIND == MGS_ACT_SWIGLU) {
+    return g * sigmoidf_(g) * u;
+  } else {
+    float gc = fminf(g, aa.limit);
+    float uc = fminf(fmaxf(u, -aa.limit), aa.limit);
+    return gc * sigmoidf_(aa.alpha * gc) * (uc + aa.beta);
+  }
+}
+
+// (a, da/dgate, da/dup) for gated kinds
+template <int KIND>
+__device__ __forceinline__ void dact_gated(float g, float u, const ActArgs& aa, float& a, float& dg,
+                                           float& du) {
+  if constexpr (KIND == MGS_ACT_SWIGLU) {
+    float sg = sigmoidf_(g);
+    float silu = g * sg;
+    a = silu * u;
+    dg = u * sg * (1.0f + g * (1.0f - sg));
+    du = silu;
+  } else {
+    float gc = fminf(g, aa.limit);
+    float uc = fminf(fmaxf(u, -aa.limit), aa.limit);
+    float sg = sigmoidf_(aa.alpha * gc);
+    float silu = gc * sg;
+    float up = uc + aa.beta;
+    a = silu * up;
+    dg = g <= aa.limit ? up * sg * (1.0f + aa.alpha * gc * (1.0f - sg)) : 0.0f;
+    du = (u >= -aa.limit && u <= aa.limit) ? silu : 0.0f;
+  }
+}
+
+}  // namespace mgs

@@ -1,0 +1,85 @@
+// Internal interface between the C-ABI layer (argument validation, group bookkeeping) and the kernel
+// launchers.  Not installed; the public interface is include/mgs.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mgs.h"
+
+namespace mgs {
+
+// Rows of one panel: a panel is 32 consecutive rows of one group, the unit of both the columnwise
+// quantization blocks (32 for MXFP8, 2 x 16 for NVFP4) and of the padded columnwise token layout.
+constexpr int PANEL_ROWS = 32;
+// Output columns covered by one workgroup per iteration (4 waves x 128 columns).
+constexpr int TILE_COLS = 512;
+
+// Group bookkeeping passed by value in the kernel arguments.
+//   row_off[g]   = sum_{h<g} m_h                 (E + 1 entries)
+//   panel_off[g] = sum_{h<g} ceil(m_h / 32)      (E + 1 entries); the padded columnwise token offset
+//                  of group g is 32 * panel_off[g] and its padded length 32 * (panel_off[g+1] - panel_off[g]).
+struct GroupTable {
+  int32_t num_groups;
+  int32_t num_panels;
+  int32_t row_off[MGS_MAX_GROUPS + 1];
+  int32_t panel_off[MGS_MAX_GROUPS + 1];
+};
+
+// One quantized output (rowwise and/or columnwise copies) of logical width `width`.
+struct QOut {
+  uint8_t* row_data;
+  uint8_t* row_scales;
+  uint8_t* col_data;
+  uint8_t* col_scales;
+  float* row_gscale;  // NVFP4 S_dec outputs (may be null)
+  float* col_gscale;
+  const float* amax;  // NVFP4: per-group amax the encode scale derives from
+  int64_t width;
+};
+
+struct ActHost {
+  int kind;
+  float s, inv_s, limit, alpha, beta;
+};
+
+// Group table for the GEMM tile scheduler.
+struct GemmTable {
+  int32_t num_groups;
+  int32_t total_tiles;
+  int32_t tile_off[MGS_MAX_GROUPS + 1];  // cumulative tiles per group
+  int32_t tok_off[MGS_MAX_GROUPS + 1];   // M-grouped: row offsets; K-grouped: padded token offsets
+};
+
+struct GemmArgs {
+  int mode;  // mgs_gemm_mode
+  int fmt;   // mgs_fmt
+  int64_t m, n, k;
+  const uint8_t* a_data;
+  const uint8_t* a_scales;
+  const float* a_gscale;
+  const uint8_t* b_data;
+  const uint8_t* b_scales;
+  const float* b_gscale;
+  void* c;
+  int c_f32;
+  int accumulate;
+  const uint16_t* bias;
+};
+
+// ---- launchers (return hipGetLastError() after the launches) ----
+
+hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
+                          const uint16_t* x, const float* probs, QOut out, float* group_amax,
+                          hipStream_t stream);
+
+hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
+                          const uint16_t* x, const uint16_t* dy, const float* probs, uint16_t* dx,
+                          QOut dxq, float* dx_amax, float* dprobs, QOut actq, hipStream_t stream);
+
+hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,
+                          hipStream_t stream);
+
+hipError_t launch_gemm(const GemmArgs& ga, const GemmTable& tt, hipStream_t stream);
+
+}  // namespace mgs

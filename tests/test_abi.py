@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments before anything touches a GPU (validation runs on the host, so these run without one)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "mgs.h")).read()
+    return sorted(set(re.findall(r"\b(mgs_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_entry_points():
+    syms = _declared_symbols()
+    for name in ("mgs_grouped_scaled_act_fwd", "mgs_grouped_scaled_act_bwd", "mgs_grouped_mx_quantize",
+                 "mgs_grouped_gemm_mx"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    from moe_grouped_scaled_amd import _native
+    lib = ctypes.CDLL(_native.LIB_PATH)
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+    assert set(_native.EXPORTED) == set(_declared_symbols())
+    assert _native.abi_version() == 1
+
+
+def test_qtensor_nbytes_layouts():
+    from moe_grouped_scaled_amd import _native as N
+    from oracle.quant import qtensor_nbytes as oracle_nbytes
+    for splits in ([64, 128, 32, 32], [0, 1, 31, 33, 64], [512] * 4):
+        for fmt in ("mxfp8", "nvfp4"):
+            for col in (False, True):
+                d, s = oracle_nbytes(fmt, col, splits, 96)
+                assert N.qtensor_nbytes(fmt, col, splits, 96, "data") == d
+                assert N.qtensor_nbytes(fmt, col, splits, 96, "scales") == s
+        assert N.qtensor_nbytes("nvfp4", False, splits, 96, "group_scale") == 4 * len(splits)
+        assert N.qtensor_nbytes("mxfp8", False, splits, 96, "group_scale") == 0
+
+
+def _expect(code, fn, *args, match=None, **kw):
+    from moe_grouped_scaled_amd import _native as N
+    with pytest.raises(N.MgsError) as ei:
+        fn(*args, **kw)
+    assert ei.value.code == code, str(ei.value)
+    if match:
+        assert re.search(match, str(ei.value)), str(ei.value)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation before any launch
+
+
+class _FakeQ:
+    def __init__(self, gs=True):
+        from moe_grouped_scaled_amd import _native as N
+        self.q = N.QBuf(FAKE, FAKE, FAKE if gs else None)
+
+
+def test_argument_validation_act_fwd():
+    from moe_grouped_scaled_amd import _native as N
+    act = N.act_params("srelu")
+    q = _FakeQ().q
+    f = N.grouped_scaled_act_fwd
+    _expect(-2, f, act, "mxfp8", [32, -1], 64, FAKE, FAKE, out_row=q, stream=0, match="negative")
+    _expect(-2, f, act, "mxfp8", [32], 48, FAKE, FAKE, out_row=q, stream=0, match="multiple of 32")
+    _expect(-2, f, N.act_params("swiglu"), "mxfp8", [32], 96, FAKE, FAKE, out_row=q, stream=0)
+    _expect(-1, f, act, "mxfp8", [32], 64, None, FAKE, out_row=q, stream=0, match="x_bf16")
+    _expect(-1, f, act, "mxfp8", [32], 64, FAKE, FAKE, stream=0, match="no output")
+    _expect(-1, f, act, "nvfp4", [32], 64, FAKE, FAKE, out_row=q, stream=0, match="group_amax")
+    _expect(-1, f, act, "nvfp4", [32], 64, FAKE, FAKE, out_row=_FakeQ(gs=False).q, group_amax=FAKE,
+            stream=0, match="group_scale")
+    _expect(-1, f, N.act_params("tanh_srelu", s=0.0), "mxfp8", [32], 64, FAKE, FAKE, out_row=q, stream=0)
+    _expect(-1, f, N.ActParams(9, 1, 1, 1, 0), "mxfp8", [32], 64, FAKE, FAKE, out_row=q, stream=0)
+    _expect(-1, f, act, "mxfp8", [1] * 257, 64, FAKE, FAKE, out_row=q, stream=0, match="num_groups")
+
+
+def test_argument_validation_act_bwd_and_recompute():
+    from moe_grouped_scaled_amd import _native as N
+    act = N.act_params("srelu")
+    q = _FakeQ().q
+    b = N.grouped_scaled_act_bwd
+    _expect(-1, b, act, "mxfp8", [32], 64, FAKE, None, FAKE, dx=FAKE, stream=0, match="dy_bf16")
+    _expect(-1, b, act, "mxfp8", [32], 64, FAKE, FAKE, FAKE, stream=0, match="no output")
+    _expect(-3, b, act, "nvfp4", [32], 64, FAKE, FAKE, FAKE, act_col=q, stream=0, match="saved_group_amax")
+    _expect(-1, b, act, "nvfp4", [32], 64, FAKE, FAKE, FAKE, dx_row=q, stream=0, match="dx_group_amax")
+
+
+def test_argument_validation_gemm():
+    from moe_grouped_scaled_amd import _native as N
+    import torch
+    q = _FakeQ().q
+    c = torch.empty(1, dtype=torch.float32)
+    g = N.grouped_gemm_mx
+    _expect(-2, g, "fprop", "mxfp8", [32, 32], 63, 64, 64, q, q, c, stream=0, match="split sum")
+    _expect(-2, g, "fprop", "mxfp8", [32, 32], 64, 64, 48, q, q, c, stream=0, match="multiple of 32")
+    _expect(-2, g, "wgrad", "mxfp8", [32, 32], 64, 64, 63, q, q, c, stream=0, match="split sum")
+    _expect(-1, g, "wgrad", "mxfp8", [32, 32], 64, 64, 64, q, q, c, bias=FAKE, stream=0, match="bias")
+    cb = torch.empty(1, dtype=torch.bfloat16)
+    _expect(-3, g, "fprop", "mxfp8", [32], 32, 64, 64, q, q, cb, accumulate=True, stream=0)
+    _expect(-1, g, "fprop", "nvfp4", [32], 32, 64, 64, _FakeQ(gs=False).q, q, c, stream=0)
+
+
+def test_last_error_is_cleared_on_success():
+    from moe_grouped_scaled_amd import _native as N
+    with pytest.raises(N.MgsError):
+        N.qtensor_nbytes("mxfp8", False, [32], 33, "data")
+    assert "multiple of 32" in N.last_error()
+    N.qtensor_nbytes("mxfp8", False, [32], 32, "data")
+    assert N.last_error() == ""

@@ -1,0 +1,324 @@
+"""GPU parity of the fused scaled-activation + grouped quantization kernels against the oracle.
+
+Every call goes through the C ABI (libmgs.so via the ctypes binding).  Inputs come from the seeded
+generators in ``workloads``; expected values from ``oracle`` only.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import activations as A
+from oracle import quant as Q
+from tests.helpers import (
+    bf16_f64,
+    bf16_host,
+    compare_quantized,
+    f32,
+    mx_elementwise,
+    nv_elementwise,
+    to_dev,
+    to_dev_bf16,
+    u8,
+)
+
+pytestmark = pytest.mark.gpu
+
+EXACT_KINDS = ("srelu", "identity")
+
+
+@pytest.fixture(scope="module")
+def N():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from moe_grouped_scaled_amd import _native
+    return _native
+
+
+def _params(kind, **kw):
+    p = {}
+    if kind == "tanh_srelu":
+        p["s"] = kw.get("s", 2.0)
+    if kind == "clamped_swiglu":
+        p.update(limit=kw.get("limit", 7.0), alpha=kw.get("alpha", 1.0), beta=kw.get("beta", 0.0))
+    return p
+
+
+def gpu_fwd(N, kind, fmt, splits, width_in, x_bits, p, row=True, col=True, **kw):
+    import torch
+    wa = A.out_width(kind, width_in)
+    qr = N.QTensor(fmt, False, splits, wa) if row else None
+    qc = N.QTensor(fmt, True, splits, wa) if col else None
+    amax = torch.empty(len(splits), dtype=torch.float32, device="cuda") if fmt == "nvfp4" else None
+    N.grouped_scaled_act_fwd(N.act_params(kind, **_params(kind, **kw)), fmt, splits, width_in,
+                             to_dev_bf16(x_bits), None if p is None else to_dev(p), qr, qc, amax)
+    torch.cuda.synchronize()
+    out = {}
+    if row:
+        out["row_data"], out["row_scales"] = u8(qr.data), u8(qr.scales)
+        if fmt == "nvfp4":
+            out["row_gs"] = f32(qr.group_scale)
+    if col:
+        out["col_data"], out["col_scales"] = u8(qc.data), u8(qc.scales)
+        if fmt == "nvfp4":
+            out["col_gs"] = f32(qc.group_scale)
+    if fmt == "nvfp4":
+        out["amax"] = f32(amax)
+    return out
+
+
+def oracle_fwd(kind, fmt, splits, x_bits, p, row=True, col=True, **kw):
+    x = bf16_f64(x_bits)
+    pp = np.ones(x.shape[0]) if p is None else p.astype(np.float64)
+    y = A.scaled_act_fwd(kind, x, pp, **_params(kind, **kw))
+    return Q.quantize_grouped(y, splits, fmt, rowwise=row, colwise=col), y
+
+
+def _row_view(fmt, data, scales, splits, width, gs):
+    m = int(np.sum(splits))
+    if fmt == "mxfp8":
+        return mx_elementwise(data, scales, m, width)
+    off = Q.group_offsets(splits)
+    s_dec = np.concatenate([np.full(int(splits[g]), gs[g]) for g in range(len(splits))])[:, None]
+    return nv_elementwise(data, scales, m, width, s_dec)
+
+
+def _col_view(fmt, data, scales, splits, width, gs):
+    coff = Q.col_offsets(splits)  # flat view: every block of the per-group [width x mp_g] layout
+    if fmt == "mxfp8":
+        return mx_elementwise(data, scales, int(coff[-1]) * width // 32, 32)
+    parts = []
+    for g in range(len(splits)):
+        n_el = width * int(coff[g + 1] - coff[g])
+        parts.append(np.full(n_el // 16, gs[g]))
+    s_dec = np.concatenate(parts)[:, None] if parts else np.zeros((0, 1))
+    return nv_elementwise(data, scales, int(coff[-1]) * width // 16, 16, s_dec)
+
+
+def check_fwd(fmt, kind, got, ref, splits, width_out, exact):
+    if fmt == "nvfp4":
+        if exact:
+            assert np.array_equal(got["amax"], ref["group_amax"]), "group amax differs"
+        else:
+            assert np.allclose(got["amax"], ref["group_amax"], rtol=1e-5, atol=0), "group amax differs"
+        for k in ("row_gs", "col_gs"):
+            if k in got:
+                if exact:
+                    assert np.array_equal(got[k], ref["group_scale"]), k
+                else:
+                    assert np.allclose(got[k], ref["group_scale"], rtol=1e-5, atol=0), k
+    for orient, view in (("row", _row_view), ("col", _col_view)):
+        if orient + "_data" not in got:
+            continue
+        gd, gsc = got[orient + "_data"], got[orient + "_scales"]
+        rd, rsc = ref[orient + "_data"], ref[orient + "_scales"]
+        if exact:
+            assert np.array_equal(gsc, rsc), "%s scales differ at %s" % (orient, np.flatnonzero(gsc != rsc)[:8])
+            assert np.array_equal(gd, rd), "%s codes differ at %s" % (orient, np.flatnonzero(gd != rd)[:8])
+        else:
+            gs = ref.get("group_scale")
+            compare_quantized(fmt, view(fmt, gd, gsc, splits, width_out, gs),
+                              view(fmt, rd, rsc, splits, width_out, gs))
+
+
+FWD_CASES = [
+    # (kind, fmt, splits, width_in, x std)
+    ("srelu", "mxfp8", [64, 128, 32, 32], 512, 1.0),          # 4 experts, 256 tokens, width 512
+    ("srelu", "mxfp8", [0, 1, 31, 33, 64], 96, 1.0),          # ragged groups, partial column tile
+    ("identity", "mxfp8", [3, 77, 0, 160], 1056, 1.0),        # plain quantize, 1056 = 2 x 512 + 32
+    ("srelu", "nvfp4", [128, 128, 128, 128], 1024, 1.5),
+    ("identity", "nvfp4", [0, 1, 31, 33, 64], 64, 1.0),
+    ("tanh_srelu", "nvfp4", [512, 512, 512, 512], 1024, 1.5),  # 4 experts x 512 tokens, width 1024
+    ("tanh_srelu", "mxfp8", [40, 0, 300], 1024, 1.5),
+    ("swiglu", "mxfp8", [100, 0, 333, 591], 4096, 1.0),
+    ("swiglu", "nvfp4", [17, 250], 1024, 1.0),
+    ("clamped_swiglu", "mxfp8", [0, 300, 1, 700, 23], 4096, 3.0),
+    ("clamped_swiglu", "nvfp4", [64, 100], 512, 3.0),
+]
+
+
+@pytest.mark.parametrize("kind,fmt,splits,width_in,std", FWD_CASES)
+def test_act_fwd_parity(N, kind, fmt, splits, width_in, std):
+    d = workloads.act_case(kind, splits, width_in, seed=11, std=std, with_dy=False)
+    got = gpu_fwd(N, kind, fmt, splits, width_in, d["x"], d["p"])
+    ref, _ = oracle_fwd(kind, fmt, splits, d["x"], d["p"])
+    check_fwd(fmt, kind, got, ref, splits, A.out_width(kind, width_in), kind in EXACT_KINDS)
+
+
+def test_act_fwd_swiglu_zipf_full_size(N):
+    """The Zipf-split SwiGLU workload at full size: 8 experts, 8192 tokens, FC1 out 2 x 2048."""
+    d = workloads.make("swiglu_zipf")
+    got = gpu_fwd(N, "swiglu", "mxfp8", d["splits"], 4096, d["x"], d["p"])
+    ref, _ = oracle_fwd("swiglu", "mxfp8", d["splits"], d["x"], d["p"])
+    check_fwd("mxfp8", "swiglu", got, ref, d["splits"], 2048, False)
+
+
+def test_act_fwd_clamped_alpha_beta(N):
+    d = workloads.act_case("clamped_swiglu", [96, 64], 512, seed=3, std=4.0, with_dy=False)
+    got = gpu_fwd(N, "clamped_swiglu", "mxfp8", [96, 64], 512, d["x"], d["p"], alpha=1.702, beta=1.0)
+    ref, _ = oracle_fwd("clamped_swiglu", "mxfp8", [96, 64], d["x"], d["p"], alpha=1.702, beta=1.0)
+    check_fwd("mxfp8", "clamped_swiglu", got, ref, [96, 64], 256, False)
+
+
+def test_act_fwd_edge_values(N):
+    """Exact representable edge inputs: +-7.0 at the clamp, all-zero rows, powers of two at the block
+    maximum, large values that saturate, and p = 1 (probs omitted)."""
+    rng = np.random.default_rng(5)
+    splits = [32, 33, 0, 31]
+    m, w = sum(splits), 128
+    x = rng.standard_normal((m, w)).astype(np.float32)
+    x[0, :] = 0.0
+    x[1, :32] = 7.0
+    x[2, :32] = -7.0
+    x[3, 5] = 16.0                      # SReLU -> 256 exactly: a power-of-two block maximum
+    x[4, 7] = 2.0 ** 60                 # SReLU -> 2^120: the scale code saturates upward
+    x[5:9, :] = 2.0 ** -70              # tiny values: scale code clamps at 0
+    bits = workloads.bf16_bits(x)
+    for kind in ("srelu", "identity"):
+        got = gpu_fwd(N, kind, "mxfp8", splits, w, bits, None)
+        ref, _ = oracle_fwd(kind, "mxfp8", splits, bits, None)
+        check_fwd("mxfp8", kind, got, ref, splits, w, True)
+    got = gpu_fwd(N, "clamped_swiglu", "mxfp8", splits, w, bits, None)
+    ref, _ = oracle_fwd("clamped_swiglu", "mxfp8", splits, bits, None)
+    check_fwd("mxfp8", "clamped_swiglu", got, ref, splits, w // 2, False)
+
+
+# ------------------------------------------------------------------------------------------ bwd
+
+def gpu_bwd(N, kind, fmt, splits, width_in, x_bits, dy_bits, p, dense=True, row=True, col=True,
+            dprobs=True, recompute=True, saved_amax=None, **kw):
+    import torch
+    wa = A.out_width(kind, width_in)
+    m = int(np.sum(splits))
+    dx = torch.empty((m, width_in), dtype=torch.bfloat16, device="cuda") if dense else None
+    qr = N.QTensor(fmt, False, splits, width_in) if row else None
+    qc = N.QTensor(fmt, True, splits, width_in) if col else None
+    qa = N.QTensor(fmt, True, splits, wa) if recompute else None
+    dxa = torch.empty(len(splits), dtype=torch.float32, device="cuda") if fmt == "nvfp4" else None
+    dp = torch.empty(m, dtype=torch.float32, device="cuda") if dprobs else None
+    sa = to_dev(saved_amax.astype(np.float32)) if saved_amax is not None else None
+    N.grouped_scaled_act_bwd(N.act_params(kind, **_params(kind, **kw)), fmt, splits, width_in,
+                             to_dev_bf16(x_bits), to_dev_bf16(dy_bits), None if p is None else to_dev(p),
+                             dx=dx, dx_row=qr, dx_col=qc, dx_group_amax=dxa, dprobs=dp, act_col=qa,
+                             saved_group_amax=sa)
+    torch.cuda.synchronize()
+    out = {}
+    if dense:
+        out["dx"] = bf16_host(dx)
+    if row:
+        out["row_data"], out["row_scales"] = u8(qr.data), u8(qr.scales)
+        if fmt == "nvfp4":
+            out["row_gs"] = f32(qr.group_scale)
+    if col:
+        out["col_data"], out["col_scales"] = u8(qc.data), u8(qc.scales)
+        if fmt == "nvfp4":
+            out["col_gs"] = f32(qc.group_scale)
+    if fmt == "nvfp4" and (row or col):
+        out["amax"] = f32(dxa)
+    if dprobs:
+        out["dp"] = f32(dp)
+    if recompute:
+        out["act_col_data"], out["act_col_scales"] = u8(qa.data), u8(qa.scales)
+        if fmt == "nvfp4":
+            out["act_col_gs"] = f32(qa.group_scale)
+    return out
+
+
+BWD_CASES = [
+    ("srelu", "mxfp8", [64, 128, 32, 32], 512, 1.0),
+    ("srelu", "mxfp8", [0, 1, 31, 33, 64], 1056, 1.0),
+    ("srelu", "nvfp4", [96, 0, 160], 512, 1.5),
+    ("tanh_srelu", "nvfp4", [512, 512, 512, 512], 1024, 1.5),  # 4 experts x 512 tokens, width 1024
+    ("tanh_srelu", "mxfp8", [100, 28], 512, 1.5),
+    ("swiglu", "mxfp8", [300, 0, 212], 4096, 1.0),
+    ("swiglu", "nvfp4", [70, 58], 1024, 1.0),
+    ("clamped_swiglu", "mxfp8", [0, 200, 56], 2048, 3.0),
+]
+
+
+@pytest.mark.parametrize("kind,fmt,splits,width_in,std", BWD_CASES)
+def test_act_bwd_parity(N, kind, fmt, splits, width_in, std):
+    d = workloads.act_case(kind, splits, width_in, seed=21, std=std)
+    params = _params(kind)
+    x = bf16_f64(d["x"])
+    p = d["p"].astype(np.float64)
+    dy = bf16_f64(d["dy"])
+    y = A.scaled_act_fwd(kind, x, p, **params)
+    saved = Q.quantize_grouped(y, splits, fmt, rowwise=False)["group_amax"] if fmt == "nvfp4" else None
+    got = gpu_bwd(N, kind, fmt, splits, width_in, d["x"], d["dy"], d["p"], saved_amax=saved)
+    dx32, dp = A.scaled_act_bwd(kind, x, dy, p, **params)
+    exact = kind in EXACT_KINDS
+    # dense BF16 dL/dx
+    from oracle.codecs import f32_to_bf16_bits
+    ref_dx = f32_to_bf16_bits(dx32.astype(np.float32))
+    if exact:
+        assert np.array_equal(got["dx"], ref_dx)
+    else:
+        diff = got["dx"] != ref_dx
+        assert diff.mean() <= 1e-3
+        gv, rv = bf16_f64(got["dx"][diff]), bf16_f64(ref_dx[diff])
+        assert np.all(np.abs(gv - rv) <= np.abs(rv) * 2.0 ** -7 * 1.0001 + 1e-30)
+    # quantized dL/dx (row + col) against the oracle quantizer on the oracle's FP32 dx
+    ref_q = Q.quantize_grouped(dx32, splits, fmt)
+    check_fwd(fmt, kind, got, ref_q, splits, width_in, exact)
+    # dprobs: any FP32 summation order lies within (W + 8) * 2^-24 * sum |dy * a|
+    a = A.act(kind, x, **params)
+    bound = (a.shape[1] + 8) * 2.0 ** -24 * np.sum(np.abs(dy * a), axis=1) + 1e-30
+    assert np.all(np.abs(got["dp"] - dp) <= bound), np.max(np.abs(got["dp"] - dp) / bound)
+    # the recompute output equals the oracle's columnwise quantization of y
+    ref_a = Q.quantize_grouped(y, splits, fmt, rowwise=False)
+    got_a = {"col_data": got["act_col_data"], "col_scales": got["act_col_scales"]}
+    if fmt == "nvfp4":
+        got_a["amax"] = saved
+        got_a["col_gs"] = got["act_col_gs"]
+    check_fwd(fmt, kind, got_a, ref_a, splits, A.out_width(kind, width_in), exact)
+
+
+@pytest.mark.parametrize("kind,fmt", [("srelu", "mxfp8"), ("tanh_srelu", "mxfp8"), ("swiglu", "mxfp8"),
+                                      ("clamped_swiglu", "mxfp8"), ("srelu", "nvfp4"),
+                                      ("tanh_srelu", "nvfp4")])
+def test_recompute_is_bitwise_equal_to_forward_columnwise(N, kind, fmt):
+    """The backward's regenerated FC2 input (act_col) is byte-identical to what the forward's
+    columnwise output would have stored (recompute changes only what is kept)."""
+    splits = [37, 0, 256, 95]
+    width_in = 1024 if kind in A.GATED else 512
+    d = workloads.act_case(kind, splits, width_in, seed=31)
+    fwd = gpu_fwd(N, kind, fmt, splits, width_in, d["x"], d["p"], row=True, col=True)
+    bwd = gpu_bwd(N, kind, fmt, splits, width_in, d["x"], d["dy"], d["p"], dense=False, row=False,
+                  col=False, dprobs=True, recompute=True,
+                  saved_amax=fwd.get("amax"))
+    assert np.array_equal(bwd["act_col_data"], fwd["col_data"])
+    assert np.array_equal(bwd["act_col_scales"], fwd["col_scales"])
+    if fmt == "nvfp4":
+        assert np.array_equal(bwd["act_col_gs"], fwd["col_gs"])
+
+
+def test_bwd_outputs_independent_of_requests(N):
+    """Requesting fewer outputs (NULL = not computed) changes no requested output: dprobs and dense
+    dx are identical whether or not the quantized outputs and the recompute output are requested."""
+    splits = [64, 96]
+    d = workloads.act_case("swiglu", splits, 1024, seed=41)
+    full = gpu_bwd(N, "swiglu", "mxfp8", splits, 1024, d["x"], d["dy"], d["p"])
+    part = gpu_bwd(N, "swiglu", "mxfp8", splits, 1024, d["x"], d["dy"], d["p"], row=False, col=False,
+                   recompute=False)
+    assert np.array_equal(full["dp"], part["dp"]) and np.array_equal(full["dx"], part["dx"])
+    only_q = gpu_bwd(N, "swiglu", "mxfp8", splits, 1024, d["x"], d["dy"], d["p"], dense=False,
+                     dprobs=False, recompute=False)
+    assert np.array_equal(only_q["row_data"], full["row_data"]) and np.array_equal(only_q["col_data"], full["col_data"])
+
+
+def test_col_sum(N):
+    import torch
+    rng = np.random.default_rng(7)
+    splits = [5, 0, 300, 64]
+    x = workloads.normal_bf16(rng, (sum(splits), 1040))
+    out = torch.empty((len(splits), 1040), dtype=torch.float32, device="cuda")
+    N.grouped_col_sum(splits, 1040, to_dev_bf16(x), out)
+    torch.cuda.synchronize()
+    got = f32(out)
+    xv = bf16_f64(x)
+    off = Q.group_offsets(splits)
+    for g in range(len(splits)):
+        ref = xv[off[g]:off[g + 1]].sum(axis=0)
+        bound = (splits[g] + 1) * 2.0 ** -24 * np.abs(xv[off[g]:off[g + 1]]).sum(axis=0) + 1e-30
+        assert np.all(np.abs(got[g] - ref) <= bound)
