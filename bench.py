@@ -1,0 +1,246 @@
+"""Benchmark of the fused MoE expert-MLP hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: FC1 input / weight quantization, the FC1
+grouped GEMM (+ bias), the fused per-row scaled activation + MXFP8 quantize, FC2, then the backward
+(upstream-gradient quantization, FC2 dgrad, the fused activation backward with dprobs and the
+recompute of FC2's columnwise input, FC1 dgrad) and the delayed weight gradients (FC2 and FC1 wgrad,
+both bias gradients).  Workload: 16 experts x 2048 tokens, hidden 4096, ffn 4096, ScaledSReLU, bias on,
+recompute on, delayed wgrad, seeded synthetic inputs already resident in HBM.
+
+Prints one JSON line.  `value` is the step's GEMM work over the whole step time (TFLOP/s); the line
+also carries the per-kernel breakdown (fused act+quant GB/s forward and backward, grouped GEMM TFLOP/s),
+the roofline of the dominant kernel (the grouped GEMM) and the oracle's CPU throughput on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused act+MX-quant GB/s (% of HBM peak) fwd/bwd; grouped MX GEMM TFLOP/s"
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"mxfp8": 5000.0, "nvfp4": 2500.0}   # FP8 dense; NVFP4 runs on the FP16 MFMA
+
+
+def act_fwd_bytes(m, w_in, w_a, fmt, row=True, col=False, col_rows=None):
+    """Algorithmic bytes of one fused forward: x read once, p read once, each requested output
+    written once (codes + scales)."""
+    b = 2 * m * w_in + 4 * m
+    per = (w_a + w_a // 32) if fmt == "mxfp8" else (w_a // 2 + w_a // 16)
+    if row:
+        b += m * per
+    if col:
+        b += (col_rows if col_rows is not None else m) * per
+    return b
+
+
+def act_bwd_bytes(m, w_in, w_a, fmt, dense=True, row=True, col=True, dprobs=True, recompute=True,
+                  col_rows=None):
+    cr = col_rows if col_rows is not None else m
+    b = 2 * m * w_in + 2 * m * w_a + 4 * m
+    per_in = (w_in + w_in // 32) if fmt == "mxfp8" else (w_in // 2 + w_in // 16)
+    per_a = (w_a + w_a // 32) if fmt == "mxfp8" else (w_a // 2 + w_a // 16)
+    if dense:
+        b += 2 * m * w_in
+    if row:
+        b += m * per_in
+    if col:
+        b += cr * per_in
+    if dprobs:
+        b += 4 * m
+    if recompute:
+        b += cr * per_a
+    return b
+
+
+class Timer:
+    """Wraps the binding's entry points to record HIP events around every call on the stream the
+    library launches on (torch's current stream)."""
+
+    def __init__(self, N):
+        import torch
+        self.torch, self.N = torch, N
+        self.records = []
+        self.enabled = False
+        self._orig = {}
+        for name in ("grouped_scaled_act_fwd", "grouped_scaled_act_bwd", "grouped_mx_quantize",
+                     "grouped_gemm_mx", "grouped_col_sum"):
+            self._wrap(name)
+
+    def _wrap(self, name):
+        orig = getattr(self.N, name)
+        self._orig[name] = orig
+        torch = self.torch
+
+        def wrapped(*a, **kw):
+            if not self.enabled:
+                return orig(*a, **kw)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            r = orig(*a, **kw)
+            e.record()
+            tag = name if name != "grouped_gemm_mx" else "gemm_" + a[0]
+            self.records.append((tag, s, e))
+            return r
+
+        setattr(self.N, name, wrapped)
+
+    def durations(self):
+        out = {}
+        for tag, s, e in self.records:
+            out.setdefault(tag, []).append(s.elapsed_time(e) * 1e-3)
+        return out
+
+
+def cpu_baseline(kind, fmt, seed=0):
+    """The oracle's expert-MLP step on a bounded sample of the workload: one of the 16 experts with
+    512 tokens, full hidden 4096 / ffn 4096 weights.  Returns the oracle's GEMM TFLOP/s."""
+    from oracle import mlp as M
+    import workloads
+    from oracle.codecs import bf16_bits_to_f64
+    rng = np.random.default_rng(seed)
+    e, tok, h, f = 1, 512, 4096, 4096
+    splits = [tok] * e
+    m = e * tok
+    x1 = bf16_bits_to_f64(workloads.normal_bf16(rng, (m, h)))
+    w1 = bf16_bits_to_f64(workloads.normal_bf16(rng, (e, f, h), 0.02))
+    w2 = bf16_bits_to_f64(workloads.normal_bf16(rng, (e, h, f), 0.02))
+    b1 = bf16_bits_to_f64(workloads.normal_bf16(rng, (e, f), 0.02))
+    b2 = bf16_bits_to_f64(workloads.normal_bf16(rng, (e, h), 0.02))
+    p = workloads.uniform_f32(rng, m).astype(np.float64)
+    dy2 = bf16_bits_to_f64(workloads.normal_bf16(rng, (m, h)))
+    t0 = time.perf_counter()
+    M.mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2)
+    dt = time.perf_counter() - t0
+    flops = 2 * m * (h * f + f * h) * 3
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the visible cores
+        threads = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "oracle expert-MLP step (numpy float64), 1 expert x 512 tokens, hidden 4096, "
+                      "ffn 4096, same recipe; %.1f s wall" % dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--fmt", default="mxfp8", choices=["mxfp8", "nvfp4"])
+    ap.add_argument("--act", default="srelu", choices=["srelu", "tanh_srelu"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel "
+              "sharding is a design note); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from moe_grouped_scaled_amd import _native as N
+    from moe_grouped_scaled_amd.expert_mlp import ExpertMLP, gemm_flops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    d = workloads.make("mlp_step", seed=0, act=args.act)
+    splits = list(map(int, d["splits"]))
+    e, h, f = 16, d["hidden"], d["ffn"]
+    m = int(sum(splits))
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x1, w1, w2, b1, b2, dy2 = (dev(d[k]) for k in ("x1", "w1", "w2", "b1", "b2", "dy2"))
+    p = torch.from_numpy(d["p"]).cuda()
+    del d
+
+    # recompute memory drop, measured between forward and backward
+    held = {}
+    for rc in (False, True):
+        mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=rc, delay_wgrad=True, s=2.0)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        y = mlp.forward(x1, p, splits)
+        torch.cuda.synchronize()
+        held[rc] = torch.cuda.memory_allocated() - base
+        mlp.backward(dy2)
+        mlp.backward_dw()
+        del y, mlp
+    col_rows = m  # every expert's token count is a multiple of 32
+    drop_closed = col_rows * f + col_rows * f // 32 if args.fmt == "mxfp8" else col_rows * f // 2 + col_rows * f // 16
+
+    mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=True, delay_wgrad=True, s=2.0)
+
+    def step():
+        mlp.forward(x1, p, splits)
+        mlp.backward(dy2)
+        mlp.backward_dw()
+
+    for _ in range(args.warmup):
+        step()
+    timer = Timer(N)
+    torch.cuda.synchronize()
+    timer.enabled = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.enabled = False
+    dur = timer.durations()
+
+    ms_per_step = wall / args.steps * 1e3
+    flops_step = gemm_flops(m, h, f, f)
+    value = flops_step / (wall / args.steps) / 1e12
+
+    gemm_t = []
+    for tag in ("gemm_fprop", "gemm_dgrad", "gemm_wgrad"):
+        gemm_t += dur.get(tag, [])
+    flops_launch = 2 * m * h * f          # every one of the six GEMMs has this size here
+    gemm_avg = float(np.mean(gemm_t))
+    gemm_tflops = flops_launch / gemm_avg / 1e12
+    peak = MFMA_PEAK_TFLOPS[args.fmt]
+    fwd_b = act_fwd_bytes(m, f, f, args.fmt, row=True, col=False)
+    bwd_b = act_bwd_bytes(m, f, f, args.fmt, dense=True, row=True, col=True, dprobs=True, recompute=True)
+    t_fwd = float(np.mean(dur["grouped_scaled_act_fwd"]))
+    t_bwd = float(np.mean(dur["grouped_scaled_act_bwd"]))
+    kernels = {
+        "act_fwd": {"GB/s": fwd_b / t_fwd / 1e9, "frac_hbm": fwd_b / t_fwd / 1e9 / HBM_PEAK_GBPS,
+                    "us": t_fwd * 1e6, "bytes": fwd_b},
+        "act_bwd": {"GB/s": bwd_b / t_bwd / 1e9, "frac_hbm": bwd_b / t_bwd / 1e9 / HBM_PEAK_GBPS,
+                    "us": t_bwd * 1e6, "bytes": bwd_b},
+        "gemm": {"TFLOP/s": gemm_tflops, "frac_mfma": gemm_tflops / peak, "us_avg": gemm_avg * 1e6,
+                 "flops_per_launch": flops_launch,
+                 "us_by_mode": {t: float(np.mean(dur[t])) * 1e6 for t in ("gemm_fprop", "gemm_dgrad", "gemm_wgrad") if t in dur}},
+        "mx_quantize_us": float(np.mean(dur["grouped_mx_quantize"])) * 1e6,
+        "col_sum_us": float(np.mean(dur["grouped_col_sum"])) * 1e6,
+    }
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8" if args.fmt == "mxfp8" else "fp4", "data": "synthetic",
+        "config": {"workload": "expert-MLP train step: 16 experts x 2048 tokens, hidden 4096, ffn 4096, "
+                               "%s, %s, bias, recompute on, delayed wgrad" % (args.act, args.fmt.upper()),
+                   "experts": e, "tokens": m, "hidden": h, "ffn": f, "recipe": args.fmt, "act": args.act},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / peak, "traffic": None},
+        "kernels": kernels,
+        "recompute_memory_drop_bytes": {"measured": held[False] - held[True], "closed_form": drop_closed},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.act, args.fmt)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

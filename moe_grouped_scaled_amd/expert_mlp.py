@@ -1,0 +1,140 @@
+"""One MoE expert-MLP training step (FC1 -> per-row scaled activation -> FC2) driven through the C ABI.
+
+Sources:
+  * page "Activation + GroupedLinear Fusion for MOE", sequence diagram: forward = fused scaled
+    activation + grouped quantize, then the FC2 grouped GEMM, saving (input_, scales); backward = FC2
+    backward giving dL/d(act_out * scales), then the fused activation backward giving (grouped_dy,
+    dense_dy, grad_scales), then FC1's backward.
+  * page "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU", Description: with
+    activation recompute the forward keeps only the BF16 FC1 output and the backward regenerates FC2's
+    input from it; forward, dgrad, dprobs and FC1 wgrad are unchanged; memory drops between forward and
+    backward; bias and delayed weight-gradient computation change what wgrad consumes, and the
+    regenerated tensor must live until the delayed wgrad runs.
+
+Every arithmetic step runs in the library's HIP kernels; this module only allocates torch buffers,
+orders the calls and decides what is kept between forward and backward.  Tensor shapes:
+  x1 [M, H] BF16, probs [M] FP32, w1 [E, F_in, H], b1 [E, F_in], w2 [E, H, F], b2 [E, H] (BF16),
+  with F_in = F for unary activations and 2 F for gated ones ([gate | up]).
+"""
+
+import torch
+
+from . import _native as N
+
+GATED = ("swiglu", "clamped_swiglu")
+
+
+class ExpertMLP:
+    def __init__(self, kind, fmt, w1, w2, b1=None, b2=None, recompute=False, delay_wgrad=False,
+                 s=2.0, limit=7.0, alpha=1.0, beta=0.0):
+        self.kind, self.fmt = kind, fmt
+        self.w1, self.w2, self.b1, self.b2 = w1, w2, b1, b2
+        self.e, self.f_in, self.h = w1.shape
+        self.f = w2.shape[2]
+        assert w2.shape == (self.e, self.h, self.f)
+        assert self.f_in == (2 * self.f if kind in GATED else self.f)
+        self.recompute, self.delay_wgrad = recompute, delay_wgrad
+        self.act = N.act_params(kind, s=s, limit=limit, alpha=alpha, beta=beta)
+        self.ctx = None
+        self.pending_wgrad = None
+        # which fused outputs each pass requested (the recompute path writes FC2's columnwise input
+        # in the backward launch instead of the forward one)
+        self.trace = {"fwd_act_col": 0, "bwd_act_col": 0}
+
+    # ------------------------------------------------------------------ helpers
+    def _quant(self, x, splits, width, row=True, col=True):
+        qr = N.QTensor(self.fmt, False, splits, width) if row else None
+        qc = N.QTensor(self.fmt, True, splits, width) if col else None
+        amax = torch.empty(len(splits), dtype=torch.float32, device="cuda") if self.fmt == "nvfp4" else None
+        N.grouped_mx_quantize(self.fmt, splits, width, x, qr, qc, amax)
+        return qr, qc
+
+    def _amax_buf(self, n):
+        return torch.empty(n, dtype=torch.float32, device="cuda") if self.fmt == "nvfp4" else None
+
+    # ------------------------------------------------------------------ forward
+    def forward(self, x1, probs, splits):
+        e, h, f, f_in = self.e, self.h, self.f, self.f_in
+        m = x1.shape[0]
+        fmt = self.fmt
+        wsplit1, wsplit2 = [f_in] * e, [h] * e
+        x1_row, x1_col = self._quant(x1, splits, h)                         # FC1 fprop / FC1 wgrad
+        w1_row, w1_col = self._quant(self.w1.view(e * f_in, h), wsplit1, h)  # fprop / dgrad copies
+        y1 = torch.empty((m, f_in), dtype=torch.bfloat16, device="cuda")
+        N.grouped_gemm_mx("fprop", fmt, splits, m, f_in, h, x1_row, w1_row, y1, bias=self.b1)
+        del x1_row, w1_row
+        a_row = N.QTensor(fmt, False, splits, f)
+        a_col = None if self.recompute else N.QTensor(fmt, True, splits, f)
+        a_amax = self._amax_buf(e)
+        N.grouped_scaled_act_fwd(self.act, fmt, splits, f_in, y1, probs, a_row, a_col, a_amax)
+        self.trace["fwd_act_col"] += a_col is not None
+        w2_row, w2_col = self._quant(self.w2.view(e * h, f), wsplit2, f)
+        y2 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
+        N.grouped_gemm_mx("fprop", fmt, splits, m, h, f, a_row, w2_row, y2, bias=self.b2)
+        del a_row, w2_row
+        self.ctx = dict(splits=list(map(int, splits)), m=m, y1=y1, probs=probs, a_col=a_col,
+                        a_amax=a_amax, x1_col=x1_col, w1_col=w1_col, w2_col=w2_col)
+        return y2
+
+    # ------------------------------------------------------------------ backward
+    def backward(self, dy2):
+        c = self.ctx
+        splits, m, fmt = c["splits"], c["m"], self.fmt
+        e, h, f, f_in = self.e, self.h, self.f, self.f_in
+        dy2_row, dy2_col = self._quant(dy2, splits, h)
+        da = torch.empty((m, f), dtype=torch.bfloat16, device="cuda")
+        N.grouped_gemm_mx("dgrad", fmt, splits, m, f, h, dy2_row, c["w2_col"], da)
+        del dy2_row
+        dy1_dense = torch.empty((m, f_in), dtype=torch.bfloat16, device="cuda") if self.b1 is not None else None
+        dy1_row = N.QTensor(fmt, False, splits, f_in)
+        dy1_col = N.QTensor(fmt, True, splits, f_in)
+        dprobs = torch.empty(m, dtype=torch.float32, device="cuda")
+        a_col = c["a_col"]
+        if self.recompute:
+            a_col = N.QTensor(fmt, True, splits, f)
+            self.trace["bwd_act_col"] += 1
+        N.grouped_scaled_act_bwd(self.act, fmt, splits, f_in, c["y1"], da, c["probs"], dx=dy1_dense,
+                                 dx_row=dy1_row, dx_col=dy1_col, dx_group_amax=self._amax_buf(e),
+                                 dprobs=dprobs, act_col=a_col if self.recompute else None,
+                                 saved_group_amax=c["a_amax"])
+        del da
+        dx1 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
+        N.grouped_gemm_mx("dgrad", fmt, splits, m, h, f_in, dy1_row, c["w1_col"], dx1)
+        del dy1_row
+        # what the weight gradients consume stays alive until backward_dw (possibly delayed)
+        self.pending_wgrad = dict(splits=splits, m=m, dy2=dy2, dy2_col=dy2_col, a_col=a_col,
+                                  dy1_col=dy1_col, x1_col=c["x1_col"], dy1_dense=dy1_dense)
+        self.ctx = None
+        grads = {"dx1": dx1, "dprobs": dprobs}
+        if not self.delay_wgrad:
+            grads.update(self.backward_dw())
+        return grads
+
+    def backward_dw(self, dw1=None, dw2=None, accumulate=False):
+        """Weight (and bias) gradients from the kept columnwise copies; FP32 results."""
+        p = self.pending_wgrad
+        assert p is not None, "backward_dw() without a pending backward"
+        splits, m, fmt = p["splits"], p["m"], self.fmt
+        e, h, f, f_in = self.e, self.h, self.f, self.f_in
+        if dw2 is None:
+            dw2 = torch.empty((e, h, f), dtype=torch.float32, device="cuda")
+        if dw1 is None:
+            dw1 = torch.empty((e, f_in, h), dtype=torch.float32, device="cuda")
+        N.grouped_gemm_mx("wgrad", fmt, splits, h, f, m, p["dy2_col"], p["a_col"], dw2, accumulate=accumulate)
+        N.grouped_gemm_mx("wgrad", fmt, splits, f_in, h, m, p["dy1_col"], p["x1_col"], dw1, accumulate=accumulate)
+        out = {"dw1": dw1, "dw2": dw2}
+        if self.b2 is not None:
+            db2 = torch.empty((e, h), dtype=torch.float32, device="cuda")
+            N.grouped_col_sum(splits, h, p["dy2"], db2)
+            out["db2"] = db2
+        if self.b1 is not None:
+            db1 = torch.empty((e, f_in), dtype=torch.float32, device="cuda")
+            N.grouped_col_sum(splits, f_in, p["dy1_dense"], db1)
+            out["db1"] = db1
+        self.pending_wgrad = None
+        return out
+
+
+def gemm_flops(m, h, f, f_in):
+    """FLOPs of the six grouped GEMMs of one step (fprop, dgrad and wgrad of FC1 and FC2)."""
+    return 2 * m * (h * f_in + f * h) * 3

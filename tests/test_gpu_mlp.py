@@ -1,0 +1,127 @@
+"""The expert-MLP training step on the GPU: parity with the oracle step, the recompute twin (bitwise
+equal outputs, measured memory drop), delayed weight gradients and bias."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import mlp as M
+from tests.helpers import bf16_f64, bf16_host, f32, rel_rms, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _inputs(kind, e, splits, h, f, seed):
+    rng = np.random.default_rng(seed)
+    f_in = 2 * f if kind in ("swiglu", "clamped_swiglu") else f
+    m = int(np.sum(splits))
+    return dict(x1=workloads.normal_bf16(rng, (m, h)), w1=workloads.normal_bf16(rng, (e, f_in, h), 0.05),
+                w2=workloads.normal_bf16(rng, (e, h, f), 0.05), b1=workloads.normal_bf16(rng, (e, f_in), 0.05),
+                b2=workloads.normal_bf16(rng, (e, h), 0.05), p=workloads.uniform_f32(rng, m),
+                dy2=workloads.normal_bf16(rng, (m, h)), splits=np.asarray(splits, np.int64))
+
+
+def _run_gpu(kind, fmt, d, recompute, delay, bias=True):
+    import torch
+    from moe_grouped_scaled_amd.expert_mlp import ExpertMLP
+    w1, w2 = to_dev_bf16(d["w1"]), to_dev_bf16(d["w2"])
+    b1 = to_dev_bf16(d["b1"]) if bias else None
+    b2 = to_dev_bf16(d["b2"]) if bias else None
+    x1, p, dy2 = to_dev_bf16(d["x1"]), to_dev(d["p"]), to_dev_bf16(d["dy2"])
+    mlp = ExpertMLP(kind, fmt, w1, w2, b1, b2, recompute=recompute, delay_wgrad=delay)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    y2 = mlp.forward(x1, p, list(d["splits"]))
+    torch.cuda.synchronize()
+    held = torch.cuda.memory_allocated() - base
+    g = mlp.backward(dy2)
+    if delay:
+        assert "dw1" not in g
+        g.update(mlp.backward_dw())
+    torch.cuda.synchronize()
+    out = {"y2": bf16_host(y2), "dx1": bf16_host(g["dx1"]), "dprobs": f32(g["dprobs"]),
+           "dw1": f32(g["dw1"]), "dw2": f32(g["dw2"]), "held": held, "trace": dict(mlp.trace)}
+    if bias:
+        out["db1"], out["db2"] = f32(g["db1"]), f32(g["db2"])
+    return out
+
+
+@pytest.mark.parametrize("kind,fmt", [("srelu", "mxfp8"), ("tanh_srelu", "mxfp8"), ("srelu", "nvfp4"),
+                                      ("tanh_srelu", "nvfp4"), ("swiglu", "mxfp8")])
+def test_mlp_step_matches_oracle(torch_mod, kind, fmt):
+    e, splits, h, f = 4, [64, 0, 96, 37], 128, 128
+    d = _inputs(kind, e, splits, h, f, seed=3)
+    got = _run_gpu(kind, fmt, d, recompute=True, delay=True)
+    ref = M.mlp_step(kind, fmt, list(splits), bf16_f64(d["x1"]), bf16_f64(d["w1"]), bf16_f64(d["b1"]),
+                     bf16_f64(d["w2"]), bf16_f64(d["b2"]), d["p"].astype(np.float64), bf16_f64(d["dy2"]),
+                     act_params={"s": 2.0} if kind == "tanh_srelu" else None)
+    # chained quantities: the oracle's own BF16 / quantization roundings feed its later steps, so rare
+    # bin flips propagate; relative RMS stays far below the quantization error itself
+    tol = {"y2": 5e-3, "dx1": 1e-2, "dprobs": 1e-2, "dw1": 1e-2, "dw2": 5e-3, "db1": 1e-2, "db2": 1e-5}
+    vals = {"y2": bf16_f64(got["y2"]), "dx1": bf16_f64(got["dx1"]), "dprobs": got["dprobs"],
+            "dw1": got["dw1"], "dw2": got["dw2"], "db1": got["db1"], "db2": got["db2"]}
+    refs = {"y2": ref["y2"], "dx1": ref["dx1"], "dprobs": ref["dp"], "dw1": ref["dw1"], "dw2": ref["dw2"],
+            "db1": ref["db1"], "db2": ref["db2"]}
+    errs = {k: rel_rms(vals[k], refs[k]) for k in tol}
+    print(kind, fmt, {k: "%.2e" % v for k, v in errs.items()})
+    for k in tol:
+        assert errs[k] <= tol[k], (k, errs[k])
+    assert np.all(got["dw1"][1] == 0) and np.all(got["dw2"][1] == 0)   # empty expert
+
+
+@pytest.mark.parametrize("kind,fmt", [("srelu", "mxfp8"), ("tanh_srelu", "mxfp8"), ("srelu", "nvfp4"),
+                                      ("tanh_srelu", "nvfp4")])
+def test_recompute_twin_full_size(torch_mod, kind, fmt):
+    """The full step at 16 experts x 2048 tokens, hidden 4096, ffn 4096, bias on, delayed wgrad:
+    recompute on vs off gives bitwise-equal forward, dgrad, dprobs and FC1 wgrad; FC2 wgrad within the
+    pages' deviation bounds (here exactly equal, since both runs activate the same BF16 FC1 output);
+    the memory held between forward and backward drops by the closed-form size of FC2's columnwise
+    input; and the two runs took different paths (forward vs backward wrote that input)."""
+    e, h, f = 16, 4096, 4096
+    splits = [2048] * e
+    d = _inputs(kind, e, splits, h, f, seed=5)
+    off = _run_gpu(kind, fmt, d, recompute=False, delay=True)
+    on = _run_gpu(kind, fmt, d, recompute=True, delay=True)
+    for k in ("y2", "dx1", "dprobs", "dw1", "db1", "db2"):
+        assert np.array_equal(on[k], off[k]), k
+    with open(os.path.join(GOLDEN, "recompute_deviation_gb300.json")) as fh:
+        rows = json.load(fh)["rows"]
+    bound = [r for r in rows if r["recipe"] == fmt and r["act"] == kind][0]
+    dev = rel_rms(on["dw2"], off["dw2"])
+    diff = on["dw2"] - off["dw2"]
+    rms = np.sqrt(np.mean(off["dw2"] ** 2))
+    assert dev * 100 <= bound["rms_pct"]
+    assert np.max(np.abs(diff)) / rms * 100 <= bound["max_abs_pct"]
+    assert abs(np.mean(diff)) / rms <= 0.01
+    drop = off["held"] - on["held"]
+    want = M.recompute_memory_drop(fmt, splits, f) + (512 if fmt == "nvfp4" else 0)
+    assert drop == want, (drop, want)
+    assert off["trace"] == {"fwd_act_col": 1, "bwd_act_col": 0}
+    assert on["trace"] == {"fwd_act_col": 0, "bwd_act_col": 1}
+
+
+def test_delayed_wgrad_equals_immediate(torch_mod):
+    e, splits, h, f = 4, [96, 32, 0, 160], 256, 256
+    d = _inputs("srelu", e, splits, h, f, seed=7)
+    a = _run_gpu("srelu", "mxfp8", d, recompute=True, delay=True)
+    b = _run_gpu("srelu", "mxfp8", d, recompute=True, delay=False)
+    for k in ("y2", "dx1", "dprobs", "dw1", "dw2", "db1", "db2"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_no_bias_variant(torch_mod):
+    e, splits, h, f = 2, [64, 64], 128, 128
+    d = _inputs("srelu", e, splits, h, f, seed=8)
+    a = _run_gpu("srelu", "mxfp8", d, recompute=False, delay=False, bias=False)
+    assert "db1" not in a and np.isfinite(a["dw1"]).all()
