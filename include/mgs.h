@@ -24,14 +24,18 @@
  *
  * Quantized tensor layouts (mgs_qbuf), for a logical [M x W] tensor quantized along W:
  *   MXFP8 (E4M3 elements, E8M0 scale per 32):
- *     rowwise : data u8 [M, W]                      scales u8 [M, W/32]
+ *     rowwise : data u8 [M, W]                      scales: K-step grouped over [M, W]
  *     colwise : group g at data + W*coff[g]:        data [W, mp_g]   (tokens contiguous)
- *               group g at scales + W*coff[g]/32:   scales [W, mp_g/32]
+ *               group g at scales + W*coff[g]/32:   scales: K-step grouped over [W, mp_g]
  *   NVFP4 (E2M1 elements two per byte, element 2i in the low nibble; E4M3 scale per 16; FP32 per group):
  *     rowwise : data u8 [M, W/2]                    scales u8 [M, W/16]   group_scale f32 [E]
  *     colwise : group g at data + W*coff[g]/2:      data [W, mp_g/2]
  *               group g at scales + W*coff[g]/16:   scales [W, mp_g/16]   group_scale f32 [E]
- *   where mp_g = roundup(m_g, 32) and coff[g] = sum_{h<g} mp_h; padding tokens are written as zeros.
+ *   where mp_g = roundup(m_g, 128) and coff[g] = sum_{h<g} mp_h; padding tokens are written as zeros.
+ *   "K-step grouped" MXFP8 scales of an [R x K] matrix keep the four 32-block scales of each
+ *   128-wide K step together per row, steps outermost: the scale of (row r, block kb) is the byte
+ *   ((kb / 4) * R + r) * 4 + kb % 4; 4 * R * ceil(K / 128) bytes, unused bytes of a partial last
+ *   step zero.  (One aligned dword per row and K step: what the grouped GEMM stages per step.)
  *   MXFP8 scale of a block with maximum magnitude amax: E8M0 code clamp(floor(log2 amax) - 8 + 127, 0, 254)
  *   (0 for an all-zero block), element = E4M3(y / 2^(code-127)) rounded to nearest-even, saturated at 448.
  *   NVFP4 (per group g, FP32): S_enc = 2688 / amax_g (1 if amax_g == 0, FLT_MAX on overflow);
@@ -120,9 +124,9 @@ int64_t mgs_qtensor_nbytes(int32_t fmt, int32_t colwise, const mgs_groups* group
                            int32_t which);
 
 /* Fused forward: y = act(x) * p, quantized rowwise and/or columnwise in one pass over x.
- * [P2] Greptile summary, first bullet ("fuse per-row scale multiplication with activation and grouped
- * quantization into one pass") and sequence diagram (grouped_scaled_{swiglu,srelu}(x, scales,
- * quantizer, split_sizes) -> grouped_x).
+ * [P2] Greptile summary, first bullet (the per-row scale, the activation and the grouped quantization
+ * share one pass) and sequence diagram (the forward activation call takes x, the scales, the
+ * quantizer and split_sizes and returns the grouped quantized tensor).
  *   x_bf16     [M x width_in] BF16, row-major (required)
  *   probs      [M] FP32 per-row scale; NULL means 1 for every row
  *   out_row    rowwise qtensor of y [M x W_a] (W_a = width_in, or width_in/2 for gated kinds); nullable
@@ -164,8 +168,10 @@ int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width
 /* Grouped GEMM on quantized operands with FP32 accumulation.  [P2] Greptile summary, second bullet and
  * sequence diagram (GroupedLinear forward / backward on a pre-built grouped tensor).
  *   FPROP, DGRAD (grouped over M; m = M = sum of splits, n, k = reduction width, k % 32 == 0):
- *     A = rowwise qtensor [M x k]; B = [E x n x k] block-quantized along k with per-group stride
- *     (n*k data bytes) -- a rowwise weight for FPROP, the columnwise copy of the weight for DGRAD;
+ *     A = rowwise qtensor [M x k];
+ *     B (FPROP) = rowwise qtensor of the weight [E * n x k] (expert g owns rows g*n .. g*n + n - 1);
+ *     B (DGRAD) = columnwise qtensor of the weight [E * k x n] with split_sizes [k] * E (per expert
+ *                 [n x roundup(k, 128)], zero padded);
  *     C [M x n] row-major; bias_bf16 [E x n] optional.
  *   WGRAD (grouped over K; k = M = sum of splits; m, n = widths of A and B):
  *     A = columnwise qtensor of width m, B = columnwise qtensor of width n, both over the same groups;

@@ -43,7 +43,7 @@ __device__ __forceinline__ PanelInfo find_panel(const GroupTable& gt, int panel)
   pi.lpanel = panel - gt.panel_off[lo];
   pi.row0 = gt.row_off[lo] + PANEL_ROWS * pi.lpanel;
   int end = gt.row_off[lo + 1];
-  pi.nrows = min(PANEL_ROWS, end - pi.row0);
+  pi.nrows = min(PANEL_ROWS, end - pi.row0);  // <= 0 for the padding panels of the columnwise layout
   pi.coff = (int64_t)PANEL_ROWS * gt.panel_off[lo];
   pi.mp = (int64_t)PANEL_ROWS * (gt.panel_off[lo + 1] - gt.panel_off[lo]);
   return pi;
@@ -63,11 +63,14 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_c
 
 // Rowwise quantization of an 8 x 8 tile: rows r0 + i (i < 8, real when lr0 + i < nrows), columns
 // col..col+7 of a quantized tensor of width w.
+// MXFP8 scales are grouped per 128-wide K step (the byte of row r, 32-block kb of an R-row matrix
+// sits at ((kb / 4) * R + r) * 4 + kb % 4); `srows` is R.  Unused bytes of a partial last step are
+// written as zero by the lane that owns the row's last block.
 template <int FMT>
 __device__ __forceinline__ void emit_row(const float (&y)[8][8], uint8_t* __restrict__ data,
-                                         uint8_t* __restrict__ scales, int64_t w, int64_t r0,
-                                         int lr0, int nrows, int64_t col, bool valid, int lane,
-                                         float s_enc) {
+                                         uint8_t* __restrict__ scales, int64_t w, int64_t srows,
+                                         int64_t r0, int lr0, int nrows, int64_t col, bool valid,
+                                         int lane, float s_enc) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float m = 0.0f;
@@ -84,7 +87,13 @@ __device__ __forceinline__ void emit_row(const float (&y)[8][8], uint8_t* __rest
       q.y = e4m3x4(y[i][4] * inv, y[i][5] * inv, y[i][6] * inv, y[i][7] * inv);
       if (rv) {
         *reinterpret_cast<uint2*>(data + r * w + col) = q;
-        if (((lane >> 2) & 3) == 0) scales[r * (w >> 5) + (col >> 5)] = (uint8_t)c;
+        if (((lane >> 2) & 3) == 0) {
+          const int64_t kb = col >> 5, nkb = w >> 5;
+          scales[(((kb >> 2) * srows + r) << 2) + (kb & 3)] = (uint8_t)c;
+          if (kb == nkb - 1)
+            for (int64_t t = kb + 1; t < ((nkb + 3) & ~(int64_t)3); ++t)
+              scales[(((t >> 2) * srows + r) << 2) + (t & 3)] = 0;
+        }
       }
     } else {
       m = pair4_max(m);
@@ -124,7 +133,9 @@ __device__ __forceinline__ void emit_col(const float (&y)[8][8], uint8_t* __rest
       q.y = e4m3x4(y[4][j] * inv, y[5][j] * inv, y[6][j] * inv, y[7][j] * inv);
       if (valid) {
         *reinterpret_cast<uint2*>(data + w * pi.coff + cj * pi.mp + tok) = q;
-        if (lr0 == 0) scales[((w * pi.coff) >> 5) + cj * (pi.mp >> 5) + (tok >> 5)] = (uint8_t)c;
+        // K-step grouped scales of the group's [w x mp] matrix (mp is a multiple of 128)
+        const int64_t tb = tok >> 5;
+        if (lr0 == 0) scales[((w * pi.coff) >> 5) + (((tb >> 2) * w + cj) << 2) + (tb & 3)] = (uint8_t)c;
       }
     } else {
       m = pair1_max(m);
@@ -242,7 +253,7 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
   float y[8][8];
   compute_y<KIND>(aa, x, probs, width_in, wa, pi, lr0, col, valid, y);
   if (out.row_data)
-    emit_row<FMT>(y, out.row_data, out.row_scales, wa, pi.row0 + lr0, lr0, pi.nrows, col, valid, lane, s_enc);
+    emit_row<FMT>(y, out.row_data, out.row_scales, wa, gt.total_rows, pi.row0 + lr0, lr0, pi.nrows, col, valid, lane, s_enc);
   if (out.col_data) emit_col<FMT>(y, out.col_data, out.col_scales, wa, pi, lr0, col, valid, s_enc);
 }
 
@@ -340,9 +351,9 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
       }
     }
     if (dxq.row_data) {
-      emit_row<FMT>(d0, dxq.row_data, dxq.row_scales, width_in, r0, lr0, pi.nrows, col, valid, lane, s_dx);
+      emit_row<FMT>(d0, dxq.row_data, dxq.row_scales, width_in, gt.total_rows, r0, lr0, pi.nrows, col, valid, lane, s_dx);
       if constexpr (GATED)
-        emit_row<FMT>(d1, dxq.row_data, dxq.row_scales, width_in, r0, lr0, pi.nrows, wa + col, valid, lane, s_dx);
+        emit_row<FMT>(d1, dxq.row_data, dxq.row_scales, width_in, gt.total_rows, r0, lr0, pi.nrows, wa + col, valid, lane, s_dx);
     }
     if (dxq.col_data) {
       emit_col<FMT>(d0, dxq.col_data, dxq.col_scales, width_in, pi, lr0, col, valid, s_dx);

@@ -33,18 +33,24 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int LDS_STRIDE8 = BK + 16;     // bytes per LDS row, FP8 tiles
 constexpr int LDS_STRIDE16 = BK + 8;     // halfs per LDS row, FP16 tiles
+
+// One operand of a tile: `rows` valid rows starting at `data` (row stride `ld` bytes).  Scales:
+// MXFP8 keeps them grouped per 128-wide K step -- the byte of (row r, 32-block kb) of the scale
+// matrix is at sbase[((kb / 4) * srows + srow0 + r) * 4 + kb % 4]; NVFP4 keeps them row-major with
+// `sld` bytes per row starting at sbase + srow0 * sld.
+struct Operand {
+  const uint8_t* data;
+  int64_t ld;
+  const uint8_t* sbase;
+  int64_t srows, srow0, sld;
+  int rows;
+};
 
 struct TileJob {
   int g;
-  const uint8_t* a;   // first row of the A tile (row stride lda bytes)
-  const uint8_t* as;  // scales of that row (row stride K / block bytes)
-  const uint8_t* b;
-  const uint8_t* bs;
-  int64_t lda, ldb;   // data bytes per row
+  Operand a, b;
   int64_t k;          // reduction length (elements)
-  int arows, brows;   // valid rows of the A / B tile
   int64_t crow0, ccol0;
   float* c32;
   uint16_t* c16;
@@ -53,6 +59,12 @@ struct TileJob {
   const uint16_t* bias;  // bias row of the group (length N) or null
 };
 
+// Operand layouts by mode (E groups, elements per byte 1 for MXFP8 and 2 for NVFP4):
+//   FPROP / DGRAD A: rowwise qtensor [M x k]                 (scale matrix: all M rows)
+//   FPROP B:         rowwise qtensor [E * n x k]             (scale matrix: all E * n rows)
+//   DGRAD B:         columnwise qtensor of an [E * k x n] weight: per group [n x kp], kp = roundup(k, 128)
+//   WGRAD A / B:     columnwise qtensors of widths m / n: per group [m x mp_g] / [n x mp_g]
+template <int TM, int TN>
 __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable& tt, int tile) {
   int lo = 0, hi = tt.num_groups;  // tile_off[lo] <= tile < tile_off[hi]
   while (hi - lo > 1) {
@@ -64,26 +76,27 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
   j.g = g;
   const int lt = tile - tt.tile_off[g];
   const bool nv = ga.fmt == MGS_FMT_NVFP4;
-  const int sblk = nv ? 16 : 32;
-  int64_t arows_total, brows_total;
+  const int ediv = nv ? 2 : 1;            // elements per byte
+  const int sblk = nv ? 16 : 32;          // elements per scale
+  const int ntn = (int)((ga.n + TN - 1) / TN);
+  const int tm = lt / ntn, tn = lt - tm * ntn;
+  const int64_t brow0 = (int64_t)tn * TN;
+  int64_t arows_total;
   if (ga.mode == MGS_GEMM_WGRAD) {
-    // A = columnwise copy of width m, B = columnwise copy of width n; K = padded tokens of group g
     const int64_t coff = tt.tok_off[g];
     const int64_t mp = tt.tok_off[g + 1] - coff;
-    const int ntn = (int)((ga.n + BN - 1) / BN);
-    const int tm = lt / ntn, tn = lt - tm * ntn;
+    const int64_t arow0 = (int64_t)tm * TM;
     j.k = mp;
-    j.lda = nv ? mp / 2 : mp;
-    j.ldb = j.lda;
-    const int64_t arow0 = (int64_t)tm * BM, brow0 = (int64_t)tn * BN;
-    j.a = ga.a_data + (nv ? ga.m * coff / 2 : ga.m * coff) + arow0 * j.lda;
-    j.as = ga.a_scales + ga.m * coff / sblk + arow0 * (mp / sblk);
-    j.b = ga.b_data + (nv ? ga.n * coff / 2 : ga.n * coff) + brow0 * j.ldb;
-    j.bs = ga.b_scales + ga.n * coff / sblk + brow0 * (mp / sblk);
+    j.a.ld = j.b.ld = mp / ediv;
+    j.a.data = ga.a_data + ga.m * coff / ediv + arow0 * j.a.ld;
+    j.b.data = ga.b_data + ga.n * coff / ediv + brow0 * j.b.ld;
+    j.a.sbase = ga.a_scales + ga.m * coff / sblk;
+    j.b.sbase = ga.b_scales + ga.n * coff / sblk;
+    j.a.srows = ga.m; j.a.srow0 = arow0;
+    j.b.srows = ga.n; j.b.srow0 = brow0;
+    j.a.sld = j.b.sld = mp / sblk;
     arows_total = ga.m - arow0;
-    brows_total = ga.n - brow0;
     j.crow0 = arow0;
-    j.ccol0 = brow0;
     j.ldc = ga.n;
     const int64_t cbase = (int64_t)g * ga.m * ga.n;
     j.c32 = ga.c_f32 ? reinterpret_cast<float*>(ga.c) + cbase : nullptr;
@@ -92,27 +105,40 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
   } else {
     const int64_t r0 = tt.tok_off[g];
     const int64_t mg = tt.tok_off[g + 1] - r0;
-    const int ntn = (int)((ga.n + BN - 1) / BN);
-    const int tm = lt / ntn, tn = lt - tm * ntn;
+    const int64_t arow0 = r0 + (int64_t)tm * TM;
     j.k = ga.k;
-    j.lda = nv ? ga.k / 2 : ga.k;
-    j.ldb = j.lda;
-    const int64_t arow0 = r0 + (int64_t)tm * BM, brow0 = (int64_t)tn * BN;
-    j.a = ga.a_data + arow0 * j.lda;
-    j.as = ga.a_scales + arow0 * (ga.k / sblk);
-    j.b = ga.b_data + (int64_t)g * ga.n * j.ldb + brow0 * j.ldb;
-    j.bs = ga.b_scales + ((int64_t)g * ga.n + brow0) * (ga.k / sblk);
-    arows_total = mg - (int64_t)tm * BM;
-    brows_total = ga.n - brow0;
+    j.a.ld = ga.k / ediv;
+    j.a.data = ga.a_data + arow0 * j.a.ld;
+    j.a.sbase = ga.a_scales;
+    j.a.srows = tt.tok_off[tt.num_groups];
+    j.a.srow0 = arow0;
+    j.a.sld = ga.k / sblk;
+    if (ga.mode == MGS_GEMM_FPROP) {
+      j.b.ld = ga.k / ediv;
+      j.b.data = ga.b_data + ((int64_t)g * ga.n + brow0) * j.b.ld;
+      j.b.sbase = ga.b_scales;
+      j.b.srows = (int64_t)tt.num_groups * ga.n;
+      j.b.srow0 = (int64_t)g * ga.n + brow0;
+      j.b.sld = ga.k / sblk;
+    } else {
+      const int64_t kp = (ga.k + COL_ALIGN - 1) / COL_ALIGN * COL_ALIGN;
+      j.b.ld = kp / ediv;
+      j.b.data = ga.b_data + (int64_t)g * ga.n * j.b.ld + brow0 * j.b.ld;
+      j.b.sbase = ga.b_scales + (int64_t)g * ga.n * kp / sblk;
+      j.b.srows = ga.n;
+      j.b.srow0 = brow0;
+      j.b.sld = kp / sblk;
+    }
+    arows_total = mg - (int64_t)tm * TM;
     j.crow0 = arow0;
-    j.ccol0 = brow0;
     j.ldc = ga.n;
     j.c32 = ga.c_f32 ? reinterpret_cast<float*>(ga.c) : nullptr;
     j.c16 = ga.c_f32 ? nullptr : reinterpret_cast<uint16_t*>(ga.c);
     j.bias = ga.bias ? ga.bias + (int64_t)g * ga.n : nullptr;
   }
-  j.arows = (int)min<int64_t>(BM, arows_total);
-  j.brows = (int)min<int64_t>(BN, brows_total);
+  j.ccol0 = brow0;
+  j.a.rows = (int)min<int64_t>(TM, arows_total);
+  j.b.rows = (int)min<int64_t>(TN, ga.n - brow0);
   j.gfactor = nv ? ga.a_gscale[g] * ga.b_gscale[g] : 1.0f;
   return j;
 }
@@ -120,7 +146,7 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
 // Epilogue for one 16 x 16 fragment held as C[row][col0 .. col0 + 3] in each lane.
 __device__ __forceinline__ void store_frag(const TileJob& j, const GemmArgs& ga, int row, int col,
                                            v4f acc) {
-  if (row >= j.arows || col >= j.brows) return;  // brows is a multiple of 4 (N % 32 == 0)
+  if (row >= j.a.rows || col >= j.b.rows) return;  // b.rows is a multiple of 4 (N % 32 == 0)
   const int64_t gr = j.crow0 + row, gc = j.ccol0 + col;
   float v[4] = {acc[0] * j.gfactor, acc[1] * j.gfactor, acc[2] * j.gfactor, acc[3] * j.gfactor};
   if (j.bias) {
@@ -142,113 +168,174 @@ __device__ __forceinline__ void store_frag(const TileJob& j, const GemmArgs& ga,
   }
 }
 
+template <int TM, int TN>
 __device__ __forceinline__ void write_zero_tile(const TileJob& j, const GemmArgs& ga) {
   // empty group in WGRAD: dW_g = 0 (unchanged when accumulating)
   if (ga.accumulate) return;
-  for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
-    const int r = idx / BN, c = idx - (idx / BN) * BN;
-    if (r >= j.arows || c >= j.brows) continue;
+  for (int idx = threadIdx.x; idx < TM * TN; idx += blockDim.x) {
+    const int r = idx / TN, c = idx - (idx / TN) * TN;
+    if (r >= j.a.rows || c >= j.b.rows) continue;
     const int64_t gr = j.crow0 + r, gc = j.ccol0 + c;
     if (j.c32) j.c32[gr * j.ldc + gc] = 0.0f;
     else j.c16[gr * j.ldc + gc] = 0;
   }
 }
 
-// ------------------------------------------------------------------------------------ MXFP8 path
+// ------------------------------------------------------------------------------------ MXFP8, large tile
+//
+// 256 x 256 output tile per workgroup (4 waves in 2 x 2, each 128 x 128 = 8 x 8 MFMA fragments, 256
+// FP32 accumulators per lane held in AGPRs), K step 128.  Operands and their E8M0 scales go from
+// global memory straight into LDS with the direct-to-LDS loads (no VGPR staging), double-buffered:
+// the loads of step s + 1 are in flight while step s is multiplied (a scheduling barrier keeps the
+// MFMAs ahead of the wait for those loads).  LDS data rows are 128 bytes; the 16-byte chunk c of row
+// r is stored at chunk position c ^ (r & 7) so the 16 lanes reading one fragment column spread over
+// all banks.  Scales are staged as [row][4] bytes per step.  Rows past the tile edge load a clamped
+// in-range row (their outputs are not stored); K past the end of the reduction is zeroed in
+// registers in a peeled last step.
+constexpr int BM2 = 256, BN2 = 256;
+constexpr int DATA_BYTES = (BM2 + BN2) * BK;           // 64 KiB of operand data per stage
+constexpr int STAGE_BYTES = DATA_BYTES + (BM2 + BN2) * 4;  // + 2 KiB of scales
 
-__global__ __launch_bounds__(256) void gemm_mxfp8_kernel(GemmArgs ga, GemmTable tt) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * LDS_STRIDE8];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[BN * LDS_STRIDE8];
-  const TileJob j = make_job(ga, tt, blockIdx.x);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// a pointer that is the same in every lane, moved to scalar registers
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int xcd_remap_gemm(int b, int n) {
+  int q = n >> 3, r = n & 7;
+  int x = b & 7, i = b >> 3;
+  return x * q + min(x, r) + i;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
+  const int tile = xcd_remap_gemm(blockIdx.x, gridDim.x);
+  const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
   if (j.k == 0) {
-    write_zero_tile(j, ga);
+    write_zero_tile<BM2, BN2>(j, ga);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, r16 = lane & 15;
-  const int64_t nkb = j.k >> 5;  // 32-blocks along K
+  const int64_t nkb = j.k >> 5;
   const int nsteps = (int)((j.k + BK - 1) / BK);
 
-  // staging: thread loads rows (tid / 8) + 32 i, 16-byte chunk tid % 8 of the K step
-  const int srow = tid >> 3, schunk = tid & 7;
-  uint4 ra[4], rb[4];
-  auto gload = [&](int step) {
-    const int64_t kb = (int64_t)step * BK + schunk * 16;
-    const bool kok = kb < j.k;
+  // direct-to-LDS loads of step `st` into stage buffer `stg`: wave w fills data rows 64w .. 64w + 63
+  // of A and of B (8 instructions of 8 rows each per operand) and their scale bytes (4 instructions
+  // of 16 rows x 4 blocks each per operand).  Addresses are a wave-uniform 64-bit base (SGPRs) plus
+  // a 32-bit per-lane offset, computed once.
+  const uint8_t* abase = uniform_ptr(j.a.data);
+  const uint8_t* bbase = uniform_ptr(j.b.data);
+  const uint8_t* asbase = uniform_ptr(j.a.sbase);
+  const uint8_t* bsbase = uniform_ptr(j.b.sbase);
+  const int lrow = lane >> 3, pchunk = lane & 7;
+  uint32_t offa[8], offb[8], c16[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = srow + 32 * i;
-      ra[i] = (kok && row < j.arows) ? *reinterpret_cast<const uint4*>(j.a + row * j.lda + kb) : make_uint4(0, 0, 0, 0);
-      rb[i] = (kok && row < j.brows) ? *reinterpret_cast<const uint4*>(j.b + row * j.ldb + kb) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = srow + 32 * i;
-      *reinterpret_cast<uint4*>(lds_a + row * LDS_STRIDE8 + schunk * 16) = ra[i];
-      *reinterpret_cast<uint4*>(lds_b + row * LDS_STRIDE8 + schunk * 16) = rb[i];
-    }
-  };
-  // per-lane scales of the lane's fragment rows for one K step (K block = step * 4 + q)
-  int sa[4], sb[4];
-  auto sload = [&](int step) {
-    const int64_t kb = (int64_t)step * 4 + q;
-    const bool kok = kb < nkb;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int ar = wm * 64 + f * 16 + r16, br = wn * 64 + f * 16 + r16;
-      sa[f] = (kok && ar < j.arows) ? j.as[ar * nkb + kb] : 127;
-      sb[f] = (kok && br < j.brows) ? j.bs[br * nkb + kb] : 127;
-    }
-  };
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  gload(0);
-  sload(0);
-  lstore();
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    int csa[4], csb[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) { csa[f] = sa[f]; csb[f] = sb[f]; }
-    if (step + 1 < nsteps) {
-      gload(step + 1);
-      sload(step + 1);
-    }
-    v8i af[4], bfr[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint8_t* pa = lds_a + (wm * 64 + f * 16 + r16) * LDS_STRIDE8 + q * 16;
-      const uint8_t* pb = lds_b + (wn * 64 + f * 16 + r16) * LDS_STRIDE8 + q * 16;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(pa), a1 = *reinterpret_cast<const uint4*>(pa + 64);
-      const uint4 b0 = *reinterpret_cast<const uint4*>(pb), b1 = *reinterpret_cast<const uint4*>(pb + 64);
-      af[f] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      bfr[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-    }
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bfr[fn], af[fm], acc[fm][fn], 0, 0, 0, csb[fn], 0, csa[fm]);
-    __syncthreads();
-    if (step + 1 < nsteps) {
-      lstore();
-      __syncthreads();
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int row = wave * 64 + i * 8 + lrow;
+    const int ra = row < j.a.rows ? row : j.a.rows - 1;
+    const int rb = row < j.b.rows ? row : j.b.rows - 1;
+    c16[i] = (uint32_t)((pchunk ^ (row & 7)) << 4);
+    offa[i] = (uint32_t)(ra * j.a.ld);
+    offb[i] = (uint32_t)(rb * j.b.ld);
   }
+  // scale rows of this lane (one dword = the 4 block scales of a K step per row)
+  const int srow = wave * 64 + lane;
+  const uint32_t sra = (uint32_t)(j.a.srow0 + (srow < j.a.rows ? srow : j.a.rows - 1));
+  const uint32_t srb = (uint32_t)(j.b.srow0 + (srow < j.b.rows ? srow : j.b.rows - 1));
+  const uint32_t a_srows = (uint32_t)j.a.srows, b_srows = (uint32_t)j.b.srows;
+  auto issue = [&](int st, uint8_t* stg) {
+    const uint32_t k0 = (uint32_t)st * BK;
+    uint8_t* sa = stg;
+    uint8_t* sb = stg + BM2 * BK;
+    uint8_t* ssa = stg + DATA_BYTES;
+    uint8_t* ssb = ssa + BM2 * 4;
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+    for (int i = 0; i < 8; ++i) {
+      // tail chunks (at or past K) read chunk 0 of the step instead; they are zeroed in registers
+      const uint32_t kk = k0 + ((int64_t)(k0 + c16[i]) < j.k ? c16[i] : 0u);
+      __builtin_amdgcn_global_load_lds(abase + (offa[i] + kk), (lds_ptr_t)(sa + (wave * 8 + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bbase + (offb[i] + kk), (lds_ptr_t)(sb + (wave * 8 + i) * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(asbase + ((uint32_t)st * a_srows + sra) * 4u, (lds_ptr_t)(ssa + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(bsbase + ((uint32_t)st * b_srows + srb) * 4u, (lds_ptr_t)(ssb + wave * 256), 4, 0, 0);
+  };
+
+  v4f acc[8][8];
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
-      store_frag(j, ga, wm * 64 + fm * 16 + r16, wn * 64 + fn * 16 + 4 * q, acc[fm][fn]);
+  for (int fm = 0; fm < 8; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 8; ++fn) acc[fm][fn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // One K step from stage buffer `stg`: every fragment of the step is read from LDS first, then the
+  // direct-to-LDS loads of the next step are issued into the other buffer (the compiler makes LDS
+  // reads wait for all direct loads in flight, so they must not come after them), then the 64 MFMAs
+  // run while those loads are in flight.  With `tail`, K chunks at or past `rem` are zeroed.
+  auto step = [&](const uint8_t* stg, bool tail, int64_t rem, int next_st, uint8_t* next_stg) {
+    const uint8_t* sa = stg;
+    const uint8_t* sb = stg + BM2 * BK;
+    const uint8_t* ssa = stg + DATA_BYTES;
+    const uint8_t* ssb = ssa + BM2 * 4;
+    const bool lo_ok = !tail || 16 * q < rem, hi_ok = !tail || 64 + 16 * q < rem;
+    const uint32_t mlo = lo_ok ? 0xffffffffu : 0u, mhi = hi_ok ? 0xffffffffu : 0u;
+    v8i bfr[8], afr[8];
+    int csb[8], csa[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int row = wn * 128 + f * 16 + r16;
+      const uint8_t* pr = sb + row * BK;
+      const uint4 b0 = *reinterpret_cast<const uint4*>(pr + ((q ^ (row & 7)) << 4));
+      const uint4 b1 = *reinterpret_cast<const uint4*>(pr + (((4 + q) ^ (row & 7)) << 4));
+      bfr[f] = v8i{(int)(b0.x & mlo), (int)(b0.y & mlo), (int)(b0.z & mlo), (int)(b0.w & mlo),
+                   (int)(b1.x & mhi), (int)(b1.y & mhi), (int)(b1.z & mhi), (int)(b1.w & mhi)};
+      csb[f] = ssb[row * 4 + q];
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int row = wm * 128 + f * 16 + r16;
+      const uint8_t* pr = sa + row * BK;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(pr + ((q ^ (row & 7)) << 4));
+      const uint4 a1 = *reinterpret_cast<const uint4*>(pr + (((4 + q) ^ (row & 7)) << 4));
+      afr[f] = v8i{(int)(a0.x & mlo), (int)(a0.y & mlo), (int)(a0.z & mlo), (int)(a0.w & mlo),
+                   (int)(a1.x & mhi), (int)(a1.y & mhi), (int)(a1.z & mhi), (int)(a1.w & mhi)};
+      csa[f] = ssa[row * 4 + q];
+    }
+    if (next_st >= 0) issue(next_st, next_stg);
+#pragma unroll
+    for (int fm = 0; fm < 8; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 8; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[fn], afr[fm], acc[fm][fn], 0, 0, 0,
+                                                                       csb[fn], 0, csa[fm]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  issue(0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int64_t last_rem = j.k - (int64_t)(nsteps - 1) * BK;
+  const bool tail_step = last_rem < BK;
+  const int full_steps = tail_step ? nsteps - 1 : nsteps;
+  for (int st = 0; st < full_steps; ++st) {
+    const int nx = st + 1 < nsteps ? st + 1 : -1;
+    step(smem + (st & 1) * STAGE_BYTES, false, BK, nx, smem + ((st + 1) & 1) * STAGE_BYTES);
+  }
+  if (tail_step) step(smem + ((nsteps - 1) & 1) * STAGE_BYTES, true, last_rem, -1, nullptr);
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 8; ++fn)
+      store_frag(j, ga, wm * 128 + fm * 16 + r16, wn * 128 + fn * 16 + 4 * q, acc[fm][fn]);
 }
 
 // ------------------------------------------------------------------------------------ NVFP4 path
@@ -281,15 +368,14 @@ __device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, v2h scale) {
 __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable tt) {
   __shared__ __attribute__((aligned(16))) _Float16 lds_a[BM * LDS_STRIDE16];
   __shared__ __attribute__((aligned(16))) _Float16 lds_b[BN * LDS_STRIDE16];
-  const TileJob j = make_job(ga, tt, blockIdx.x);
+  const TileJob j = make_job<BM, BN>(ga, tt, blockIdx.x);
   if (j.k == 0) {
-    write_zero_tile(j, ga);
+    write_zero_tile<BM, BN>(j, ga);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, r16 = lane & 15;
-  const int64_t nsb = j.k >> 4;  // 16-blocks per row
   const int nsteps = (int)((j.k + BK - 1) / BK);
 
   // staging: a K step is 64 packed bytes per row; thread handles rows (tid / 8) + 32 i and the
@@ -303,11 +389,11 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = srow + 32 * i;
-      const bool av = kok && row < j.arows, bv = kok && row < j.brows;
-      ra[i] = av ? *reinterpret_cast<const uint2*>(j.a + row * j.lda + e0 / 2) : make_uint2(0, 0);
-      rb[i] = bv ? *reinterpret_cast<const uint2*>(j.b + row * j.ldb + e0 / 2) : make_uint2(0, 0);
-      sa[i] = av ? j.as[row * nsb + e0 / 16] : 0u;
-      sb[i] = bv ? j.bs[row * nsb + e0 / 16] : 0u;
+      const bool av = kok && row < j.a.rows, bv = kok && row < j.b.rows;
+      ra[i] = av ? *reinterpret_cast<const uint2*>(j.a.data + row * j.a.ld + e0 / 2) : make_uint2(0, 0);
+      rb[i] = bv ? *reinterpret_cast<const uint2*>(j.b.data + row * j.b.ld + e0 / 2) : make_uint2(0, 0);
+      sa[i] = av ? j.a.sbase[(j.a.srow0 + row) * j.a.sld + e0 / 16] : 0u;
+      sb[i] = bv ? j.b.sbase[(j.b.srow0 + row) * j.b.sld + e0 / 16] : 0u;
     }
   };
   auto lstore = [&]() {
@@ -365,13 +451,50 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable 
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& ga, const GemmTable& tt, hipStream_t st) {
-  if (tt.total_tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)tt.total_tiles);
-  if (ga.fmt == MGS_FMT_MXFP8)
-    hipLaunchKernelGGL(gemm_mxfp8_kernel, grid, dim3(256), 0, st, ga, tt);
-  else
-    hipLaunchKernelGGL(gemm_nvfp4_kernel, grid, dim3(256), 0, st, ga, tt);
+namespace {
+
+// Tile table for one launch: tiles of group g are [tile_off[g], tile_off[g+1]), ordered row-tile
+// major (column tiles fastest) so neighbouring tiles share their A rows.
+GemmTable make_table(const GemmArgs& ga, const GroupTable& gt, int tm, int tn) {
+  GemmTable tt;
+  tt.num_groups = gt.num_groups;
+  const int64_t ntn = (ga.n + tn - 1) / tn;
+  int64_t tiles = 0;
+  for (int g = 0; g < gt.num_groups; ++g) {
+    tt.tile_off[g] = (int32_t)tiles;
+    if (ga.mode == MGS_GEMM_WGRAD) {
+      tt.tok_off[g] = PANEL_ROWS * gt.panel_off[g];
+      tiles += ((ga.m + tm - 1) / tm) * ntn;
+    } else {
+      tt.tok_off[g] = gt.row_off[g];
+      const int64_t mg = gt.row_off[g + 1] - gt.row_off[g];
+      tiles += ((mg + tm - 1) / tm) * ntn;
+    }
+  }
+  tt.tok_off[gt.num_groups] = ga.mode == MGS_GEMM_WGRAD ? PANEL_ROWS * gt.panel_off[gt.num_groups]
+                                                         : gt.row_off[gt.num_groups];
+  tt.tile_off[gt.num_groups] = (int32_t)tiles;
+  tt.total_tiles = (int32_t)tiles;
+  return tt;
+}
+
+}  // namespace
+
+int64_t gemm_tile_count(const GemmArgs& ga, const GroupTable& gt) {
+  const int t = ga.fmt == MGS_FMT_MXFP8 ? BM2 : BM;
+  return make_table(ga, gt, t, t).total_tiles;
+}
+
+hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t st) {
+  if (ga.fmt == MGS_FMT_MXFP8) {
+    const GemmTable tt = make_table(ga, gt, BM2, BN2);
+    if (tt.total_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_mxfp8_256_kernel, dim3((unsigned)tt.total_tiles), dim3(256), 0, st, ga, tt);
+  } else {
+    const GemmTable tt = make_table(ga, gt, BM, BN);
+    if (tt.total_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_nvfp4_kernel, dim3((unsigned)tt.total_tiles), dim3(256), 0, st, ga, tt);
+  }
   return hipGetLastError();
 }
 

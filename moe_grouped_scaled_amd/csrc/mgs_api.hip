@@ -47,12 +47,13 @@ int build_groups(const mgs_groups* groups, mgs::GroupTable* gt, int64_t* total_r
     gt->row_off[g] = (int32_t)rows;
     gt->panel_off[g] = (int32_t)panels;
     rows += m;
-    panels += (m + mgs::PANEL_ROWS - 1) / mgs::PANEL_ROWS;
+    panels += (m + mgs::COL_ALIGN - 1) / mgs::COL_ALIGN * (mgs::COL_ALIGN / mgs::PANEL_ROWS);
     if (rows > INT32_MAX - 64) return fail(MGS_ERR_SHAPE, "total rows exceed 2^31 - 64");
   }
   gt->row_off[groups->num_groups] = (int32_t)rows;
   gt->panel_off[groups->num_groups] = (int32_t)panels;
   gt->num_panels = (int32_t)panels;
+  gt->total_rows = (int32_t)rows;
   *total_rows = rows;
   return MGS_OK;
 }
@@ -132,7 +133,11 @@ int64_t mgs_qtensor_nbytes(int32_t fmt, int32_t colwise, const mgs_groups* group
   const int64_t r = colwise ? (int64_t)mgs::PANEL_ROWS * gt.num_panels : rows;
   switch (which) {
     case MGS_NBYTES_DATA: ok(); return fmt == MGS_FMT_MXFP8 ? r * width : r * width / 2;
-    case MGS_NBYTES_SCALES: ok(); return fmt == MGS_FMT_MXFP8 ? r * width / 32 : r * width / 16;
+    case MGS_NBYTES_SCALES:
+      ok();
+      if (fmt == MGS_FMT_NVFP4) return r * width / 16;
+      // MXFP8 scales are grouped per 128-wide K step: 4 bytes per row and step
+      return colwise ? r * width / 32 : 4 * r * ((width + 127) / 128);
     case MGS_NBYTES_GROUP_SCALE: ok(); return fmt == MGS_FMT_MXFP8 ? 0 : 4 * (int64_t)gt.num_groups;
     default: return fail(MGS_ERR_INVALID_ARG, "unknown buffer selector %d", which);
   }
@@ -230,37 +235,14 @@ int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int
     return fail(MGS_ERR_INVALID_ARG, "NVFP4 operands need group_scale");
   if (!c) return fail(MGS_ERR_INVALID_ARG, "c is NULL");
   if ((rc = check_width(n, "n"))) return rc;
-  mgs::GemmTable tt;
-  std::memset(&tt, 0, sizeof tt);
-  tt.num_groups = gt.num_groups;
-  const int64_t ntn = (n + 127) / 128;
-  int64_t tiles = 0;
   if (mode == MGS_GEMM_WGRAD) {
     if ((rc = check_width(m, "m"))) return rc;
     if (k != rows) return fail(MGS_ERR_SHAPE, "WGRAD k = %lld must equal the split sum %lld", (long long)k, (long long)rows);
     if (bias_bf16) return fail(MGS_ERR_INVALID_ARG, "bias is not defined for WGRAD");
-    const int64_t ntm = (m + 127) / 128;
-    for (int g = 0; g < gt.num_groups; ++g) {
-      tt.tile_off[g] = (int32_t)tiles;
-      tt.tok_off[g] = mgs::PANEL_ROWS * gt.panel_off[g];
-      tiles += ntm * ntn;
-      if (tiles > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
-    }
-    tt.tok_off[gt.num_groups] = mgs::PANEL_ROWS * gt.panel_off[gt.num_groups];
   } else {
     if ((rc = check_width(k, "k"))) return rc;
     if (m != rows) return fail(MGS_ERR_SHAPE, "m = %lld must equal the split sum %lld", (long long)m, (long long)rows);
-    for (int g = 0; g < gt.num_groups; ++g) {
-      tt.tile_off[g] = (int32_t)tiles;
-      tt.tok_off[g] = gt.row_off[g];
-      const int64_t mg = gt.row_off[g + 1] - gt.row_off[g];
-      tiles += ((mg + 127) / 128) * ntn;
-      if (tiles > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
-    }
-    tt.tok_off[gt.num_groups] = gt.row_off[gt.num_groups];
   }
-  tt.tile_off[gt.num_groups] = (int32_t)tiles;
-  tt.total_tiles = (int32_t)tiles;
   mgs::GemmArgs ga{};
   ga.mode = mode;
   ga.fmt = fmt;
@@ -277,7 +259,8 @@ int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int
   ga.c_f32 = c_dtype == MGS_DTYPE_F32;
   ga.accumulate = accumulate != 0;
   ga.bias = static_cast<const uint16_t*>(bias_bf16);
-  return hip_status(mgs::launch_gemm(ga, tt, static_cast<hipStream_t>(stream)));
+  if (mgs::gemm_tile_count(ga, gt) > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
+  return hip_status(mgs::launch_gemm(ga, gt, static_cast<hipStream_t>(stream)));
 }
 
 int mgs_grouped_col_sum(const mgs_groups* groups, int64_t width, const void* x_bf16, float* out,

@@ -9,19 +9,24 @@
 
 namespace mgs {
 
-// Rows of one panel: a panel is 32 consecutive rows of one group, the unit of both the columnwise
-// quantization blocks (32 for MXFP8, 2 x 16 for NVFP4) and of the padded columnwise token layout.
+// Rows of one panel: a panel is 32 consecutive rows of one group, the unit of the columnwise
+// quantization blocks (32 for MXFP8, 2 x 16 for NVFP4).
 constexpr int PANEL_ROWS = 32;
+// The columnwise (token-contiguous) layout pads each group to a multiple of 128 tokens: a whole
+// number of 128-wide K steps of the weight-gradient GEMM.
+constexpr int COL_ALIGN = 128;
 // Output columns covered by one workgroup per iteration (4 waves x 128 columns).
 constexpr int TILE_COLS = 512;
 
 // Group bookkeeping passed by value in the kernel arguments.
-//   row_off[g]   = sum_{h<g} m_h                 (E + 1 entries)
-//   panel_off[g] = sum_{h<g} ceil(m_h / 32)      (E + 1 entries); the padded columnwise token offset
-//                  of group g is 32 * panel_off[g] and its padded length 32 * (panel_off[g+1] - panel_off[g]).
+//   row_off[g]   = sum_{h<g} m_h                            (E + 1 entries)
+//   panel_off[g] = sum_{h<g} roundup(m_h, 128) / 32         (E + 1 entries); the padded columnwise
+//                  token offset of group g is 32 * panel_off[g] and its padded length
+//                  32 * (panel_off[g+1] - panel_off[g]); panels past a group's last row are padding.
 struct GroupTable {
   int32_t num_groups;
   int32_t num_panels;
+  int32_t total_rows;
   int32_t row_off[MGS_MAX_GROUPS + 1];
   int32_t panel_off[MGS_MAX_GROUPS + 1];
 };
@@ -80,6 +85,8 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,
                           hipStream_t stream);
 
-hipError_t launch_gemm(const GemmArgs& ga, const GemmTable& tt, hipStream_t stream);
+// Builds the per-group tile table for the kernel variant of `ga.fmt` and launches it.
+hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t stream);
+int64_t gemm_tile_count(const GemmArgs& ga, const GroupTable& gt);
 
 }  // namespace mgs

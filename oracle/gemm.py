@@ -23,19 +23,20 @@ the CPU tests); the general case is the definition above.
 import numpy as np
 
 from .codecs import e2m1_decode, e4m3_decode, e8m0_decode, unpack_e2m1
-from .quant import MXFP8, NVFP4, col_offsets, group_offsets
+from .quant import MXFP8, NVFP4, col_offsets, group_offsets, mx_scales_from_kstep
 
 
 def dequant_rows(fmt, data, scales, rows, width, group_scale=None):
     """Dequantize a [rows x width] K-contiguous block-quantized matrix to float64.
 
-    ``group_scale`` (NVFP4 only) is a scalar S_dec applied to the whole matrix.
+    MXFP8 scales are in the K-step grouped layout of that matrix; ``group_scale`` (NVFP4 only) is a
+    scalar S_dec applied to the whole matrix.
     """
     if rows == 0:
         return np.zeros((0, width))
     if fmt == MXFP8:
         q = e4m3_decode(np.asarray(data, np.uint8).reshape(rows, width))
-        s = e8m0_decode(np.asarray(scales, np.uint8).reshape(rows, width // 32))
+        s = e8m0_decode(mx_scales_from_kstep(scales, rows, width))
         return q * np.repeat(s, 32, axis=1)
     codes = unpack_e2m1(np.asarray(data, np.uint8).reshape(rows, width // 2))
     q = e2m1_decode(codes)
@@ -44,7 +45,9 @@ def dequant_rows(fmt, data, scales, rows, width, group_scale=None):
 
 
 def dequant_row_grouped(fmt, data, scales, split_sizes, width, group_scale=None):
-    """Dequantize a rowwise grouped qtensor [M x width]; NVFP4 applies each group's S_dec."""
+    """Dequantize a rowwise grouped qtensor [M x width]; NVFP4 applies each group's S_dec.
+
+    MXFP8 scales are K-step grouped over the whole [M x width] matrix."""
     off = group_offsets(split_sizes)
     m = int(off[-1])
     if fmt == MXFP8:
@@ -73,6 +76,12 @@ def dequant_col_grouped(fmt, data, scales, split_sizes, width, group_scale=None)
         gs = None if group_scale is None else group_scale[g]
         mats.append(dequant_rows(fmt, d, s, width, mp, gs))
     return mats
+
+
+def dgrad_weight(col_mats, k):
+    """The columnwise copy of a weight, per group [n x roundup(k, 128)] with zero padding, as the
+    [n x k] DGRAD operand (the padding columns meet no input column)."""
+    return [np.asarray(w)[:, :k] for w in col_mats]
 
 
 def gemm_grouped_m(a, b_per_group, split_sizes, bias=None):

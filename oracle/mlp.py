@@ -29,6 +29,7 @@ from . import activations as act_mod
 from .codecs import bf16_bits_to_f64, f32, f32_to_bf16_bits
 from .gemm import (
     dequant_col_grouped,
+    dgrad_weight,
     dequant_row_grouped,
     gemm_grouped_k,
     gemm_grouped_m,
@@ -69,14 +70,14 @@ def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None):
     qx1 = _q(x1, splits, fmt, h)
     qw1 = _q(w1.reshape(e * f_in, h), wsplit_1, fmt, h)
     w1_row = qw1["row"].reshape(e, f_in, h)
-    w1_col = qw1["col"]                      # per expert [H x F_in]
+    w1_col = dgrad_weight(qw1["col"], f_in)  # per expert [H x F_in]
     y1 = _bf16(gemm_grouped_m(qx1["row"], list(w1_row), splits, bias=b1))
 
     a32 = act_mod.scaled_act_fwd(kind, y1, p, **act_params)
     qa = _q(a32, splits, fmt, f)
     qw2 = _q(w2.reshape(e * h, f), wsplit_2, fmt, f)
     w2_row = qw2["row"].reshape(e, h, f)
-    w2_col = qw2["col"]                      # per expert [F x H]
+    w2_col = dgrad_weight(qw2["col"], h)     # per expert [F x H]
     y2 = _bf16(gemm_grouped_m(qa["row"], list(w2_row), splits, bias=b2))
 
     qdy2 = _q(dy2, splits, fmt, h)

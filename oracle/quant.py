@@ -23,16 +23,22 @@ Readings (listed in the design notes):
     sf = f32(f32(amax_b / 6) * S_enc); s_b = E4M3(sf); d_b = decode(s_b); if d_b == 0 all codes are 0,
     else r_b = f32(S_enc / d_b) and code = E2M1(f32(y * r_b)).  S_dec = f32(1 / S_enc).
   * Columnwise layout: per group, the [m_g x W] slice is transposed to [W x m_g], rows padded with
-    zeros to roundup(m_g, 32) for both formats, and quantized along the (token) rows, so blocks never
-    straddle groups and a partial last block takes its amax over its real rows only.
+    zeros to roundup(m_g, 128) for both formats (a whole number of 128-token K steps of the weight-
+    gradient GEMM), and quantized along the (token) rows, so blocks never straddle groups and a
+    partial last block takes its amax over its real rows only.
   * E2M1 packing: element 2i in the low nibble.
 
 Buffer layouts produced here are the library's documented qtensor layouts:
-  rowwise MXFP8 : data u8 [M, W],                         scales u8 [M, W/32]
+  rowwise MXFP8 : data u8 [M, W],                         scales: K-step grouped over [M, W]
   rowwise NVFP4 : data u8 [M, W/2],                       scales u8 [M, W/16],  group_scale f32 [E]
-  colwise MXFP8 : per group g at data offset W*coff[g]:    data [W, mp_g],       scales [W, mp_g/32]
+  colwise MXFP8 : per group g at data offset W*coff[g]:    data [W, mp_g],
+                  scales at W*coff[g]/32:                  K-step grouped over [W, mp_g]
   colwise NVFP4 : per group g at data offset W*coff[g]/2: data [W, mp_g/2],     scales [W, mp_g/16]
-  with mp_g = roundup(m_g, 32) and coff[g] = sum_{h<g} mp_h.
+  with mp_g = roundup(m_g, 128) and coff[g] = sum_{h<g} mp_h.
+  "K-step grouped" (MXFP8 scales of an [R x K] matrix): the four 32-block scales of each 128-wide K
+  step are stored together per row, steps outermost -- the byte of (row r, block kb) is at
+  ((kb // 4) * R + r) * 4 + kb % 4, 4 * R * ceil(K / 128) bytes in all, unused bytes of a partial
+  last step zero.
 
 Parity: MXFP8 pinned (closed-form scale codes, exhaustive codec tests, M6 statistics).  The NVFP4
 FP32 sequence is a reading; it is pinned only by invariants (the block holding the group maximum gets
@@ -54,7 +60,7 @@ from .codecs import (
 MXFP8 = "mxfp8"
 NVFP4 = "nvfp4"
 BLOCK = {MXFP8: 32, NVFP4: 16}
-COL_ALIGN = 32
+COL_ALIGN = 128
 FLT_MAX = float(np.finfo(np.float32).max)
 
 
@@ -68,7 +74,7 @@ def group_offsets(split_sizes):
 
 
 def col_offsets(split_sizes):
-    """Padded token offsets of the columnwise layout: coff[g] = sum_{h<g} roundup(m_h, 32)."""
+    """Padded token offsets of the columnwise layout: coff[g] = sum_{h<g} roundup(m_h, 128)."""
     padded = [roundup(int(m), COL_ALIGN) for m in split_sizes]
     return np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
 
@@ -95,6 +101,28 @@ def mxfp8_quantize_rows(y32):
     x_scale = np.ldexp(1.0, code.astype(np.int64) - 127)  # 2^(c - 127)
     q = e4m3_encode(blocks / x_scale[..., None])
     return q.reshape(rows, w), code
+
+
+def mx_scales_to_kstep(scales_rk):
+    """Row-major [R, K/32] E8M0 codes -> the K-step grouped byte layout (flat, zero padded)."""
+    s = np.asarray(scales_rk, dtype=np.uint8)
+    r, nkb = s.shape
+    nsteps = (nkb + 3) // 4
+    out = np.zeros((nsteps, r, 4), dtype=np.uint8)
+    for kb in range(nkb):
+        out[kb // 4, :, kb % 4] = s[:, kb]
+    return out.reshape(-1)
+
+
+def mx_scales_from_kstep(flat, r, k):
+    """Inverse of mx_scales_to_kstep for an [R, K] matrix: returns [R, K/32] codes."""
+    nkb = k // 32
+    nsteps = (nkb + 3) // 4
+    a = np.asarray(flat, dtype=np.uint8).reshape(nsteps, r, 4)
+    out = np.zeros((r, nkb), dtype=np.uint8)
+    for kb in range(nkb):
+        out[:, kb] = a[kb // 4, :, kb % 4]
+    return out
 
 
 # ----------------------------------------------------------------------------- NVFP4
@@ -173,7 +201,7 @@ def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True):
             d = np.concatenate(parts_d) if parts_d else np.zeros((0, w // 2), np.uint8)
             s = np.concatenate(parts_s) if parts_s else np.zeros((0, w // 16), np.uint8)
         out["row_data"] = d.reshape(-1)
-        out["row_scales"] = s.reshape(-1)
+        out["row_scales"] = mx_scales_to_kstep(s) if fmt == MXFP8 else s.reshape(-1)
     if colwise:
         parts_d, parts_s = [], []
         for g in range(e):
@@ -185,6 +213,7 @@ def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True):
             yt[:, :m_g] = y[off[g]:off[g + 1]].T
             if fmt == MXFP8:
                 d_g, s_g = mxfp8_quantize_rows(yt)
+                s_g = mx_scales_to_kstep(s_g)
             else:
                 d_g, s_g = nvfp4_quantize_rows(yt, s_enc[g])
             parts_d.append(d_g.reshape(-1))
@@ -198,5 +227,7 @@ def qtensor_nbytes(fmt, colwise, split_sizes, width):
     """(data bytes, scale bytes) of a grouped qtensor in the documented layout."""
     rows = int(col_offsets(split_sizes)[-1]) if colwise else int(np.sum(split_sizes))
     if fmt == MXFP8:
-        return rows * width, rows * width // 32
+        if colwise:   # per group [width x mp_g], mp_g a multiple of 128
+            return rows * width, rows * width // 32
+        return rows * width, 4 * rows * ((width + 127) // 128)
     return rows * width // 2, rows * width // 16

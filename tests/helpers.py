@@ -12,6 +12,7 @@ Criteria (applied in the tests):
 import numpy as np
 
 from oracle import codecs
+from oracle.quant import mx_scales_from_kstep
 
 
 def to_dev_bf16(bits):
@@ -45,9 +46,10 @@ def bf16_f64(bits):
 # ---------------------------------------------------------------------------- dequantization views
 
 def mx_elementwise(data, scales, rows, width):
-    """Per-element (code, block scale value, dequantized value) of a [rows x width] MXFP8 block."""
+    """Per-element (code, block scale value, dequantized value) of a [rows x width] MXFP8 matrix
+    whose scales are in the K-step grouped layout."""
     q = np.asarray(data, np.uint8).reshape(rows, width)
-    s = codecs.e8m0_decode(np.asarray(scales, np.uint8).reshape(rows, width // 32))
+    s = codecs.e8m0_decode(mx_scales_from_kstep(scales, rows, width))
     s = np.repeat(s, 32, axis=1)
     return q, s, codecs.e4m3_decode(q) * s
 

@@ -86,7 +86,17 @@ def _row_view(fmt, data, scales, splits, width, gs):
 def _col_view(fmt, data, scales, splits, width, gs):
     coff = Q.col_offsets(splits)  # flat view: every block of the per-group [width x mp_g] layout
     if fmt == "mxfp8":
-        return mx_elementwise(data, scales, int(coff[-1]) * width // 32, 32)
+        views = []
+        for g in range(len(splits)):
+            mp = int(coff[g + 1] - coff[g])
+            if mp == 0:
+                continue
+            d0, s0 = width * int(coff[g]), width * int(coff[g]) // 32
+            views.append(mx_elementwise(data[d0:d0 + width * mp], scales[s0:s0 + width * mp // 32], width, mp))
+        if not views:
+            z = np.zeros((0, 1))
+            return z, z, z
+        return tuple(np.concatenate([v[i].reshape(-1) for v in views]) for i in range(3))
     parts = []
     for g in range(len(splits)):
         n_el = width * int(coff[g + 1] - coff[g])

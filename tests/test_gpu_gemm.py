@@ -64,8 +64,9 @@ def test_integer_codes_unit_scales_exact(N):
         c = np.vectorize(lambda t: enc[abs(int(t))])(v).astype(np.uint8)
         return c | np.where(v < 0, 0x80, 0).astype(np.uint8)
 
-    qa = {"row_data": codes(a_int).reshape(-1), "row_scales": np.full(m * k // 32, 127, np.uint8)}
-    qb = {"row_data": codes(b_int).reshape(-1), "row_scales": np.full(len(splits) * n * k // 32, 127, np.uint8)}
+    unit = lambda r: Q.mx_scales_to_kstep(np.full((r, k // 32), 127, np.uint8))
+    qa = {"row_data": codes(a_int).reshape(-1), "row_scales": unit(m)}
+    qb = {"row_data": codes(b_int).reshape(-1), "row_scales": unit(len(splits) * n)}
     A = dev_q(N, "mxfp8", False, splits, k, qa)
     B = dev_q(N, "mxfp8", False, [n] * len(splits), k, qb)
     c = torch.empty((m, n), dtype=torch.float32, device="cuda")
@@ -110,7 +111,8 @@ def test_fprop_dgrad(N, fmt, out_dtype):
     Ad = dev_q(N, fmt, False, splits, n, qdy)
     Bd = dev_q(N, fmt, True, [n] * e, k, qw)            # per group [k x n]
     dy_ref = G.dequant_row_grouped(fmt, qdy["row_data"], qdy["row_scales"], splits, n, qdy.get("group_scale"))
-    w_col = G.dequant_col_grouped(fmt, qw["col_data"], qw["col_scales"], [n] * e, k, qw.get("group_scale"))
+    w_col = G.dgrad_weight(G.dequant_col_grouped(fmt, qw["col_data"], qw["col_scales"], [n] * e, k,
+                                                 qw.get("group_scale")), n)
     ref_d = G.gemm_grouped_m(dy_ref, w_col, splits)
     cd = torch.empty((m, k), dtype=torch.float32, device="cuda")
     N.grouped_gemm_mx("dgrad", fmt, splits, m, k, n, Ad, Bd, cd)
@@ -172,8 +174,9 @@ def test_fc2_clamped_workload_sampled(N):
     groups = [g for g in np.argsort(-splits)[:2]] + [g for g in range(e) if 0 < splits[g] < 200][:1]
     from oracle import activations as Aa
     got_c = bf16_f64(bf16_host(c))
-    a_data, a_sc = qa.data.cpu().numpy(), qa.scales.cpu().numpy()
-    w_data, w_sc = qw.data.cpu().numpy(), qw.scales.cpu().numpy()
+    a_data = qa.data.cpu().numpy()
+    w_data = qw.data.cpu().numpy()
+    w_sc = Q.mx_scales_from_kstep(qw.scales.cpu().numpy(), e * h, k)
     for g in groups:
         rows = rng.choice(np.arange(off[g], off[g + 1]), size=min(16, int(splits[g])), replace=False)
         x_rows = bf16_f64(d["x"][rows])
@@ -185,7 +188,7 @@ def test_fc2_clamped_workload_sampled(N):
         w_g = bf16_f64(d["w2"][g])
         qwg = Q.quantize_grouped(w_g, [h], "mxfp8", colwise=False)
         assert np.array_equal(w_data.reshape(e * h, k)[g * h:(g + 1) * h].reshape(-1), qwg["row_data"])
-        assert np.array_equal(w_sc.reshape(e * h, k // 32)[g * h:(g + 1) * h].reshape(-1), qwg["row_scales"])
+        assert np.array_equal(w_sc[g * h:(g + 1) * h], Q.mx_scales_from_kstep(qwg["row_scales"], h, k))
         a_deq = G.dequant_rows("mxfp8", qrow["row_data"], qrow["row_scales"], len(rows), k)
         w_deq = G.dequant_rows("mxfp8", qwg["row_data"], qwg["row_scales"], h, k)
         ref = a_deq @ w_deq.T

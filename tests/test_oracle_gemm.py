@@ -5,6 +5,7 @@ import numpy as np
 from oracle import codecs, quant
 from oracle.gemm import (
     dequant_col_grouped,
+    dgrad_weight,
     dequant_row_grouped,
     dequant_rows,
     gemm_grouped_k,
@@ -27,8 +28,9 @@ def test_unit_scale_integer_gemm_is_exact_int_matmul():
     m, n, k = sum(splits), 48, 96
     a_int = rng.integers(-4, 5, (m, k))
     b_int = rng.integers(-4, 5, (len(splits), n, k))
-    a = dequant_rows(quant.MXFP8, _e4m3_int_codes(a_int), np.full(m * k // 32, 127, np.uint8), m, k)
-    bs = [dequant_rows(quant.MXFP8, _e4m3_int_codes(b_int[g]), np.full(n * k // 32, 127, np.uint8), n, k)
+    unit = lambda r: quant.mx_scales_to_kstep(np.full((r, k // 32), 127, np.uint8))
+    a = dequant_rows(quant.MXFP8, _e4m3_int_codes(a_int), unit(m), m, k)
+    bs = [dequant_rows(quant.MXFP8, _e4m3_int_codes(b_int[g]), unit(n), n, k)
           for g in range(len(splits))]
     c = gemm_grouped_m(a, bs, splits)
     off = quant.group_offsets(splits)
@@ -65,7 +67,9 @@ def test_dgrad_and_wgrad_through_transposed_copies_exact_for_representable_value
     dy_int = rng.integers(-4, 5, (m, n)).astype(np.float64)
     x_int = rng.integers(-4, 5, (m, k)).astype(np.float64)
     qw = quant.quantize_grouped(w_int.reshape(e * n, k), [n] * e, quant.MXFP8)
-    w_col = dequant_col_grouped(quant.MXFP8, qw["col_data"], qw["col_scales"], [n] * e, k)  # [K x N]
+    w_col = dequant_col_grouped(quant.MXFP8, qw["col_data"], qw["col_scales"], [n] * e, k)  # [K x NP]
+    assert w_col[0].shape == (k, 128) and np.all(w_col[0][:, n:] == 0)
+    w_col = dgrad_weight(w_col, n)
     qdy = quant.quantize_grouped(dy_int, splits, quant.MXFP8)
     dy_row = dequant_row_grouped(quant.MXFP8, qdy["row_data"], qdy["row_scales"], splits, n)
     dx = gemm_grouped_m(dy_row, w_col, splits)

@@ -45,7 +45,7 @@ def test_mxfp8_grouped_roundtrip_bound_and_layout(splits):
     assert q["col_data"].size == nd and q["col_scales"].size == ns
     # rowwise: each block dequantizes within half an E4M3 step of its values
     deq = dequant_row_grouped(quant.MXFP8, q["row_data"], q["row_scales"], splits, w)
-    xs = codecs.e8m0_decode(q["row_scales"].reshape(m, w // 32))
+    xs = codecs.e8m0_decode(quant.mx_scales_from_kstep(q["row_scales"], m, w))
     assert _mx_error_ok(deq, y, np.repeat(xs, 32, axis=1))
     # columnwise: element (token r of group g, column j) sits at [j, r] of group g's [w x mp_g] block
     mats = dequant_col_grouped(quant.MXFP8, q["col_data"], q["col_scales"], splits, w)
@@ -58,22 +58,39 @@ def test_mxfp8_grouped_roundtrip_bound_and_layout(splits):
         assert np.all(mat[:, m_g:] == 0)                         # padding is zero
         yt = y[off[g]:off[g + 1]].T
         s0 = w * coff[g] // 32
-        cs = codecs.e8m0_decode(q["col_scales"][s0:s0 + w * mp // 32].reshape(w, mp // 32))
+        cs_codes = quant.mx_scales_from_kstep(q["col_scales"][s0:s0 + w * mp // 32], w, mp)
+        cs = codecs.e8m0_decode(cs_codes)
         assert _mx_error_ok(mat[:, :m_g], yt, np.repeat(cs, 32, axis=1)[:, :m_g])
         # the column scale is the closed-form code of the amax over the block's real rows only
         for b in range(mp // 32):
             blk = np.abs(yt[:, 32 * b:min(32 * b + 32, m_g)])
-            want = quant.mxfp8_scale_code(blk.max(axis=1))
-            assert np.array_equal(q["col_scales"][s0:s0 + w * mp // 32].reshape(w, mp // 32)[:, b], want)
+            want = quant.mxfp8_scale_code(blk.max(axis=1)) if blk.shape[1] else np.zeros(w, np.uint8)
+            assert np.array_equal(cs_codes[:, b], want)   # all-padding blocks get code 0
+
+
+def test_kstep_scale_layout():
+    """Scale byte of (row r, block kb) sits at ((kb // 4) * R + r) * 4 + kb % 4; partial steps padded."""
+    codes = np.arange(5 * 3, dtype=np.uint8).reshape(5, 3) + 1       # R = 5 rows, K = 96 (3 blocks)
+    flat = quant.mx_scales_to_kstep(codes)
+    assert flat.size == 4 * 5 * 1
+    for r in range(5):
+        for kb in range(3):
+            assert flat[((kb // 4) * 5 + r) * 4 + kb % 4] == codes[r, kb]
+        assert flat[r * 4 + 3] == 0
+    assert np.array_equal(quant.mx_scales_from_kstep(flat, 5, 96), codes)
+    wide = np.arange(2 * 8, dtype=np.uint8).reshape(2, 8)             # K = 256: two full steps
+    f2 = quant.mx_scales_to_kstep(wide)
+    assert f2.tolist() == [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
 
 
 def test_mxfp8_colwise_is_rowwise_of_transpose():
     rng = np.random.default_rng(1)
-    splits = [64, 32]
-    y = codecs.f32(rng.standard_normal((96, 64)))
+    splits = [128, 32]
+    y = codecs.f32(rng.standard_normal((160, 64)))
     q = quant.quantize_grouped(y, splits, quant.MXFP8, rowwise=False)
-    qt0 = quant.mxfp8_quantize_rows(y[:64].T)
-    assert np.array_equal(q["col_data"][:64 * 64], qt0[0].reshape(-1))
+    qt0 = quant.mxfp8_quantize_rows(y[:128].T)        # a full group: no padding tokens
+    assert np.array_equal(q["col_data"][:64 * 128], qt0[0].reshape(-1))
+    assert np.array_equal(q["col_scales"][:64 * 128 // 32], quant.mx_scales_to_kstep(qt0[1]))
 
 
 def _brute_e4m3(v):
@@ -146,7 +163,7 @@ def test_nvfp4_colwise_reuses_group_amax_and_pads():
     nd, ns = quant.qtensor_nbytes(quant.NVFP4, True, splits, 32)
     assert q["col_data"].size == nd and q["col_scales"].size == ns
     mats = dequant_col_grouped(quant.NVFP4, q["col_data"], q["col_scales"], splits, 32, q["group_scale"])
-    assert mats[0].shape == (32, 32) and np.all(mats[0][:, 20:] == 0)
-    assert mats[1].shape == (32, 64) and np.all(mats[1][:, 40:] == 0)
+    assert mats[0].shape == (32, 128) and np.all(mats[0][:, 20:] == 0)
+    assert mats[1].shape == (32, 128) and np.all(mats[1][:, 40:] == 0)
     rel = np.sqrt(np.mean((mats[1][:, :40] - y[20:].T) ** 2) / np.mean(y[20:] ** 2))
     assert rel < 0.2
