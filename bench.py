@@ -14,6 +14,7 @@ sample of the same workload.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -100,6 +101,28 @@ class Timer:
         return out
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_scaled_amd", "csrc", "gemm_mx.hip")
+
+
+def gemm_source_sha():
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(fmt):
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by
+    the copy-kernel calibration; None when the counters were taken on a different GEMM source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != gemm_source_sha() or t.get("recipe") != fmt:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(kind, fmt, seed=0):
     """The oracle's expert-MLP step on a bounded sample of the workload: one of the 16 experts with
     512 tokens, full hidden 4096 / ffn 4096 weights.  Returns the oracle's GEMM TFLOP/s."""
@@ -139,6 +162,8 @@ def main():
     ap.add_argument("--fmt", default="mxfp8", choices=["mxfp8", "nvfp4"])
     ap.add_argument("--act", default="srelu", choices=["srelu", "tanh_srelu"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel "
@@ -163,6 +188,13 @@ def main():
     x1, w1, w2, b1, b2, dy2 = (dev(d[k]) for k in ("x1", "w1", "w2", "b1", "b2", "dy2"))
     p = torch.from_numpy(d["p"]).cuda()
     del d
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # recompute memory drop, measured between forward and backward
     held = {}
@@ -233,7 +265,7 @@ def main():
                                "%s, %s, bias, recompute on, delayed wgrad" % (args.act, args.fmt.upper()),
                    "experts": e, "tokens": m, "hidden": h, "ffn": f, "recipe": args.fmt, "act": args.act},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / peak, "traffic": None},
+                     "frac": gemm_tflops / peak, "traffic": measured_traffic(args.fmt)},
         "kernels": kernels,
         "recompute_memory_drop_bytes": {"measured": held[False] - held[True], "closed_form": drop_closed},
     }
