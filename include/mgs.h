@@ -10,7 +10,8 @@
  * General conventions (all entry points):
  *   - Every pointer argument named *_bf16, probs, dprobs, group_amax, data, scales, group_scale, c and
  *     bias is a DEVICE pointer; mgs_groups.split_sizes and the mgs_* structs themselves are HOST memory.
- *   - The caller owns every buffer.  The library allocates no memory and keeps no state between calls.
+ *   - The caller owns every buffer, workspaces included.  The library allocates no memory and keeps no
+ *     state between calls.
  *   - Every call validates its arguments on the host, then enqueues its kernels on `stream` (a
  *     hipStream_t; NULL = the null stream) and returns without synchronizing.
  *   - A NULL output pointer (or an mgs_qbuf with data == NULL) means "not requested": it is not computed.
@@ -18,7 +19,10 @@
  *     fails.  mgs_last_error() returns a thread-local message describing the last failure.
  *   - Row groups: `groups->split_sizes[g]` rows belong to group (expert) g, stored contiguously in
  *     group order ([P2] sequence diagram: split_sizes).  M = sum of split sizes.
- *   - Quantized widths (the quantized, contiguous dimension) must be multiples of 32.
+ *   - Quantized widths (the quantized, contiguous dimension) must be multiples of 32, at most 2^24.
+ *   - Size limits of the quantizing entry points (MGS_ERR_SHAPE beyond them): one group's columnwise
+ *     matrix, roundup(m_g, 128) x W elements, stays below 2^31, and so does the byte size of the
+ *     rowwise MXFP8 scale array, 4 * M * ceil(W / 128).
  *   - Arithmetic follows IEEE FP32 with round-to-nearest-even; results are deterministic (no float
  *     atomics, fixed reduction orders).
  *
@@ -51,13 +55,14 @@
 extern "C" {
 #endif
 
-#define MGS_ABI_VERSION 1
+#define MGS_ABI_VERSION 2
 #define MGS_MAX_GROUPS 256
 
 enum mgs_status {
   MGS_OK = 0,
   MGS_ERR_INVALID_ARG = -1, /* NULL required pointer, unknown enum value, bad group count      */
-  MGS_ERR_SHAPE = -2,       /* width not a multiple of 32, negative split, split sum mismatch   */
+  MGS_ERR_SHAPE = -2,       /* width not a multiple of 32, negative split, split sum mismatch,
+                               size limits (see the conventions above)                          */
   MGS_ERR_UNSUPPORTED = -3, /* a valid but unsupported combination (e.g. NVFP4 recompute
                                without the forward's group amax)                                 */
   MGS_ERR_HIP = -4          /* a HIP launch error                                                */
@@ -151,12 +156,24 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
  *   dprobs        [M] FP32 dL/dp = sum_j dy * a(x); nullable
  *   act_col       columnwise qtensor of y = a(x) * p regenerated from x (recompute); nullable.  Its bytes
  *                 equal those the forward's out_col would have held.
- *   saved_group_amax [E] FP32 group amax written by the forward; required for an NVFP4 act_col. */
+ *   saved_group_amax [E] FP32 group amax written by the forward; required for an NVFP4 act_col.
+ *   workspace     DEVICE scratch of at least mgs_act_bwd_workspace_bytes() bytes, required when dprobs
+ *                 is requested (else ignored; may be NULL); owned by the caller, contents undefined
+ *                 before and after the call.  The kernel writes one partial sum per row and
+ *                 128-column tile there and a second kernel adds them in tile order, so dprobs is
+ *                 deterministic.  Calls that share a workspace must not overlap.
+ *   workspace_bytes its size; MGS_ERR_INVALID_ARG when dprobs is requested and it is too small. */
 int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
                                int64_t width_in, const void* x_bf16, const void* dy_bf16,
                                const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
                                const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
-                               const mgs_qbuf* act_col, const float* saved_group_amax, void* stream);
+                               const mgs_qbuf* act_col, const float* saved_group_amax,
+                               void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes mgs_grouped_scaled_act_bwd needs for dprobs: 4 * M * ceil(W_a / 128).
+ * Negative MGS_ERR_* on invalid arguments. */
+int64_t mgs_act_bwd_workspace_bytes(const mgs_act_params* act, const mgs_groups* groups,
+                                    int64_t width_in);
 
 /* Plain grouped quantization of a BF16 tensor (weights, upstream gradients, FC1 input): the forward
  * above with act = IDENTITY and p = 1.  [P2] Greptile summary, second bullet (GroupedLinear consumes a

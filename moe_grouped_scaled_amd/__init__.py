@@ -10,6 +10,7 @@ from . import _native  # noqa: F401
 from ._native import (  # noqa: F401
     MgsError,
     QTensor,
+    act_bwd_workspace_bytes,
     act_params,
     grouped_col_sum,
     grouped_gemm_mx,

@@ -59,7 +59,8 @@ def _load():
         "mgs_qtensor_nbytes": (i64, [i32, i32, pgr, i64, i32]),
         "mgs_grouped_scaled_act_fwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, pq, pq, vp, vp]),
         "mgs_grouped_scaled_act_bwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, vp, vp, pq, pq, vp,
-                                                      vp, pq, vp, vp]),
+                                                      vp, pq, vp, vp, i64, vp]),
+        "mgs_act_bwd_workspace_bytes": (i64, [pact, pgr, i64]),
         "mgs_grouped_mx_quantize": (ctypes.c_int, [i32, pgr, i64, vp, pq, pq, vp, vp]),
         "mgs_grouped_gemm_mx": (ctypes.c_int, [i32, i32, pgr, i64, i64, i64, pq, pq, vp, i32, vp, i32,
                                                vp]),
@@ -74,8 +75,8 @@ def _load():
 
 LIB = _load()
 EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
-            "mgs_grouped_scaled_act_bwd", "mgs_grouped_mx_quantize", "mgs_grouped_gemm_mx",
-            "mgs_grouped_col_sum")
+            "mgs_grouped_scaled_act_bwd", "mgs_act_bwd_workspace_bytes", "mgs_grouped_mx_quantize",
+            "mgs_grouped_gemm_mx", "mgs_grouped_col_sum")
 
 
 def _check(rc):
@@ -169,17 +170,32 @@ def grouped_scaled_act_fwd(act, fmt, split_sizes, width_in, x, probs, out_row=No
                                           _ptr(probs), rref, cref, _ptr(group_amax), _stream(stream)))
 
 
+def act_bwd_workspace_bytes(act, split_sizes, width_in):
+    g = _GroupsArg(split_sizes)
+    n = LIB.mgs_act_bwd_workspace_bytes(ctypes.byref(act), g.ref, int(width_in))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
 def grouped_scaled_act_bwd(act, fmt, split_sizes, width_in, x, dy, probs, dx=None, dx_row=None,
                            dx_col=None, dx_group_amax=None, dprobs=None, act_col=None,
-                           saved_group_amax=None, stream=None):
+                           saved_group_amax=None, workspace=None, stream=None):
+    """`workspace` (a CUDA tensor) is needed with dprobs; when it is None one of the right size is
+    allocated here for the call."""
     g = _GroupsArg(split_sizes)
     _r, rref = _qref(dx_row)
     _c, cref = _qref(dx_col)
     _a, aref = _qref(act_col)
+    if dprobs is not None and workspace is None:
+        workspace = torch.empty(max(act_bwd_workspace_bytes(act, split_sizes, width_in), 1),
+                                dtype=torch.uint8, device="cuda")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(LIB.mgs_grouped_scaled_act_bwd(ctypes.byref(act), FMT[fmt], g.ref, int(width_in), _ptr(x),
                                           _ptr(dy), _ptr(probs), _ptr(dx), rref, cref,
                                           _ptr(dx_group_amax), _ptr(dprobs), aref,
-                                          _ptr(saved_group_amax), _stream(stream)))
+                                          _ptr(saved_group_amax), _ptr(workspace), int(ws_bytes),
+                                          _stream(stream)))
 
 
 def grouped_mx_quantize(fmt, split_sizes, width, x, out_row=None, out_col=None, group_amax=None,

@@ -57,120 +57,273 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * q + min(x, r) + i;
 }
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// ------------------------------------------------------------------------------- buffer views
+//
+// Every tensor is addressed through a raw buffer descriptor whose base is the current panel (a
+// wave-uniform value, so it lives in scalar registers), a 32-bit per-lane offset and a scalar offset
+// for the row (or column) step.  This keeps one vector register per tensor instead of a 64-bit
+// address per row.  The descriptor's record count ends the view at the end of its allocation.
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef unsigned int v2u __attribute__((__vector_size__(8)));
+typedef unsigned int v4u __attribute__((__vector_size__(16)));
+
+// dword 3 of a gfx9-family buffer descriptor: 32-bit data format, no swizzle
+constexpr int RSRC_WORD3 = 0x00020000;
+// Views address at most 2^31 - 1 bytes, so a lane offset of 2^31 is always past the record count:
+// the buffer unit returns zero for such a load (no memory access), which masks a lane without a
+// branch.  Callers keep every real offset below 2^31 (the C-ABI layer checks the extents).
+constexpr uint32_t MASKED = 0x80000000u;
+
+// view of bytes [off, total) of an allocation
+__device__ __forceinline__ rsrc_t view(const void* base, int64_t off, int64_t total) {
+  int64_t n = total - off;
+  n = n < 0 ? 0 : (n > 0x7FFFFFFFll ? 0x7FFFFFFFll : n);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + off,
+                                           (short)0, (int)n, RSRC_WORD3);
+}
+
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t vo, uint32_t so) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void bst16(uint4 d, rsrc_t r, uint32_t vo, uint32_t so) {
+  const v4u v = {d.x, d.y, d.z, d.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)vo, (int)so, 0);
+}
+__device__ __forceinline__ void bst8(uint2 d, rsrc_t r, uint32_t vo, uint32_t so) {
+  const v2u v = {d.x, d.y};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)vo, (int)so, 0);
+}
+__device__ __forceinline__ void bst4(uint32_t d, rsrc_t r, uint32_t vo, uint32_t so) {
+  __builtin_amdgcn_raw_buffer_store_b32(d, r, (int)vo, (int)so, 0);
+}
+__device__ __forceinline__ void bst1(uint32_t d, rsrc_t r, uint32_t vo, uint32_t so) {
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)d, r, (int)vo, (int)so, 0);
+}
+
+// A BF16 row-major tensor seen from the panel's first row: element (lr, c) at byte
+// ((lr * ld + c) * 2); `vo` is the lane's offset of (lr0, col), `ld2` the row pitch in bytes.
+struct Bf16View {
+  rsrc_t r;
+  uint32_t vo, ld2;
+};
+
+__device__ __forceinline__ Bf16View bf16_view(const uint16_t* p, int64_t ld, int64_t row0,
+                                              int64_t rows, int lr0, int64_t col) {
+  Bf16View v;
+  v.r = view(p, row0 * ld * 2, rows * ld * 2);
+  v.ld2 = (uint32_t)(ld * 2);
+  v.vo = ((uint32_t)lr0 * (uint32_t)ld + (uint32_t)col) * 2u;
+  return v;
+}
+
+// Rowwise destination of one panel: codes of row lr0 + i at data + dvo + i * dpitch, the lane's
+// block scale at scales + svo + i * spitch.
+struct RowDst {
+  rsrc_t data, scales;
+  uint32_t dvo, dpitch, svo, spitch;
+  uint32_t pad;  // MXFP8: zero bytes to write after the row's last scale (rest of the K step)
+  bool sc_lane;  // this lane writes its block's scale
+};
+
+// MXFP8 row scales are grouped per 128-wide K step: the byte of row r, 32-block kb of an R-row
+// matrix sits at ((kb / 4) * R + r) * 4 + kb % 4 (R = srows).
+template <int FMT>
+__device__ __forceinline__ RowDst row_dst(const QOut& q, int64_t w, int64_t srows, int64_t row0,
+                                          int lr0, int64_t col, int lane) {
+  RowDst d;
+  if constexpr (FMT == MGS_FMT_MXFP8) {
+    const int64_t nkb = w >> 5, nks = (nkb + 3) >> 2, kb = col >> 5;
+    d.data = view(q.row_data, row0 * w, srows * w);
+    d.scales = view(q.row_scales, row0 * 4, srows * 4 * nks);
+    d.dvo = (uint32_t)lr0 * (uint32_t)w + (uint32_t)col;
+    d.dpitch = (uint32_t)w;
+    d.svo = (uint32_t)(kb >> 2) * (uint32_t)srows * 4u + (uint32_t)lr0 * 4u + (uint32_t)(kb & 3);
+    d.spitch = 4;
+    d.pad = kb == nkb - 1 ? (uint32_t)(nks * 4 - nkb) : 0u;
+    d.sc_lane = ((lane >> 2) & 3) == 0;
+  } else {
+    d.data = view(q.row_data, row0 * w / 2, srows * w / 2);
+    d.scales = view(q.row_scales, row0 * (w >> 4), srows * (w >> 4));
+    d.dvo = ((uint32_t)lr0 * (uint32_t)w + (uint32_t)col) >> 1;
+    d.dpitch = (uint32_t)(w >> 1);
+    d.svo = (uint32_t)lr0 * (uint32_t)(w >> 4) + (uint32_t)(col >> 4);
+    d.spitch = (uint32_t)(w >> 4);
+    d.pad = 0;
+    d.sc_lane = ((lane >> 2) & 1) == 0;
+  }
+  return d;
+}
+
+// Columnwise destination of one panel (tokens 32 * lpanel .. +31 of the group): the codes of
+// column col + j at data + dvo + j * dpitch, its block scale at scales + svo + j * spitch.
+struct ColDst {
+  rsrc_t data, scales;
+  uint32_t dvo, dpitch, svo, spitch;
+  bool sc_lane;
+};
+
+// The group's columnwise matrix is [w x mp] (mp = padded token count, a multiple of 128) at
+// element offset w * coff; MXFP8 scales of it use the K-step grouping over tokens.
+template <int FMT>
+__device__ __forceinline__ ColDst col_dst(const QOut& q, int64_t w, int64_t total_padded,
+                                          const PanelInfo& pi, int lr0, int64_t col) {
+  ColDst d;
+  const int64_t lp = pi.lpanel, e0 = w * pi.coff;
+  const uint32_t mp = (uint32_t)pi.mp;
+  if constexpr (FMT == MGS_FMT_MXFP8) {
+    d.data = view(q.col_data, e0 + 32 * lp, w * total_padded);
+    d.scales = view(q.col_scales, (e0 >> 5) + (((lp >> 2) * w) << 2) + (lp & 3), (w * total_padded) >> 5);
+    d.dvo = (uint32_t)col * mp + (uint32_t)lr0;
+    d.dpitch = mp;
+    d.svo = (uint32_t)col * 4u;
+    d.spitch = 4;
+    d.sc_lane = lr0 == 0;
+  } else {
+    d.data = view(q.col_data, (e0 + 32 * lp) >> 1, (w * total_padded) >> 1);
+    d.scales = view(q.col_scales, (e0 >> 4) + 2 * lp, (w * total_padded) >> 4);
+    d.dvo = ((uint32_t)col * mp + (uint32_t)lr0) >> 1;
+    d.dpitch = mp >> 1;
+    d.svo = (uint32_t)col * (mp >> 4) + (uint32_t)(lr0 >> 4);
+    d.spitch = mp >> 4;
+    d.sc_lane = (lr0 & 8) == 0;
+  }
+  return d;
+}
 
 // ---------------------------------------------------------------------------------- tile emitters
 
-// Rowwise quantization of an 8 x 8 tile: rows r0 + i (i < 8, real when lr0 + i < nrows), columns
-// col..col+7 of a quantized tensor of width w.
-// MXFP8 scales are grouped per 128-wide K step (the byte of row r, 32-block kb of an R-row matrix
-// sits at ((kb / 4) * R + r) * 4 + kb % 4); `srows` is R.  Unused bytes of a partial last step are
-// written as zero by the lane that owns the row's last block.
+// Rowwise quantization of row i (8 values) of the lane's tile; rv: the row is real.
 template <int FMT>
-__device__ __forceinline__ void emit_row(const float (&y)[8][8], uint8_t* __restrict__ data,
-                                         uint8_t* __restrict__ scales, int64_t w, int64_t srows,
-                                         int64_t r0, int lr0, int nrows, int64_t col, bool valid,
-                                         int lane, float s_enc) {
+__device__ __forceinline__ void quant_row(const float (&v)[8], const RowDst& d, int i, bool rv,
+                                          float s_enc) {
+  float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float m = 0.0f;
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  if constexpr (FMT == MGS_FMT_MXFP8) {
+    m = row4_max(m);
+    const uint32_t c = mx_scale_code(m);
+    const float inv = mx_inv_scale(c);
+    uint2 q;
+    q.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    q.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    const bool sv = rv && d.sc_lane;
+    bst8(q, d.data, rv ? d.dvo : MASKED, i * d.dpitch);
+    bst1(c, d.scales, sv ? d.svo : MASKED, i * d.spitch);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[i][j]));
-    const bool rv = valid && (lr0 + i) < nrows;
-    const int64_t r = r0 + i;
-    if constexpr (FMT == MGS_FMT_MXFP8) {
-      m = row4_max(m);
-      const uint32_t c = mx_scale_code(m);
-      const float inv = mx_inv_scale(c);
-      uint2 q;
-      q.x = e4m3x4(y[i][0] * inv, y[i][1] * inv, y[i][2] * inv, y[i][3] * inv);
-      q.y = e4m3x4(y[i][4] * inv, y[i][5] * inv, y[i][6] * inv, y[i][7] * inv);
-      if (rv) {
-        *reinterpret_cast<uint2*>(data + r * w + col) = q;
-        if (((lane >> 2) & 3) == 0) {
-          const int64_t kb = col >> 5, nkb = w >> 5;
-          scales[(((kb >> 2) * srows + r) << 2) + (kb & 3)] = (uint8_t)c;
-          if (kb == nkb - 1)
-            for (int64_t t = kb + 1; t < ((nkb + 3) & ~(int64_t)3); ++t)
-              scales[(((t >> 2) * srows + r) << 2) + (t & 3)] = 0;
-        }
-      }
-    } else {
-      m = pair4_max(m);
-      const NvBlock b = nv_block(m, s_enc);
-      float v[8];
+    for (uint32_t t = 1; t <= 3; ++t) bst1(0, d.scales, sv && t <= d.pad ? d.svo + t : MASKED, i * d.spitch);
+  } else {
+    m = pair4_max(m);
+    const NvBlock b = nv_block(m, s_enc);
+    float e[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = b.r != 0.0f ? y[i][j] * b.r : 0.0f;
-      const uint32_t q = e2m1x8(v);
-      if (rv) {
-        *reinterpret_cast<uint32_t*>(data + ((r * w + col) >> 1)) = q;
-        if (((lane >> 2) & 1) == 0) scales[r * (w >> 4) + (col >> 4)] = (uint8_t)b.code;
-      }
-    }
+    for (int j = 0; j < 8; ++j) e[j] = b.r != 0.0f ? v[j] * b.r : 0.0f;
+    bst4(e2m1x8(e), d.data, rv ? d.dvo : MASKED, i * d.dpitch);
+    bst1(b.code, d.scales, rv && d.sc_lane ? d.svo : MASKED, i * d.spitch);
   }
 }
 
-// Columnwise quantization of an 8 x 8 tile whose rows are tokens lr0..lr0+7 of panel `pi` (rows
-// beyond the group are zeros in y and are written as zero padding).
+// Columnwise quantization of column j (8 tokens lr0..lr0+7; rows beyond the group are zeros and
+// are written as zero padding).
 template <int FMT>
-__device__ __forceinline__ void emit_col(const float (&y)[8][8], uint8_t* __restrict__ data,
-                                         uint8_t* __restrict__ scales, int64_t w,
-                                         const PanelInfo& pi, int lr0, int64_t col, bool valid,
-                                         float s_enc) {
-  const int64_t tok = (int64_t)PANEL_ROWS * pi.lpanel + lr0;  // token index within the group
+__device__ __forceinline__ void quant_col(const float (&v)[8], const ColDst& d, int j, bool valid,
+                                          float s_enc) {
+  float m = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float m = 0.0f;
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  if constexpr (FMT == MGS_FMT_MXFP8) {
+    m = quad_max(m);
+    const uint32_t c = mx_scale_code(m);
+    const float inv = mx_inv_scale(c);
+    uint2 q;
+    q.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    q.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    bst8(q, d.data, valid ? d.dvo : MASKED, j * d.dpitch);
+    bst1(c, d.scales, valid && d.sc_lane ? d.svo : MASKED, j * d.spitch);
+  } else {
+    m = pair1_max(m);
+    const NvBlock b = nv_block(m, s_enc);
+    float e[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i][j]));
-    const int64_t cj = col + j;
-    if constexpr (FMT == MGS_FMT_MXFP8) {
-      m = quad_max(m);
-      const uint32_t c = mx_scale_code(m);
-      const float inv = mx_inv_scale(c);
-      uint2 q;
-      q.x = e4m3x4(y[0][j] * inv, y[1][j] * inv, y[2][j] * inv, y[3][j] * inv);
-      q.y = e4m3x4(y[4][j] * inv, y[5][j] * inv, y[6][j] * inv, y[7][j] * inv);
-      if (valid) {
-        *reinterpret_cast<uint2*>(data + w * pi.coff + cj * pi.mp + tok) = q;
-        // K-step grouped scales of the group's [w x mp] matrix (mp is a multiple of 128)
-        const int64_t tb = tok >> 5;
-        if (lr0 == 0) scales[((w * pi.coff) >> 5) + (((tb >> 2) * w + cj) << 2) + (tb & 3)] = (uint8_t)c;
-      }
-    } else {
-      m = pair1_max(m);
-      const NvBlock b = nv_block(m, s_enc);
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = b.r != 0.0f ? y[i][j] * b.r : 0.0f;
-      const uint32_t q = e2m1x8(v);
-      if (valid) {
-        *reinterpret_cast<uint32_t*>(data + ((w * pi.coff + cj * pi.mp + tok) >> 1)) = q;
-        if ((lr0 & 8) == 0) scales[((w * pi.coff) >> 4) + cj * (pi.mp >> 4) + (tok >> 4)] = (uint8_t)b.code;
-      }
-    }
+    for (int i = 0; i < 8; ++i) e[i] = b.r != 0.0f ? v[i] * b.r : 0.0f;
+    bst4(e2m1x8(e), d.data, valid ? d.dvo : MASKED, j * d.dpitch);
+    bst1(b.code, d.scales, valid && d.sc_lane ? d.svo : MASKED, j * d.spitch);
   }
 }
+
+// Rowwise quantization of a whole 8 x 8 tile (rows lr0 + i of the panel, real when < nrows).
+template <int FMT>
+__device__ __forceinline__ void emit_row(const float (&y)[8][8], const RowDst& d, int lr0, int nrows,
+                                         bool valid, float s_enc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) quant_row<FMT>(y[i], d, i, valid && (lr0 + i) < nrows, s_enc);
+}
+
+// Columnwise quantization of a whole 8 x 8 tile.
+template <int FMT>
+__device__ __forceinline__ void emit_col(const float (&y)[8][8], const ColDst& d, bool valid,
+                                         float s_enc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = y[i][j];
+    quant_col<FMT>(v, d, j, valid, s_enc);
+  }
+}
+
+// element j (0..7) of a packed BF16 octet
+__device__ __forceinline__ float bf16_at(const uint4& w, int j) {
+  const uint32_t x = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
+  return (j & 1) ? bf16hi(x) : bf16lo(x);
+}
+
+// An opaque copy of a packed tile row: later phases recompute from it instead of keeping the
+// earlier phase's FP32 intermediates alive (common-subexpression reuse would hold 64 extra floats).
+__device__ __forceinline__ void launder(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+// Pins a running sum at this point of the program (the compiler would otherwise sink loop-carried
+// additions to the end of the iteration and keep all their operands alive until then).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 
 template <int KIND>
 constexpr bool is_gated() { return KIND == MGS_ACT_SWIGLU || KIND == MGS_ACT_CLAMPED_SWIGLU; }
 
-// y = a(x) * p for the lane's 8 x 8 tile (zeros for rows outside the panel or invalid columns)
-template <int KIND>
-__device__ __forceinline__ void compute_y(const ActArgs& aa, const uint16_t* __restrict__ x,
-                                          const float* __restrict__ probs, int64_t width_in,
-                                          int64_t wa, const PanelInfo& pi, int lr0, int64_t col,
-                                          bool valid, float (&y)[8][8]) {
-  uint4 xg[8], xu[8];
-  float p[8];
+// probs of the lane's 8 rows (0 for rows outside the panel, 1 when probs is null)
+__device__ __forceinline__ void load_probs(const float* __restrict__ probs, const PanelInfo& pi,
+                                           int64_t total_rows, int lr0, float (&p)[8]) {
+  if (probs) {
+    const rsrc_t r = view(probs, (int64_t)pi.row0 * 4, total_rows * 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t vo = (lr0 + i) < pi.nrows ? (uint32_t)(lr0 + i) * 4u : MASKED;
+      p[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, 0, 0));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = (lr0 + i) < pi.nrows ? 1.0f : 0.0f;
+  }
+}
+
+// The lane's 8 x 8 BF16 input tile(s): gate (or only) half at column col, up half at wa + col.
+template <bool GATED>
+__device__ __forceinline__ void load_x(const Bf16View& xv, uint32_t up_off, int lr0, int nrows,
+                                       bool valid, uint4 (&xg)[8], uint4 (&xu)[GATED ? 8 : 1]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const bool rv = valid && (lr0 + i) < pi.nrows;
-    const int64_t r = pi.row0 + lr0 + i;
-    xg[i] = rv ? ld16(x + r * width_in + col) : make_uint4(0, 0, 0, 0);
-    if constexpr (is_gated<KIND>()) xu[i] = rv ? ld16(x + r * width_in + wa + col) : make_uint4(0, 0, 0, 0);
-    p[i] = rv ? (probs ? probs[r] : 1.0f) : 0.0f;
+    const bool rv = valid && (lr0 + i) < nrows;
+    xg[i] = bld16(xv.r, rv ? xv.vo : MASKED, i * xv.ld2);
+    if constexpr (GATED) xu[i] = bld16(xv.r, rv ? xv.vo + up_off : MASKED, i * xv.ld2);
   }
+}
+
+// y = a(x) * p for the lane's 8 x 8 tile (zeros for rows outside the panel or invalid columns)
+template <int KIND>
+__device__ __forceinline__ void compute_y(const ActArgs& aa, const uint4 (&xg)[8],
+                                          const uint4 (&xu)[is_gated<KIND>() ? 8 : 1],
+                                          const float (&p)[8], float (&y)[8][8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float g[8];
@@ -193,33 +346,63 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0.0f;
 }
 
-// max|y| per group (NVFP4 first pass): one unsigned atomic max per wave on the FP32 bit pattern of
-// a non-negative value, which orders like the value itself; the result is order-independent.
+// Lane placement shared by the tile kernels: workgroup tile t -> (panel, column tile), the lane's
+// first row lr0 and first column col.
+struct TilePos {
+  PanelInfo pi;
+  int ct, lane, wave, lr0;
+};
+
+__device__ __forceinline__ TilePos tile_pos(const GroupTable& gt, int n_ct) {
+  TilePos tp;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int panel = t / n_ct;
+  tp.ct = t - panel * n_ct;
+  tp.pi = find_panel(gt, panel);
+  tp.lane = threadIdx.x & 63;
+  tp.wave = threadIdx.x >> 6;
+  tp.lr0 = 8 * (tp.lane & 3);
+  return tp;
+}
+
+__device__ __forceinline__ int64_t tile_col(const TilePos& tp, int ct) {
+  return (int64_t)ct * TILE_COLS + tp.wave * 128 + 8 * (tp.lane >> 2);
+}
+
+// max over the whole wave, then one unsigned atomic max on the FP32 bit pattern of the non-negative
+// result, which orders like the value itself: the group maximum is order-independent.
+__device__ __forceinline__ void wave_amax_to(float m, int lane, float* dst) {
+  m = quad_max(m);
+  m = row4_max(m);
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(m));
+}
+
+// max|y| per group (NVFP4 first pass)
 template <int KIND>
 __global__ __launch_bounds__(256) void act_amax_kernel(ActArgs aa, GroupTable gt,
                                                        const uint16_t* __restrict__ x,
                                                        const float* __restrict__ probs,
                                                        int64_t width_in, int64_t wa, int n_ct,
                                                        float* __restrict__ amax) {
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int panel = t / n_ct, ct = t - panel * n_ct;
-  const PanelInfo pi = find_panel(gt, panel);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr0 = 8 * (lane & 3);
-  const int64_t col = (int64_t)ct * TILE_COLS + wave * 128 + 8 * (lane >> 2);
+  constexpr bool GATED = is_gated<KIND>();
+  const TilePos tp = tile_pos(gt, n_ct);
+  const int64_t col = tile_col(tp, tp.ct);
   const bool valid = col < wa;
+  const Bf16View xv = bf16_view(x, width_in, tp.pi.row0, gt.total_rows, tp.lr0, col);
+  uint4 xg[8], xu[GATED ? 8 : 1];
+  load_x<GATED>(xv, (uint32_t)wa * 2u, tp.lr0, tp.pi.nrows, valid, xg, xu);
+  float p[8];
+  load_probs(probs, tp.pi, gt.total_rows, tp.lr0, p);
   float y[8][8];
-  compute_y<KIND>(aa, x, probs, width_in, wa, pi, lr0, col, valid, y);
+  compute_y<KIND>(aa, xg, xu, p, y);
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[i][j]));
-  m = quad_max(m);
-  m = row4_max(m);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(amax + pi.g), __float_as_uint(m));
+  wave_amax_to(m, tp.lane, amax + tp.pi.g);
 }
 
 // S_dec = 1 / S_enc per group, written once per launch (covers empty groups too)
@@ -232,37 +415,198 @@ __device__ __forceinline__ void write_group_scales(const GroupTable& gt, const Q
   }
 }
 
+// --------------------------------------------------------------------- 128-token block tiles
+//
+// The quantizing kernels give a workgroup one 128-token block of one group (groups are padded to a
+// multiple of 128 tokens in the columnwise layout, so a block never straddles two groups) and 128
+// columns: wave w owns panel 4 b + w (32 rows) and each lane its 8 x 8 tile of it.  Rowwise codes
+// go straight to memory (16 lanes write a row's 128 contiguous bytes).  Columnwise codes are staged
+// in LDS and written afterwards by the whole workgroup as complete 128-token column segments: one
+// 128-byte line per column for MXFP8 (64 bytes for NVFP4) instead of four 32-byte pieces written by
+// four workgroups.  The MXFP8 column scales of the block are then the four bytes of one K step, so
+// each column's scales leave as one aligned dword.
+
+constexpr int BLOCK_COLS = 128;
+
+template <int FMT>
+struct Stage {
+  // bytes per staged column: the block's codes plus 8 bytes of padding, which spreads the lanes'
+  // 8-byte writes of eight columns apart over four bank groups instead of one
+  static constexpr int PITCH = FMT == MGS_FMT_MXFP8 ? 136 : 72;
+  static constexpr int SCALES = FMT == MGS_FMT_MXFP8 ? 4 : 8;  // scale bytes per column and block
+  static constexpr int BYTES = BLOCK_COLS * (PITCH + SCALES);
+};
+
+struct BlockPos {
+  PanelInfo pi;   // the wave's panel
+  int blk;        // 128-token block index within the group
+  int ct;         // 128-column tile
+  int lane, wave, lr0, cc;
+  int64_t col0;   // first column of the workgroup
+  int64_t col;    // the lane's first column
+};
+
+__device__ __forceinline__ BlockPos block_pos(const GroupTable& gt, int n_ct) {
+  BlockPos bp;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = t / n_ct;
+  bp.ct = t - b * n_ct;
+  bp.lane = threadIdx.x & 63;
+  bp.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  bp.pi = find_panel(gt, 4 * b + bp.wave);
+  bp.blk = bp.pi.lpanel >> 2;
+  bp.lr0 = 8 * (bp.lane & 3);
+  bp.cc = bp.lane >> 2;
+  bp.col0 = (int64_t)bp.ct * BLOCK_COLS;
+  bp.col = bp.col0 + 8 * bp.cc;
+  return bp;
+}
+
+// Quantize column j (8 tokens of the lane) into the stage: codes at column c = 8 cc + j, tokens
+// 32 w + lr0 .. +7; the block scale at the column's scale slot.
+template <int FMT>
+__device__ __forceinline__ void stage_col(const float (&v)[8], uint8_t* st, const BlockPos& bp, int j,
+                                          float s_enc) {
+  constexpr int P = Stage<FMT>::PITCH;
+  const int c = 8 * bp.cc + j;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  if constexpr (FMT == MGS_FMT_MXFP8) {
+    m = quad_max(m);
+    const uint32_t code = mx_scale_code(m);
+    const float inv = mx_inv_scale(code);
+    uint2 q;
+    q.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    q.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    *reinterpret_cast<uint2*>(st + c * P + 32 * bp.wave + bp.lr0) = q;
+    if (bp.lr0 == 0) st[BLOCK_COLS * P + 4 * c + bp.wave] = (uint8_t)code;
+  } else {
+    m = pair1_max(m);
+    const NvBlock b = nv_block(m, s_enc);
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = b.r != 0.0f ? v[i] * b.r : 0.0f;
+    *reinterpret_cast<uint32_t*>(st + c * P + 16 * bp.wave + (bp.lr0 >> 1)) = e2m1x8(e);
+    if ((bp.lr0 & 8) == 0) st[BLOCK_COLS * P + 8 * c + 2 * bp.wave + (bp.lr0 >> 4)] = (uint8_t)b.code;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void stage_tile(const float (&y)[8][8], uint8_t* st, const BlockPos& bp,
+                                           float s_enc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = y[i][j];
+    stage_col<FMT>(v, st, bp, j, s_enc);
+  }
+}
+
+// Write a staged block (after a barrier) to the group's columnwise tensor of width w: the data of
+// column cj at w * coff + cj * mp + 128 blk (elements), MXFP8 scales as the K-step dword of
+// (blk, cj), NVFP4 scales as 8 bytes at cj * mp / 16 + 8 blk.
+template <int FMT>
+__device__ __forceinline__ void flush_col(const uint8_t* st, const QOut& q, int64_t w,
+                                          int64_t total_padded, const BlockPos& bp) {
+  constexpr int P = Stage<FMT>::PITCH;
+  const int64_t e0 = w * bp.pi.coff;
+  const uint32_t mp = (uint32_t)bp.pi.mp;
+  const int t = threadIdx.x;
+  if constexpr (FMT == MGS_FMT_MXFP8) {
+    const rsrc_t dv = view(q.col_data, e0 + 128 * (int64_t)bp.blk, w * total_padded);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = t + 256 * k, c = idx >> 3, ch = idx & 7;
+      const uint2 a = *reinterpret_cast<const uint2*>(st + c * P + 16 * ch);
+      const uint2 b = *reinterpret_cast<const uint2*>(st + c * P + 16 * ch + 8);
+      const bool ok = bp.col0 + c < w;
+      bst16(make_uint4(a.x, a.y, b.x, b.y), dv, ok ? (uint32_t)(bp.col0 + c) * mp + 16u * ch : MASKED, 0);
+    }
+    const rsrc_t sv = view(q.col_scales, (e0 >> 5) + 4 * ((int64_t)bp.blk * w + bp.col0), (w * total_padded) >> 5);
+    if (t < BLOCK_COLS) {
+      const uint32_t d = *reinterpret_cast<const uint32_t*>(st + BLOCK_COLS * P + 4 * t);
+      bst4(d, sv, bp.col0 + t < w ? 4u * t : MASKED, 0);
+    }
+  } else {
+    const rsrc_t dv = view(q.col_data, (e0 + 128 * (int64_t)bp.blk) >> 1, (w * total_padded) >> 1);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = t + 256 * k, c = idx >> 2, ch = idx & 3;
+      const uint2 a = *reinterpret_cast<const uint2*>(st + c * P + 16 * ch);
+      const uint2 b = *reinterpret_cast<const uint2*>(st + c * P + 16 * ch + 8);
+      const bool ok = bp.col0 + c < w;
+      bst16(make_uint4(a.x, a.y, b.x, b.y), dv, ok ? ((uint32_t)(bp.col0 + c) * mp >> 1) + 16u * ch : MASKED, 0);
+    }
+    const rsrc_t sv = view(q.col_scales, (e0 >> 4) + 8 * (int64_t)bp.blk, (w * total_padded) >> 4);
+    if (t < BLOCK_COLS) {
+      const uint2 d = *reinterpret_cast<const uint2*>(st + BLOCK_COLS * P + 8 * t);
+      bst8(d, sv, bp.col0 + t < w ? (uint32_t)(bp.col0 + t) * (mp >> 4) : MASKED, 0);
+    }
+  }
+}
+
 template <int KIND, int FMT>
 __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
                                                       const uint16_t* __restrict__ x,
                                                       const float* __restrict__ probs,
                                                       int64_t width_in, QOut out, int n_ct) {
+  constexpr bool GATED = is_gated<KIND>();
+  __shared__ __attribute__((aligned(16))) uint8_t stage[Stage<FMT>::BYTES];
   const int64_t wa = out.width;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int panel = t / n_ct, ct = t - panel * n_ct;
-  const PanelInfo pi = find_panel(gt, panel);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr0 = 8 * (lane & 3);
-  const int64_t col = (int64_t)ct * TILE_COLS + wave * 128 + 8 * (lane >> 2);
-  const bool valid = col < wa;
+  const BlockPos bp = block_pos(gt, n_ct);
+  const PanelInfo& pi = bp.pi;
+  const bool valid = bp.col < wa;
   float s_enc = 1.0f;
   if constexpr (FMT == MGS_FMT_NVFP4) {
     write_group_scales(gt, out);
     s_enc = nv_encode_scale(out.amax[pi.g]);
   }
+  const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, bp.lr0, bp.col);
+  uint4 xg[8], xu[GATED ? 8 : 1];
+  load_x<GATED>(xv, (uint32_t)wa * 2u, bp.lr0, pi.nrows, valid, xg, xu);
+  float p[8];
+  load_probs(probs, pi, gt.total_rows, bp.lr0, p);
   float y[8][8];
-  compute_y<KIND>(aa, x, probs, width_in, wa, pi, lr0, col, valid, y);
+  compute_y<KIND>(aa, xg, xu, p, y);
   if (out.row_data)
-    emit_row<FMT>(y, out.row_data, out.row_scales, wa, gt.total_rows, pi.row0 + lr0, lr0, pi.nrows, col, valid, lane, s_enc);
-  if (out.col_data) emit_col<FMT>(y, out.col_data, out.col_scales, wa, pi, lr0, col, valid, s_enc);
+    emit_row<FMT>(y, row_dst<FMT>(out, wa, gt.total_rows, pi.row0, bp.lr0, bp.col, bp.lane), bp.lr0, pi.nrows, valid, s_enc);
+  if (out.col_data) {
+    stage_tile<FMT>(y, stage, bp, s_enc);
+    __syncthreads();
+    flush_col<FMT>(stage, out, wa, (int64_t)PANEL_ROWS * gt.num_panels, bp);
+  }
 }
 
-// Backward tile computation: dx (one or two 8 x 8 tiles), y = a * p (recompute) and dp partials.
+// Backward.  Per 8 x 8 tile: dx (the gate half for gated kinds) is computed once into an FP32 tile
+// by rows (dense BF16 store, rowwise codes and dprobs partial sums as each row completes), then
+// staged by columns; gated kinds repeat this for the up half in the same registers; the recompute
+// variant then regenerates y = a * p from the packed input by columns.  The packed inputs are
+// laundered before a later phase so the compiler evaluates it afresh instead of keeping the first
+// phase's values alive.  dprobs leaves as one partial sum per row and 128-column tile in `dp_part`
+// ([n_ct x M]); a second kernel adds the partials in tile order.
+
+// dx of element (gate half or the only half): returns (da/dg * dy) * p, and a(x) through `a`
 template <int KIND>
-struct BwdTile {
-  float d0[8][8];  // dx for columns col.. (unary) or the gate half (gated)
-  float d1[8][8];  // dx for the up half (gated only)
-};
+__device__ __forceinline__ float dx_gate(const ActArgs& aa, float g, float u, float dd, float p, float& a) {
+  if constexpr (is_gated<KIND>()) {
+    float dg, du;
+    dact_gated<KIND>(g, u, aa, a, dg, du);
+    return (dg * dd) * p;
+  } else {
+    a = act_unary<KIND>(g, aa);
+    return (dact_unary<KIND>(g, aa) * dd) * p;
+  }
+}
+
+// dx of the up half (gated kinds)
+template <int KIND>
+__device__ __forceinline__ float dx_up(const ActArgs& aa, float g, float u, float dd, float p) {
+  float a, dg, du;
+  dact_gated<KIND>(g, u, aa, a, dg, du);
+  return (du * dd) * p;
+}
 
 template <int KIND, int FMT>
 __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
@@ -271,16 +615,20 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
                                                       const float* __restrict__ probs,
                                                       int64_t width_in, int64_t wa,
                                                       uint16_t* __restrict__ dx, QOut dxq,
-                                                      float* __restrict__ dprobs, QOut actq,
-                                                      int n_ct_total, int ct_per_wg) {
+                                                      float* __restrict__ dp_part, QOut actq, int n_ct) {
   constexpr bool GATED = is_gated<KIND>();
-  __shared__ float dp_lds[4][PANEL_ROWS];
-  const int n_grid_ct = (n_ct_total + ct_per_wg - 1) / ct_per_wg;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int panel = t / n_grid_ct, ctg = t - panel * n_grid_ct;
-  const PanelInfo pi = find_panel(gt, panel);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr0 = 8 * (lane & 3);
+  constexpr int SB = Stage<FMT>::BYTES;
+  // stages: dx columnwise (gate half), dx columnwise (up half, gated kinds), recomputed activation
+  __shared__ __attribute__((aligned(16))) uint8_t stage[(GATED ? 3 : 2) * SB];
+  uint8_t* st_dx = stage;
+  uint8_t* st_up = stage + SB;
+  uint8_t* st_act = stage + (GATED ? 2 : 1) * SB;
+  const BlockPos bp = block_pos(gt, n_ct);
+  const PanelInfo& pi = bp.pi;
+  const int lr0 = bp.lr0;
+  const int64_t col = bp.col;
+  const bool valid = col < wa;
+  const int64_t total_padded = (int64_t)PANEL_ROWS * gt.num_panels;
   float s_dx = 1.0f, s_act = 1.0f;
   if constexpr (FMT == MGS_FMT_NVFP4) {
     write_group_scales(gt, dxq);
@@ -288,83 +636,81 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
     if (dxq.amax) s_dx = nv_encode_scale(dxq.amax[pi.g]);
     if (actq.amax) s_act = nv_encode_scale(actq.amax[pi.g]);
   }
-  float p[8];
+  const uint32_t up2 = (uint32_t)wa * 2u;  // byte offset of the up half in a BF16 row
+
+  const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, lr0, col);
+  const Bf16View dyv = bf16_view(dy, wa, pi.row0, gt.total_rows, lr0, col);
+  uint4 xg[8], xu[GATED ? 8 : 1], dyt[8];
+  load_x<GATED>(xv, up2, lr0, pi.nrows, valid, xg, xu);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const bool rv = (lr0 + i) < pi.nrows;
-    p[i] = rv ? (probs ? probs[pi.row0 + lr0 + i] : 1.0f) : 0.0f;
+    const bool rv = valid && (lr0 + i) < pi.nrows;
+    dyt[i] = bld16(dyv.r, rv ? dyv.vo : MASKED, i * dyv.ld2);
   }
-  float dpacc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dpacc[i] = 0.0f;
+  float p[8];
+  load_probs(probs, pi, gt.total_rows, lr0, p);
+  const Bf16View dxv = bf16_view(dx, width_in, pi.row0, gt.total_rows, lr0, col);
+  const RowDst rd = row_dst<FMT>(dxq, width_in, gt.total_rows, pi.row0, lr0, col, bp.lane);
 
-  const int ct_end = min(n_ct_total, (ctg + 1) * ct_per_wg);
-  for (int ct = ctg * ct_per_wg; ct < ct_end; ++ct) {
-    const int64_t col = (int64_t)ct * TILE_COLS + wave * 128 + 8 * (lane >> 2);
-    const bool valid = col < wa;
-    uint4 xg[8], xu[8], dyv[8];
+  float d[8][8], dpacc[8];
+  // rows: dx (gate half) -> dense store, rowwise codes, dprobs partials
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool rv = valid && (lr0 + i) < pi.nrows;
+    dpacc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float a;
+      const float dd = bf16_at(dyt[i], j);
+      d[i][j] = dx_gate<KIND>(aa, bf16_at(xg[i], j), GATED ? bf16_at(xu[GATED ? i : 0], j) : 0.0f, dd, p[i], a);
+      dpacc[i] += dd * a;
+    }
+    pin(dpacc[i]);
+    if (dx) bst16(pack8_bf16(d[i]), dxv.r, rv ? dxv.vo : MASKED, i * dxv.ld2);
+    if (dxq.row_data) quant_row<FMT>(d[i], rd, i, rv, s_dx);
+  }
+  if (dxq.col_data) stage_tile<FMT>(d, st_dx, bp, s_dx);
+  // gated: the up half in the same registers
+  if constexpr (GATED) {
+    const RowDst ru = row_dst<FMT>(dxq, width_in, gt.total_rows, pi.row0, lr0, wa + col, bp.lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      launder(xg[i]);
+      launder(xu[GATED ? i : 0]);
+      launder(dyt[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool rv = valid && (lr0 + i) < pi.nrows;
-      const int64_t r = pi.row0 + lr0 + i;
-      xg[i] = rv ? ld16(x + r * width_in + col) : make_uint4(0, 0, 0, 0);
-      if constexpr (GATED) xu[i] = rv ? ld16(x + r * width_in + wa + col) : make_uint4(0, 0, 0, 0);
-      dyv[i] = rv ? ld16(dy + r * wa + col) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        d[i][j] = dx_up<KIND>(aa, bf16_at(xg[i], j), bf16_at(xu[GATED ? i : 0], j), bf16_at(dyt[i], j), p[i]);
+      if (dx) bst16(pack8_bf16(d[i]), dxv.r, rv ? dxv.vo + up2 : MASKED, i * dxv.ld2);
+      if (dxq.row_data) quant_row<FMT>(d[i], ru, i, rv, s_dx);
     }
-    float d0[8][8], yv[8][8];
-    float d1[GATED ? 8 : 1][8];
+    if (dxq.col_data) stage_tile<FMT>(d, st_up, bp, s_dx);
+  }
+  // recompute: y = a * p -> columnwise codes of the activation
+  if (actq.col_data) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float g[8], dd[8];
-      unpack8(xg[i], g);
-      unpack8(dyv[i], dd);
-      if constexpr (GATED) {
-        float u[8];
-        unpack8(xu[i], u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float a, dg, du;
-          dact_gated<KIND>(g[j], u[j], aa, a, dg, du);
-          d0[i][j] = (dg * dd[j]) * p[i];
-          d1[i][j] = (du * dd[j]) * p[i];
-          dpacc[i] += dd[j] * a;
-          yv[i][j] = a * p[i];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float a = act_unary<KIND>(g[j], aa);
-          d0[i][j] = (dact_unary<KIND>(g[j], aa) * dd[j]) * p[i];
-          dpacc[i] += dd[j] * a;
-          yv[i][j] = a * p[i];
-        }
-      }
+      launder(xg[i]);
+      if constexpr (GATED) launder(xu[GATED ? i : 0]);
     }
-    const int64_t r0 = pi.row0 + lr0;
-    if (dx) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if (valid && (lr0 + i) < pi.nrows) {
-          *reinterpret_cast<uint4*>(dx + (r0 + i) * width_in + col) = pack8_bf16(d0[i]);
-          if constexpr (GATED) *reinterpret_cast<uint4*>(dx + (r0 + i) * width_in + wa + col) = pack8_bf16(d1[i]);
-        }
+        if constexpr (GATED) v[i] = act_gated<KIND>(bf16_at(xg[i], j), bf16_at(xu[GATED ? i : 0], j), aa) * p[i];
+        else v[i] = act_unary<KIND>(bf16_at(xg[i], j), aa) * p[i];
       }
+      stage_col<FMT>(v, st_act, bp, j, s_act);
     }
-    if (dxq.row_data) {
-      emit_row<FMT>(d0, dxq.row_data, dxq.row_scales, width_in, gt.total_rows, r0, lr0, pi.nrows, col, valid, lane, s_dx);
-      if constexpr (GATED)
-        emit_row<FMT>(d1, dxq.row_data, dxq.row_scales, width_in, gt.total_rows, r0, lr0, pi.nrows, wa + col, valid, lane, s_dx);
-    }
-    if (dxq.col_data) {
-      emit_col<FMT>(d0, dxq.col_data, dxq.col_scales, width_in, pi, lr0, col, valid, s_dx);
-      if constexpr (GATED) emit_col<FMT>(d1, dxq.col_data, dxq.col_scales, width_in, pi, lr0, wa + col, valid, s_dx);
-    }
-    if (actq.col_data) emit_col<FMT>(yv, actq.col_data, actq.col_scales, wa, pi, lr0, col, valid, s_act);
   }
 
-  if (dprobs) {
-    // fixed-order reduction: 4 column chunks of a 16-lane row (DPP), the 4 rows of the wave
-    // (cross-row shuffles), then the 4 waves in index order
+  if (dp_part) {
+    // fixed-order sum over the tile's 16 column chunks: DPP within a 16-lane row, then the rows
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float v = dpacc[i];
@@ -374,16 +720,38 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
       v += __shfl_xor(v, 32);
       dpacc[i] = v;
     }
-    if (lane < 4) {
+    if (bp.lane < 4) {
+      const rsrc_t r = view(dp_part, ((int64_t)bp.ct * gt.total_rows + pi.row0) * 4,
+                            (int64_t)n_ct * gt.total_rows * 4);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dp_lds[wave][lr0 + i] = dpacc[i];
-    }
-    __syncthreads();
-    if (threadIdx.x < PANEL_ROWS && (int)threadIdx.x < pi.nrows) {
-      const int i = threadIdx.x;
-      dprobs[pi.row0 + i] = ((dp_lds[0][i] + dp_lds[1][i]) + dp_lds[2][i]) + dp_lds[3][i];
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dpacc[i]), r,
+                                              (int)((lr0 + i) < pi.nrows ? (uint32_t)(lr0 + i) * 4u : MASKED), 0, 0);
     }
   }
+
+  if (dxq.col_data || actq.col_data) {
+    __syncthreads();
+    if (dxq.col_data) {
+      flush_col<FMT>(st_dx, dxq, width_in, total_padded, bp);
+      if constexpr (GATED) {
+        BlockPos bu = bp;
+        bu.col0 += wa;
+        flush_col<FMT>(st_up, dxq, width_in, total_padded, bu);
+      }
+    }
+    if (actq.col_data) flush_col<FMT>(st_act, actq, wa, total_padded, bp);
+  }
+}
+
+// dprobs[r] = sum over column tiles of the partials, in tile order
+__global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* __restrict__ part, int n_ct,
+                                                            int rows, float* __restrict__ dprobs) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  float s = 0.0f;
+  for (int c = 0; c < n_ct; ++c) s += part[(int64_t)c * rows + r];
+  dprobs[r] = s;
 }
 
 // max|dx| per group over the full dx width (NVFP4 first pass of the backward)
@@ -395,75 +763,90 @@ __global__ __launch_bounds__(256) void act_bwd_amax_kernel(ActArgs aa, GroupTabl
                                                            int64_t width_in, int64_t wa, int n_ct,
                                                            float* __restrict__ amax) {
   constexpr bool GATED = is_gated<KIND>();
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int panel = t / n_ct, ct = t - panel * n_ct;
-  const PanelInfo pi = find_panel(gt, panel);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr0 = 8 * (lane & 3);
-  const int64_t col = (int64_t)ct * TILE_COLS + wave * 128 + 8 * (lane >> 2);
+  const TilePos tp = tile_pos(gt, n_ct);
+  const PanelInfo& pi = tp.pi;
+  const int lr0 = tp.lr0;
+  const int64_t col = tile_col(tp, tp.ct);
   const bool valid = col < wa;
-  float m = 0.0f;
+  const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, lr0, col);
+  const Bf16View dyv = bf16_view(dy, wa, pi.row0, gt.total_rows, lr0, col);
+  uint4 xg[8], xu[GATED ? 8 : 1], dyt[8];
+  load_x<GATED>(xv, (uint32_t)wa * 2u, lr0, pi.nrows, valid, xg, xu);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const bool rv = valid && (lr0 + i) < pi.nrows;
-    const int64_t r = pi.row0 + lr0 + i;
-    const uint4 xg = rv ? ld16(x + r * width_in + col) : make_uint4(0, 0, 0, 0);
-    const uint4 dyv = rv ? ld16(dy + r * wa + col) : make_uint4(0, 0, 0, 0);
-    const float pr = rv ? (probs ? probs[r] : 1.0f) : 0.0f;
+    dyt[i] = bld16(dyv.r, rv ? dyv.vo : MASKED, i * dyv.ld2);
+  }
+  float p[8];
+  load_probs(probs, pi, gt.total_rows, lr0, p);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
     float g[8], dd[8];
-    unpack8(xg, g);
-    unpack8(dyv, dd);
+    unpack8(xg[i], g);
+    unpack8(dyt[i], dd);
     if constexpr (GATED) {
-      const uint4 xu = rv ? ld16(x + r * width_in + wa + col) : make_uint4(0, 0, 0, 0);
       float u[8];
-      unpack8(xu, u);
+      unpack8(xu[i], u);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float a, dg, du;
         dact_gated<KIND>(g[j], u[j], aa, a, dg, du);
-        m = fmaxf(m, fabsf((dg * dd[j]) * pr));
-        m = fmaxf(m, fabsf((du * dd[j]) * pr));
+        m = fmaxf(m, fabsf((dg * dd[j]) * p[i]));
+        m = fmaxf(m, fabsf((du * dd[j]) * p[i]));
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((dact_unary<KIND>(g[j], aa) * dd[j]) * pr));
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((dact_unary<KIND>(g[j], aa) * dd[j]) * p[i]));
     }
   }
-  m = quad_max(m);
-  m = row4_max(m);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(amax + pi.g), __float_as_uint(m));
+  wave_amax_to(m, tp.lane, amax + pi.g);
 }
 
-__global__ __launch_bounds__(1024) void col_sum_kernel(GroupTable gt, int64_t width,
-                                                       const uint16_t* __restrict__ x,
-                                                       float* __restrict__ out) {
-  // one group x 512 columns per workgroup; 16 waves take rows r = w, w + 16, ... in order, then the
-  // 16 partial sums are added in wave order: a fixed summation order
-  __shared__ float part[16][512];
+// Per-group column sums.  A workgroup owns one group x 128 columns; lane (rs = lane / 16,
+// cc = lane % 16) of wave w adds rows 16 t + 4 w + rs (t = 0, 1, ...) of columns 8 cc..8 cc+7 in
+// increasing t, then the 16 partial sums of a column are added in (w, rs) order: a fixed order.
+constexpr int CS_COLS = 128;
+constexpr int CS_UNROLL = 8;
+
+__global__ __launch_bounds__(256) void col_sum_kernel(GroupTable gt, int64_t width,
+                                                      const uint16_t* __restrict__ x,
+                                                      float* __restrict__ out) {
+  __shared__ float part[16][CS_COLS];
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
+  const int rs = lane >> 4, cc = lane & 15;
+  const int slot = 4 * wave + rs;
+  const int64_t col = (int64_t)blockIdx.x * CS_COLS + 8 * cc;
   const bool valid = col < width;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int r_begin = gt.row_off[g], r_end = gt.row_off[g + 1];
-  if (valid) {
-    for (int r = r_begin + wave; r < r_end; r += 16) {
-      float v[8];
-      unpack8(ld16(x + (int64_t)r * width + col), v);
+  const uint32_t ld2 = (uint32_t)width * 2u;
+  const uint32_t vo = (uint32_t)slot * ld2 + (uint32_t)col * 2u;
+  for (int rb = r_begin; rb < r_end; rb += 16 * CS_UNROLL) {
+    const rsrc_t r = view(x, (int64_t)rb * width * 2, (int64_t)gt.total_rows * width * 2);
+    uint4 v[CS_UNROLL];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += v[j];
+    for (int u = 0; u < CS_UNROLL; ++u) {
+      const bool ok = valid && rb + 16 * u + slot < r_end;
+      v[u] = bld16(r, ok ? vo : MASKED, (uint32_t)(16 * u) * ld2);
+    }
+#pragma unroll
+    for (int u = 0; u < CS_UNROLL; ++u) {
+      float f[8];
+      unpack8(v[u], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += f[j];
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) part[wave][lane * 8 + j] = acc[j];
+  for (int j = 0; j < 8; ++j) part[slot][8 * cc + j] = acc[j];
   __syncthreads();
-  if (threadIdx.x < 512) {
+  if (threadIdx.x < CS_COLS) {
     const int c = threadIdx.x;
     float s = 0.0f;
-    for (int w = 0; w < 16; ++w) s += part[w][c];
-    const int64_t oc = (int64_t)blockIdx.x * 512 + c;
+    for (int k = 0; k < 16; ++k) s += part[k][c];
+    const int64_t oc = (int64_t)blockIdx.x * CS_COLS + c;
     if (oc < width) out[(int64_t)g * width + oc] = s;
   }
 }
@@ -481,12 +864,12 @@ void fwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, con
 template <int KIND>
 void bwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
                       const uint16_t* x, const uint16_t* dy, const float* probs, int64_t width_in,
-                      int64_t wa, uint16_t* dx, const QOut& dxq, float* dprobs, const QOut& actq,
-                      int n_ct, int ct_per_wg) {
+                      int64_t wa, uint16_t* dx, const QOut& dxq, float* dp_part, const QOut& actq,
+                      int n_ct) {
   if (fmt == MGS_FMT_MXFP8)
-    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dprobs, actq, n_ct, ct_per_wg);
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, actq, n_ct);
   else
-    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dprobs, actq, n_ct, ct_per_wg);
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, actq, n_ct);
 }
 
 ActArgs to_args(const ActHost& a) { return ActArgs{a.kind, a.s, a.inv_s, a.limit, a.alpha, a.beta}; }
@@ -499,16 +882,18 @@ hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int
   if (gt.num_panels == 0) return hipSuccess;
   const ActArgs aa = to_args(act);
   const int64_t wa = out.width;
-  const int n_ct = (int)((wa + TILE_COLS - 1) / TILE_COLS);
-  const dim3 grid((unsigned)((int64_t)gt.num_panels * n_ct));
+  const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
+  const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * n_ct));
   if (fmt == MGS_FMT_NVFP4) {
+    const int n_at = (int)((wa + TILE_COLS - 1) / TILE_COLS);
+    const dim3 ag((unsigned)((int64_t)gt.num_panels * n_at));
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, group_amax, gt.num_groups);
     switch (act.kind) {
-      case MGS_ACT_IDENTITY: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_IDENTITY>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_ct, group_amax); break;
-      case MGS_ACT_SRELU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_SRELU>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_ct, group_amax); break;
-      case MGS_ACT_TANH_SRELU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_TANH_SRELU>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_ct, group_amax); break;
-      case MGS_ACT_SWIGLU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_SWIGLU>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_ct, group_amax); break;
-      default: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_CLAMPED_SWIGLU>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_ct, group_amax); break;
+      case MGS_ACT_IDENTITY: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_IDENTITY>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
+      case MGS_ACT_SRELU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_SRELU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
+      case MGS_ACT_TANH_SRELU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_TANH_SRELU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
+      case MGS_ACT_SWIGLU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_SWIGLU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
+      default: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_CLAMPED_SWIGLU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
     }
     out.amax = group_amax;
   }
@@ -524,43 +909,50 @@ hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int
 
 hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
                           const uint16_t* x, const uint16_t* dy, const float* probs, uint16_t* dx,
-                          QOut dxq, float* dx_amax, float* dprobs, QOut actq, hipStream_t st) {
+                          QOut dxq, float* dx_amax, float* dprobs, float* dp_part, QOut actq,
+                          hipStream_t st) {
   if (gt.num_panels == 0) return hipSuccess;
   const ActArgs aa = to_args(act);
   const bool gated = act.kind == MGS_ACT_SWIGLU || act.kind == MGS_ACT_CLAMPED_SWIGLU;
   const int64_t wa = gated ? width_in / 2 : width_in;
-  const int n_ct = (int)((wa + TILE_COLS - 1) / TILE_COLS);
   const bool quant_dx = dxq.row_data || dxq.col_data;
   if (fmt == MGS_FMT_NVFP4 && quant_dx) {
-    const dim3 g1((unsigned)((int64_t)gt.num_panels * n_ct));
+    const int n_at = (int)((wa + TILE_COLS - 1) / TILE_COLS);
+    const dim3 g1((unsigned)((int64_t)gt.num_panels * n_at));
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, dx_amax, gt.num_groups);
     switch (act.kind) {
-      case MGS_ACT_IDENTITY: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_IDENTITY>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_ct, dx_amax); break;
-      case MGS_ACT_SRELU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_SRELU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_ct, dx_amax); break;
-      case MGS_ACT_TANH_SRELU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_TANH_SRELU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_ct, dx_amax); break;
-      case MGS_ACT_SWIGLU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_SWIGLU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_ct, dx_amax); break;
-      default: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_CLAMPED_SWIGLU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_ct, dx_amax); break;
+      case MGS_ACT_IDENTITY: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_IDENTITY>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
+      case MGS_ACT_SRELU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_SRELU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
+      case MGS_ACT_TANH_SRELU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_TANH_SRELU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
+      case MGS_ACT_SWIGLU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_SWIGLU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
+      default: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_CLAMPED_SWIGLU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
     }
     dxq.amax = dx_amax;
   }
-  // with dprobs requested a workgroup walks the whole row width (fixed-order row sums)
-  const int ct_per_wg = dprobs ? n_ct : 1;
-  const int n_grid_ct = (n_ct + ct_per_wg - 1) / ct_per_wg;
-  const dim3 grid((unsigned)((int64_t)gt.num_panels * n_grid_ct));
+  const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
+  const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * n_ct));
+  float* part = dprobs ? dp_part : nullptr;
   switch (act.kind) {
-    case MGS_ACT_IDENTITY: bwd_dispatch_fmt<MGS_ACT_IDENTITY>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dprobs, actq, n_ct, ct_per_wg); break;
-    case MGS_ACT_SRELU: bwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dprobs, actq, n_ct, ct_per_wg); break;
-    case MGS_ACT_TANH_SRELU: bwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dprobs, actq, n_ct, ct_per_wg); break;
-    case MGS_ACT_SWIGLU: bwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dprobs, actq, n_ct, ct_per_wg); break;
-    default: bwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dprobs, actq, n_ct, ct_per_wg); break;
+    case MGS_ACT_IDENTITY: bwd_dispatch_fmt<MGS_ACT_IDENTITY>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
+    case MGS_ACT_SRELU: bwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
+    case MGS_ACT_TANH_SRELU: bwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
+    case MGS_ACT_SWIGLU: bwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
+    default: bwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
   }
+  if (dprobs && gt.total_rows > 0)
+    hipLaunchKernelGGL(dprobs_reduce_kernel, dim3((unsigned)((gt.total_rows + 255) / 256)), dim3(256), 0, st,
+                       part, n_ct, gt.total_rows, dprobs);
   return hipGetLastError();
+}
+
+int64_t act_bwd_workspace_bytes(int64_t rows, int64_t wa) {
+  return 4 * rows * ((wa + BLOCK_COLS - 1) / BLOCK_COLS);
 }
 
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,
                           hipStream_t st) {
-  const dim3 grid((unsigned)((width + 511) / 512), (unsigned)gt.num_groups);
-  hipLaunchKernelGGL(col_sum_kernel, grid, dim3(1024), 0, st, gt, width, x, out);
+  const dim3 grid((unsigned)((width + CS_COLS - 1) / CS_COLS), (unsigned)gt.num_groups);
+  hipLaunchKernelGGL(col_sum_kernel, grid, dim3(256), 0, st, gt, width, x, out);
   return hipGetLastError();
 }
 

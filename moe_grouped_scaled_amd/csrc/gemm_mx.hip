@@ -162,8 +162,8 @@ __device__ __forceinline__ void store_frag(const TileJob& j, const GemmArgs& ga,
     *p = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint2 w;
-    w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-    w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+    w.x = bf16x2(v[0], v[1]);
+    w.y = bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + gc) = w;
   }
 }
@@ -225,7 +225,6 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, r16 = lane & 15;
-  const int64_t nkb = j.k >> 5;
   const int nsteps = (int)((j.k + BK - 1) / BK);
 
   // direct-to-LDS loads of step `st` into stage buffer `stg`: wave w fills data rows 64w .. 64w + 63

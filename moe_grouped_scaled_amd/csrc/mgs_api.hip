@@ -65,6 +65,21 @@ int check_width(int64_t w, const char* what) {
   return MGS_OK;
 }
 
+// The quantizing kernels address each output through 32-bit offsets below 2^31 bytes: one group's
+// columnwise matrix (padded rows x width codes) and the whole rowwise MXFP8 scale array must fit.
+int check_extent(const mgs::GroupTable& gt, int64_t width, const char* what) {
+  const int64_t lim = (int64_t)1 << 31;
+  for (int g = 0; g < gt.num_groups; ++g) {
+    const int64_t padded = (int64_t)mgs::PANEL_ROWS * (gt.panel_off[g + 1] - gt.panel_off[g]);
+    if (padded * width >= lim)
+      return fail(MGS_ERR_SHAPE, "group %d: %lld padded rows x %s %lld reach 2^31 elements", g,
+                  (long long)padded, what, (long long)width);
+  }
+  if (4 * (int64_t)gt.total_rows * ((width + 127) / 128) >= lim)
+    return fail(MGS_ERR_SHAPE, "rows x %s too large: the rowwise scale array reaches 2 GiB", what);
+  return MGS_OK;
+}
+
 bool qbuf_requested(const mgs_qbuf* q) { return q && q->data; }
 
 int check_qbuf(const mgs_qbuf* q, int32_t fmt, const char* what) {
@@ -157,6 +172,7 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
+  if ((rc = check_extent(gt, wa, "width"))) return rc;
   if (!x_bf16) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
   if (!qbuf_requested(out_row) && !qbuf_requested(out_col))
     return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row and out_col are both empty)");
@@ -174,7 +190,7 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
                                const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
                                const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
                                const mgs_qbuf* act_col, const float* saved_group_amax,
-                               void* stream) {
+                               void* workspace, int64_t workspace_bytes, void* stream) {
   mgs::ActHost ah;
   int rc = check_act(act, &ah);
   if (rc) return rc;
@@ -185,6 +201,7 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
+  if ((rc = check_extent(gt, width_in, "width_in"))) return rc;
   if (!x_bf16) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
   if (!dy_bf16) return fail(MGS_ERR_INVALID_ARG, "dy_bf16 is NULL");
   const bool want_dxq = qbuf_requested(dx_row) || qbuf_requested(dx_col);
@@ -198,13 +215,35 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
   if (fmt == MGS_FMT_NVFP4 && qbuf_requested(act_col) && !saved_group_amax)
     return fail(MGS_ERR_UNSUPPORTED,
                 "NVFP4 recompute (act_col) needs saved_group_amax, the group amax of the forward");
+  if (dprobs) {
+    const int64_t need = mgs::act_bwd_workspace_bytes(rows, wa);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(MGS_ERR_INVALID_ARG, "dprobs needs a workspace of %lld bytes (got %lld%s)", (long long)need,
+                  (long long)workspace_bytes, workspace ? "" : ", NULL");
+  }
   mgs::QOut dxq = make_qout(dx_row, dx_col, width_in);
   mgs::QOut aq = make_qout(nullptr, act_col, wa);
   aq.amax = saved_group_amax;
   return hip_status(mgs::launch_act_bwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
                                         static_cast<const uint16_t*>(dy_bf16), probs,
                                         static_cast<uint16_t*>(dx_bf16), dxq, dx_group_amax, dprobs,
-                                        aq, static_cast<hipStream_t>(stream)));
+                                        static_cast<float*>(workspace), aq,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int64_t mgs_act_bwd_workspace_bytes(const mgs_act_params* act, const mgs_groups* groups,
+                                    int64_t width_in) {
+  mgs::ActHost ah;
+  int rc = check_act(act, &ah);
+  if (rc) return rc;
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
+  const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
+  if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
+  ok();
+  return mgs::act_bwd_workspace_bytes(rows, wa);
 }
 
 int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width, const void* x_bf16,

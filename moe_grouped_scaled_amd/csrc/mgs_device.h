@@ -18,12 +18,14 @@ namespace mgs {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// FP32 -> BF16, round to nearest, ties to even (quiet NaN kept quiet).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// FP32 -> BF16 pairs with the gfx950 convert: round to nearest, ties to even, subnormals kept (checked
+// against the integer definition over all special classes and a million random patterns); a NaN
+// stays a quiet NaN, its payload is whatever the hardware keeps.  Low half = first value.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ void unpack8(const uint4& w, float* v) {
@@ -33,10 +35,10 @@ __device__ __forceinline__ void unpack8(const uint4& w, float* v) {
 
 __device__ __forceinline__ uint4 pack8_bf16(const float* v) {
   uint4 r;
-  r.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-  r.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-  r.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
-  r.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+  r.x = bf16x2(v[0], v[1]);
+  r.y = bf16x2(v[2], v[3]);
+  r.z = bf16x2(v[4], v[5]);
+  r.w = bf16x2(v[6], v[7]);
   return r;
 }
 

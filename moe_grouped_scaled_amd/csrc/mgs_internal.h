@@ -15,7 +15,7 @@ constexpr int PANEL_ROWS = 32;
 // The columnwise (token-contiguous) layout pads each group to a multiple of 128 tokens: a whole
 // number of 128-wide K steps of the weight-gradient GEMM.
 constexpr int COL_ALIGN = 128;
-// Output columns covered by one workgroup per iteration (4 waves x 128 columns).
+// Output columns covered by one workgroup of the group-amax passes (4 waves x 128 columns).
 constexpr int TILE_COLS = 512;
 
 // Group bookkeeping passed by value in the kernel arguments.
@@ -78,9 +78,13 @@ hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int
                           const uint16_t* x, const float* probs, QOut out, float* group_amax,
                           hipStream_t stream);
 
+// dp_part: workspace of act_bwd_workspace_bytes(total rows, activation width) bytes (used when
+// dprobs is requested): per-row partial sums per 128-column tile, added in tile order afterwards.
 hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
                           const uint16_t* x, const uint16_t* dy, const float* probs, uint16_t* dx,
-                          QOut dxq, float* dx_amax, float* dprobs, QOut actq, hipStream_t stream);
+                          QOut dxq, float* dx_amax, float* dprobs, float* dp_part, QOut actq,
+                          hipStream_t stream);
+int64_t act_bwd_workspace_bytes(int64_t rows, int64_t wa);
 
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,
                           hipStream_t stream);

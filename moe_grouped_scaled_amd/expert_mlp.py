@@ -77,6 +77,13 @@ class ExpertMLP:
         return y2
 
     # ------------------------------------------------------------------ backward
+    def _workspace(self, nbytes):
+        """dprobs partial sums of the activation backward; kept between steps, grown on demand."""
+        ws = getattr(self, "_ws", None)
+        if ws is None or ws.numel() < nbytes:
+            ws = self._ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        return ws
+
     def backward(self, dy2):
         c = self.ctx
         splits, m, fmt = c["splits"], c["m"], self.fmt
@@ -96,7 +103,8 @@ class ExpertMLP:
         N.grouped_scaled_act_bwd(self.act, fmt, splits, f_in, c["y1"], da, c["probs"], dx=dy1_dense,
                                  dx_row=dy1_row, dx_col=dy1_col, dx_group_amax=self._amax_buf(e),
                                  dprobs=dprobs, act_col=a_col if self.recompute else None,
-                                 saved_group_amax=c["a_amax"])
+                                 saved_group_amax=c["a_amax"],
+                                 workspace=self._workspace(N.act_bwd_workspace_bytes(self.act, splits, f_in)))
         del da
         dx1 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
         N.grouped_gemm_mx("dgrad", fmt, splits, m, h, f_in, dy1_row, c["w1_col"], dx1)

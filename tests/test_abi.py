@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_symbols():
         assert hasattr(lib, name), name
     assert set(_native.EXPORTED) == set(_declared_symbols())
-    assert _native.abi_version() == 1
+    assert _native.abi_version() == 2
 
 
 def test_qtensor_nbytes_layouts():
@@ -90,6 +90,30 @@ def test_argument_validation_act_bwd_and_recompute():
     _expect(-1, b, act, "mxfp8", [32], 64, FAKE, FAKE, FAKE, stream=0, match="no output")
     _expect(-3, b, act, "nvfp4", [32], 64, FAKE, FAKE, FAKE, act_col=q, stream=0, match="saved_group_amax")
     _expect(-1, b, act, "nvfp4", [32], 64, FAKE, FAKE, FAKE, dx_row=q, stream=0, match="dx_group_amax")
+    import torch
+    small = torch.empty(4 * 32 - 1, dtype=torch.uint8)  # host memory: validation fails before any use
+    _expect(-1, b, act, "mxfp8", [32], 256, FAKE, FAKE, FAKE, dprobs=FAKE, workspace=small, stream=0,
+            match="workspace")
+
+
+def test_workspace_bytes():
+    from moe_grouped_scaled_amd import _native as N
+    for kind, w_in, wa in (("srelu", 4096, 4096), ("swiglu", 4096, 2048), ("identity", 96, 96)):
+        for splits in ([64, 128, 32, 32], [0, 1, 31, 33, 64], [2048] * 16):
+            m = sum(splits)
+            assert N.act_bwd_workspace_bytes(N.act_params(kind), splits, w_in) == 4 * m * -(-wa // 128)
+    _expect(-2, N.act_bwd_workspace_bytes, N.act_params("swiglu"), [32], 96)
+
+
+def test_size_limits():
+    """Quantizing calls reject a group whose padded columnwise matrix reaches 2^31 elements."""
+    from moe_grouped_scaled_amd import _native as N
+    q = _FakeQ().q
+    act = N.act_params("srelu")
+    _expect(-2, N.grouped_scaled_act_fwd, act, "mxfp8", [65536], 32768, FAKE, FAKE, out_row=q, stream=0,
+            match="2\\^31")
+    _expect(-2, N.grouped_scaled_act_bwd, act, "mxfp8", [1, 65536 - 127], 32768, FAKE, FAKE, FAKE, dx=FAKE,
+            stream=0, match="2\\^31")
 
 
 def test_argument_validation_gemm():
