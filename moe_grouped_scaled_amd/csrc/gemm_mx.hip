@@ -22,6 +22,8 @@
 // Global -> registers (prefetch of the next K step) -> LDS (rows padded to spread the banks) ->
 // fragments.  The MFMA is issued with B as its first operand so each lane's accumulator holds 4
 // consecutive output columns of one row (one 16-byte FP32 / 8-byte BF16 store per fragment).
+#include <type_traits>
+
 #include "mgs_device.h"
 
 namespace mgs {
@@ -45,6 +47,8 @@ struct Operand {
   const uint8_t* sbase;
   int64_t srows, srow0, sld;
   int rows;
+  int64_t avail;   // bytes of the operand tensor from `data` to its end
+  int64_t savail;  // bytes of the scale array from `sbase` to its end
 };
 
 struct TileJob {
@@ -58,6 +62,8 @@ struct TileJob {
   float gfactor;
   const uint16_t* bias;  // bias row of the group (length N) or null
 };
+
+constexpr int TILE_BLOCK_N = 4;
 
 // Operand layouts by mode (E groups, elements per byte 1 for MXFP8 and 2 for NVFP4):
 //   FPROP / DGRAD A: rowwise qtensor [M x k]                 (scale matrix: all M rows)
@@ -78,8 +84,26 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
   const bool nv = ga.fmt == MGS_FMT_NVFP4;
   const int ediv = nv ? 2 : 1;            // elements per byte
   const int sblk = nv ? 16 : 32;          // elements per scale
+  // Tiles of a group run in column blocks of TILE_BLOCK_N tile columns, row-major inside a block:
+  // the workgroups in flight on one XCD (dispatched together) then share each K slice of A with
+  // TILE_BLOCK_N tiles and each K slice of B with all tile rows of the block, which keeps the slices
+  // the XCD's L2 must hold small.
   const int ntn = (int)((ga.n + TN - 1) / TN);
-  const int tm = lt / ntn, tn = lt - tm * ntn;
+  const int64_t mrows = ga.mode == MGS_GEMM_WGRAD ? ga.m : tt.tok_off[g + 1] - tt.tok_off[g];
+  const int ntm = (int)((mrows + TM - 1) / TM);
+  const int full = ntn / TILE_BLOCK_N;
+  const int blk = lt / (ntm * TILE_BLOCK_N);
+  int tm, tn;
+  if (blk < full) {
+    const int r = lt - blk * ntm * TILE_BLOCK_N;
+    tm = r / TILE_BLOCK_N;
+    tn = blk * TILE_BLOCK_N + (r - tm * TILE_BLOCK_N);
+  } else {
+    const int wl = ntn - full * TILE_BLOCK_N;  // width of the last, partial block
+    const int r = lt - full * ntm * TILE_BLOCK_N;
+    tm = r / wl;
+    tn = full * TILE_BLOCK_N + (r - tm * wl);
+  }
   const int64_t brow0 = (int64_t)tn * TN;
   int64_t arows_total;
   if (ga.mode == MGS_GEMM_WGRAD) {
@@ -95,6 +119,11 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
     j.a.srows = ga.m; j.a.srow0 = arow0;
     j.b.srows = ga.n; j.b.srow0 = brow0;
     j.a.sld = j.b.sld = mp / sblk;
+    const int64_t tot = tt.tok_off[tt.num_groups];  // padded tokens of all groups
+    j.a.avail = ga.m * tot / ediv - (ga.m * coff / ediv + arow0 * j.a.ld);
+    j.b.avail = ga.n * tot / ediv - (ga.n * coff / ediv + brow0 * j.b.ld);
+    j.a.savail = ga.m * tot / sblk - ga.m * coff / sblk;
+    j.b.savail = ga.n * tot / sblk - ga.n * coff / sblk;
     arows_total = ga.m - arow0;
     j.crow0 = arow0;
     j.ldc = ga.n;
@@ -113,6 +142,10 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
     j.a.srows = tt.tok_off[tt.num_groups];
     j.a.srow0 = arow0;
     j.a.sld = ga.k / sblk;
+    const int64_t rows_all = tt.tok_off[tt.num_groups];
+    const int64_t nks = (ga.k + BK - 1) / BK;  // K steps (rowwise MXFP8 scales: 4 bytes per row and step)
+    j.a.avail = (rows_all - arow0) * j.a.ld;
+    j.a.savail = nv ? rows_all * j.a.sld : 4 * rows_all * nks;
     if (ga.mode == MGS_GEMM_FPROP) {
       j.b.ld = ga.k / ediv;
       j.b.data = ga.b_data + ((int64_t)g * ga.n + brow0) * j.b.ld;
@@ -120,6 +153,8 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
       j.b.srows = (int64_t)tt.num_groups * ga.n;
       j.b.srow0 = (int64_t)g * ga.n + brow0;
       j.b.sld = ga.k / sblk;
+      j.b.avail = ((int64_t)tt.num_groups * ga.n - ((int64_t)g * ga.n + brow0)) * j.b.ld;
+      j.b.savail = nv ? j.b.srows * j.b.sld : 4 * j.b.srows * nks;
     } else {
       const int64_t kp = (ga.k + COL_ALIGN - 1) / COL_ALIGN * COL_ALIGN;
       j.b.ld = kp / ediv;
@@ -128,6 +163,8 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
       j.b.srows = ga.n;
       j.b.srow0 = brow0;
       j.b.sld = kp / sblk;
+      j.b.avail = ((int64_t)tt.num_groups * ga.n - ((int64_t)g * ga.n + brow0)) * j.b.ld;
+      j.b.savail = ((int64_t)tt.num_groups - g) * ga.n * kp / sblk;
     }
     arows_total = mg - (int64_t)tm * TM;
     j.crow0 = arow0;
@@ -143,29 +180,41 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
   return j;
 }
 
-// Epilogue for one 16 x 16 fragment held as C[row][col0 .. col0 + 3] in each lane.
-__device__ __forceinline__ void store_frag(const TileJob& j, const GemmArgs& ga, int row, int col,
-                                           v4f acc) {
-  if (row >= j.a.rows || col >= j.b.rows) return;  // b.rows is a multiple of 4 (N % 32 == 0)
-  const int64_t gr = j.crow0 + row, gc = j.ccol0 + col;
-  float v[4] = {acc[0] * j.gfactor, acc[1] * j.gfactor, acc[2] * j.gfactor, acc[3] * j.gfactor};
+// Epilogue value of one 16 x 16 fragment held as C[row][col0 .. col0 + 3] in each lane: the group
+// factor, then the bias (four BF16 values, already fetched).
+__device__ __forceinline__ void frag_values(const TileJob& j, v4f acc, uint2 bw, float (&v)[4]) {
+  v[0] = acc[0] * j.gfactor; v[1] = acc[1] * j.gfactor; v[2] = acc[2] * j.gfactor; v[3] = acc[3] * j.gfactor;
   if (j.bias) {
-    const uint2 bw = *reinterpret_cast<const uint2*>(j.bias + j.ccol0 + col);
     v[0] += bf16lo(bw.x); v[1] += bf16hi(bw.x); v[2] += bf16lo(bw.y); v[3] += bf16hi(bw.y);
   }
+}
+
+__device__ __forceinline__ void store_values(const TileJob& j, int row, int col, const float (&v)[4]) {
+  if (row >= j.a.rows || col >= j.b.rows) return;  // b.rows is a multiple of 4 (N % 32 == 0)
+  const int64_t gr = j.crow0 + row, gc = j.ccol0 + col;
   if (j.c32) {
-    float4* p = reinterpret_cast<float4*>(j.c32 + gr * j.ldc + gc);
-    if (ga.accumulate) {
-      const float4 o = *p;
-      v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
-    }
-    *p = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(j.c32 + gr * j.ldc + gc) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint2 w;
     w.x = bf16x2(v[0], v[1]);
     w.y = bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + gc) = w;
   }
+}
+
+// Epilogue for one 16 x 16 fragment (used by the NVFP4 kernel): bias and accumulation read directly.
+__device__ __forceinline__ void store_frag(const TileJob& j, const GemmArgs& ga, int row, int col,
+                                           v4f acc) {
+  if (row >= j.a.rows || col >= j.b.rows) return;
+  uint2 bw = make_uint2(0, 0);
+  if (j.bias) bw = *reinterpret_cast<const uint2*>(j.bias + j.ccol0 + col);
+  float v[4];
+  frag_values(j, acc, bw, v);
+  if (j.c32 && ga.accumulate) {
+    const float4 o = *reinterpret_cast<const float4*>(j.c32 + (j.crow0 + row) * j.ldc + j.ccol0 + col);
+    v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+  }
+  store_values(j, row, col, v);
 }
 
 template <int TM, int TN>
@@ -198,12 +247,38 @@ constexpr int STAGE_BYTES = DATA_BYTES + (BM2 + BN2) * 4;  // + 2 KiB of scales
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// a pointer that is the same in every lane, moved to scalar registers
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+// Raw buffer descriptor of `bytes` bytes at `p` (record count capped at 2^31 - 1; gfx9 descriptor
+// word 3), as four scalar registers.  The arguments are wave-uniform (they derive from the tile
+// index); the compiler cannot prove it for values read from the kernel's group tables, so they are
+// moved to scalar registers explicitly.
+typedef int sdesc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sdesc_t gemm_view(const uint8_t* p, int64_t bytes) {
+  bytes = bytes < 0 ? 0 : (bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes);
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return sdesc_t{(int)lo, (int)(hi & 0xffffu), n, 0x00020000};
+}
+
+// Direct-to-LDS buffer loads (16 or 4 bytes per lane) to LDS byte address `lds` + 16 (or 4) x lane.
+// Issued as inline assembly: the compiler's LDS-alias tracking would otherwise make later reads of
+// the other stage wait for these loads.  It therefore does not count them either; every wait for
+// them is an explicit s_waitcnt in the kernel.
+// The scalar operands are wave-uniform by construction; readfirstlane tells the compiler so (values
+// derived from the group tables are not provably uniform to it).
+__device__ __forceinline__ void dma16(const sdesc_t& d, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(d), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const sdesc_t& d, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(d), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 __device__ __forceinline__ int xcd_remap_gemm(int b, int n) {
@@ -212,9 +287,113 @@ __device__ __forceinline__ int xcd_remap_gemm(int b, int n) {
   return x * q + min(x, r) + i;
 }
 
+// Scaled FP8 MFMA with the accumulator pinned to AGPRs.  Written as inline assembly because the
+// register allocator otherwise keeps part of the 256 accumulators of a wave in VGPRs and spills the
+// fragments.  The compiler does not see these as MFMAs, so code around them supplies the wait states
+// it would insert: mfma_valu_gap() after VALU writes of fragments that feed an MFMA, and
+// mfma_drain() before VALU reads the accumulators.
+__device__ __forceinline__ void mfma_scale_fp8(v4f& acc, const v8i& b, const v8i& a, int sb, int sa) {
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(acc)
+               : "v"(b), "v"(a), "v"(sb), "v"(sa));
+}
+__device__ __forceinline__ void mfma_valu_gap() { asm volatile("s_nop 7"); }
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+}
+
+// Epilogue of the 256 x 256 kernel: group factor, bias (from LDS), optional FP32 accumulation, store.
+__device__ __forceinline__ void epilogue_256(const TileJob& j, const GemmArgs& ga, v4f (&acc)[8][8],
+                                             const uint2* bias_lds, int wm, int wn, int q, int r16) {
+  // epilogue: bias from LDS; one straight-line variant per output kind, so that stores never wait
+  // for each other (with accumulation, the eight C fragments of a fragment row are loaded together
+  // before any of them is stored: one memory round trip per fragment row)
+  uint2 bw[8];
+#pragma unroll
+  for (int fn = 0; fn < 8; ++fn)
+    bw[fn] = j.bias ? bias_lds[(wn * 128 + fn * 16 + 4 * q) >> 2] : make_uint2(0, 0);
+  auto epilogue = [&](auto c32_tag, auto acc_tag) {
+    constexpr bool C32 = decltype(c32_tag)::value, ACC = decltype(acc_tag)::value;
+#pragma unroll
+    for (int fm = 0; fm < 8; ++fm) {
+      const int row = wm * 128 + fm * 16 + r16;
+      const bool rok = row < j.a.rows;
+      const int64_t gr = j.crow0 + row;
+      float4 old[8];
+      if constexpr (ACC) {
+#pragma unroll
+        for (int fn = 0; fn < 8; ++fn) {
+          const int col = wn * 128 + fn * 16 + 4 * q;
+          old[fn] = rok && col < j.b.rows ? *reinterpret_cast<const float4*>(j.c32 + gr * j.ldc + j.ccol0 + col)
+                                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+      }
+#pragma unroll
+      for (int fn = 0; fn < 8; ++fn) {
+        const int col = wn * 128 + fn * 16 + 4 * q;
+        float v[4];
+        frag_values(j, acc[fm][fn], bw[fn], v);
+        if constexpr (ACC) {
+          v[0] += old[fn].x; v[1] += old[fn].y; v[2] += old[fn].z; v[3] += old[fn].w;
+        }
+        if (rok && col < j.b.rows) {
+          if constexpr (C32) {
+            *reinterpret_cast<float4*>(j.c32 + gr * j.ldc + j.ccol0 + col) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            uint2 w;
+            w.x = bf16x2(v[0], v[1]);
+            w.y = bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + j.ccol0 + col) = w;
+          }
+        }
+      }
+    }
+  };
+  if (!j.c32) epilogue(std::false_type{}, std::false_type{});
+  else if (!ga.accumulate) epilogue(std::true_type{}, std::false_type{});
+  else epilogue(std::true_type{}, std::true_type{});
+}
+
+// Per-tile state of the direct-to-LDS loads: buffer descriptors of the operands, their scales and the
+// bias, and the offsets that locate the tile's rows.  Lanes differ only in voa / vob.
+struct TileDma {
+  sdesc_t ad, bd, as, bs, bias;
+  uint32_t voa, vob;      // lane offset of the lane's first data row (+ its chunk swizzle)
+  uint32_t a_ld8, b_ld8;  // bytes between successive 8-row groups
+  uint32_t a_s4, b_s4;    // bytes per K step of the scale arrays
+  uint32_t a_sr, b_sr;    // scale byte offset of the tile's first row
+  bool has_bias;
+};
+
+__device__ __forceinline__ TileDma tile_dma(const TileJob& j, int wave, int lane) {
+  TileDma d;
+  d.ad = gemm_view(j.a.data, j.a.avail);
+  d.bd = gemm_view(j.b.data, j.b.avail);
+  d.as = gemm_view(j.a.sbase, j.a.savail);
+  d.bs = gemm_view(j.b.sbase, j.b.savail);
+  const int lrow = lane >> 3, pchunk = lane & 7;
+  const uint32_t lswz = (uint32_t)((pchunk ^ (lrow & 7)) << 4);
+  d.voa = (uint32_t)((wave * 64 + lrow) * j.a.ld) + lswz;
+  d.vob = (uint32_t)((wave * 64 + lrow) * j.b.ld) + lswz;
+  d.a_ld8 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * j.a.ld));
+  d.b_ld8 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * j.b.ld));
+  d.a_s4 = __builtin_amdgcn_readfirstlane((uint32_t)(j.a.srows * 4));
+  d.b_s4 = __builtin_amdgcn_readfirstlane((uint32_t)(j.b.srows * 4));
+  d.a_sr = __builtin_amdgcn_readfirstlane((uint32_t)(j.a.srow0 * 4));
+  d.b_sr = __builtin_amdgcn_readfirstlane((uint32_t)(j.b.srow0 * 4));
+  d.has_bias = j.bias != nullptr;
+  d.bias = gemm_view(reinterpret_cast<const uint8_t*>(j.bias + j.ccol0), 2 * (int64_t)j.b.rows);
+  return d;
+}
+
+// One workgroup per 256 x 256 output tile.  (A persistent variant that walks several tiles per
+// workgroup and prefetches the next tile during the last K step measured slower: on this GPU one
+// vector-memory counter covers loads and stores in issue order, so waiting for the next step's
+// operands also waits for the previous tile's output stores.)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint2 bias_lds[BN2 / 4];
   const int tile = xcd_remap_gemm(blockIdx.x, gridDim.x);
   const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
   if (j.k == 0) {
@@ -225,47 +404,30 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, r16 = lane & 15;
-  const int nsteps = (int)((j.k + BK - 1) / BK);
+  const int swz_lo = (q ^ (r16 & 7)) << 4, swz_hi = ((4 + q) ^ (r16 & 7)) << 4;
+  const uint32_t vs = (uint32_t)((wave * 64 + lane) * 4);  // scale dword of the lane's row
+  const TileDma d = tile_dma(j, wave, lane);
 
   // direct-to-LDS loads of step `st` into stage buffer `stg`: wave w fills data rows 64w .. 64w + 63
-  // of A and of B (8 instructions of 8 rows each per operand) and their scale bytes (4 instructions
-  // of 16 rows x 4 blocks each per operand).  Addresses are a wave-uniform 64-bit base (SGPRs) plus
-  // a 32-bit per-lane offset, computed once.
-  const uint8_t* abase = uniform_ptr(j.a.data);
-  const uint8_t* bbase = uniform_ptr(j.b.data);
-  const uint8_t* asbase = uniform_ptr(j.a.sbase);
-  const uint8_t* bsbase = uniform_ptr(j.b.sbase);
-  const int lrow = lane >> 3, pchunk = lane & 7;
-  uint32_t offa[8], offb[8], c16[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = wave * 64 + i * 8 + lrow;
-    const int ra = row < j.a.rows ? row : j.a.rows - 1;
-    const int rb = row < j.b.rows ? row : j.b.rows - 1;
-    c16[i] = (uint32_t)((pchunk ^ (row & 7)) << 4);
-    offa[i] = (uint32_t)(ra * j.a.ld);
-    offb[i] = (uint32_t)(rb * j.b.ld);
-  }
-  // scale rows of this lane (one dword = the 4 block scales of a K step per row)
-  const int srow = wave * 64 + lane;
-  const uint32_t sra = (uint32_t)(j.a.srow0 + (srow < j.a.rows ? srow : j.a.rows - 1));
-  const uint32_t srb = (uint32_t)(j.b.srow0 + (srow < j.b.rows ? srow : j.b.rows - 1));
-  const uint32_t a_srows = (uint32_t)j.a.srows, b_srows = (uint32_t)j.b.srows;
+  // of A and of B (8 instructions of 8 rows x 128 bytes each per operand) and their scale dwords
+  // (one per row; the K-step scale dword of row r and step st sits at ((st * srows) + srow0 + r) * 4).
+  // Each operand is read through a buffer descriptor based at the tile's first row whose record
+  // count ends at the end of the operand tensor: rows past the tile edge read the following rows or
+  // zeros (their outputs are not stored), and a partial last K step reads past the row end (those
+  // chunks are zeroed in registers).  Rows 8 apart share the 16-byte chunk swizzle c ^ (row & 7).
   auto issue = [&](int st, uint8_t* stg) {
     const uint32_t k0 = (uint32_t)st * BK;
-    uint8_t* sa = stg;
-    uint8_t* sb = stg + BM2 * BK;
-    uint8_t* ssa = stg + DATA_BYTES;
-    uint8_t* ssb = ssa + BM2 * 4;
+    const uint32_t sa = lds_addr(stg) + wave * 8 * 1024;
+    const uint32_t sb = sa + BM2 * BK;
+    const uint32_t ssa = lds_addr(stg) + DATA_BYTES + wave * 256;
+    const uint32_t ssb = ssa + BM2 * 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // tail chunks (at or past K) read chunk 0 of the step instead; they are zeroed in registers
-      const uint32_t kk = k0 + ((int64_t)(k0 + c16[i]) < j.k ? c16[i] : 0u);
-      __builtin_amdgcn_global_load_lds(abase + (offa[i] + kk), (lds_ptr_t)(sa + (wave * 8 + i) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bbase + (offb[i] + kk), (lds_ptr_t)(sb + (wave * 8 + i) * 1024), 16, 0, 0);
+      dma16(d.ad, d.voa, i * d.a_ld8 + k0, sa + i * 1024);
+      dma16(d.bd, d.vob, i * d.b_ld8 + k0, sb + i * 1024);
     }
-    __builtin_amdgcn_global_load_lds(asbase + ((uint32_t)st * a_srows + sra) * 4u, (lds_ptr_t)(ssa + wave * 256), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(bsbase + ((uint32_t)st * b_srows + srb) * 4u, (lds_ptr_t)(ssb + wave * 256), 4, 0, 0);
+    dma4(d.as, vs, (uint32_t)st * d.a_s4 + d.a_sr, ssa);
+    dma4(d.bs, vs, (uint32_t)st * d.b_s4 + d.b_sr, ssb);
   };
 
   v4f acc[8][8];
@@ -273,55 +435,76 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   for (int fm = 0; fm < 8; ++fm)
 #pragma unroll
     for (int fn = 0; fn < 8; ++fn) acc[fm][fn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_valu_gap();
+  __builtin_amdgcn_sched_barrier(0);
 
-  // One K step from stage buffer `stg`: every fragment of the step is read from LDS first, then the
-  // direct-to-LDS loads of the next step are issued into the other buffer (the compiler makes LDS
-  // reads wait for all direct loads in flight, so they must not come after them), then the 64 MFMAs
-  // run while those loads are in flight.  With `tail`, K chunks at or past `rem` are zeroed.
+  // One K step from stage buffer `stg`: the direct-to-LDS loads of the next step go into the other
+  // buffer first, so the load engine stays busy through the fragment reads and the 64 MFMAs of this
+  // step.  The eight B fragments of the wave are read up front; A fragments stream: the reads of
+  // fragment row fm + 1 are issued between the first MFMAs of row fm, so half of the LDS reads
+  // overlap the matrix cores and 80 fragment registers are live.  With `tail`, K chunks at or past
+  // `rem` are zeroed.
   auto step = [&](const uint8_t* stg, bool tail, int64_t rem, int next_st, uint8_t* next_stg) {
+    if (next_st >= 0) issue(next_st, next_stg);
     const uint8_t* sa = stg;
     const uint8_t* sb = stg + BM2 * BK;
     const uint8_t* ssa = stg + DATA_BYTES;
     const uint8_t* ssb = ssa + BM2 * 4;
     const bool lo_ok = !tail || 16 * q < rem, hi_ok = !tail || 64 + 16 * q < rem;
     const uint32_t mlo = lo_ok ? 0xffffffffu : 0u, mhi = hi_ok ? 0xffffffffu : 0u;
-    v8i bfr[8], afr[8];
-    int csb[8], csa[8];
+    // fragment f of a wave's 128 rows starts at row (128 w + 16 f + r16); rows 16 f apart share the
+    // chunk swizzle (r16 & 7), so the fragment index only moves the address by an immediate
+    const uint8_t* pb = sb + (wn * 128 + r16) * BK;
+    const uint8_t* pa = sa + (wm * 128 + r16) * BK;
+    const uint8_t* psb = ssb + (wn * 128 + r16) * 4 + q;
+    const uint8_t* psa = ssa + (wm * 128 + r16) * 4 + q;
+    auto half = [&](const uint8_t* p, int f, int swz) {
+      return *reinterpret_cast<const uint4*>(p + f * 16 * BK + swz);
+    };
+    auto join = [&](uint4 x0, uint4 x1) {
+      return v8i{(int)(x0.x & mlo), (int)(x0.y & mlo), (int)(x0.z & mlo), (int)(x0.w & mlo),
+                 (int)(x1.x & mhi), (int)(x1.y & mhi), (int)(x1.z & mhi), (int)(x1.w & mhi)};
+    };
+    v8i bfr[8];
+    int csb[8];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      const int row = wn * 128 + f * 16 + r16;
-      const uint8_t* pr = sb + row * BK;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(pr + ((q ^ (row & 7)) << 4));
-      const uint4 b1 = *reinterpret_cast<const uint4*>(pr + (((4 + q) ^ (row & 7)) << 4));
-      bfr[f] = v8i{(int)(b0.x & mlo), (int)(b0.y & mlo), (int)(b0.z & mlo), (int)(b0.w & mlo),
-                   (int)(b1.x & mhi), (int)(b1.y & mhi), (int)(b1.z & mhi), (int)(b1.w & mhi)};
-      csb[f] = ssb[row * 4 + q];
+      bfr[f] = join(half(pb, f, swz_lo), half(pb, f, swz_hi));
+      csb[f] = psb[f * 64];
     }
+    uint4 alo = half(pa, 0, swz_lo), ahi = half(pa, 0, swz_hi);
+    int csn = psa[0];
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int row = wm * 128 + f * 16 + r16;
-      const uint8_t* pr = sa + row * BK;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(pr + ((q ^ (row & 7)) << 4));
-      const uint4 a1 = *reinterpret_cast<const uint4*>(pr + (((4 + q) ^ (row & 7)) << 4));
-      afr[f] = v8i{(int)(a0.x & mlo), (int)(a0.y & mlo), (int)(a0.z & mlo), (int)(a0.w & mlo),
-                   (int)(a1.x & mhi), (int)(a1.y & mhi), (int)(a1.z & mhi), (int)(a1.w & mhi)};
-      csa[f] = ssa[row * 4 + q];
+    for (int fm = 0; fm < 8; ++fm) {
+      const v8i afr = join(alo, ahi);
+      const int csa = csn;
+      if (tail) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_valu_gap();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int fn = 0; fn < 8; ++fn) {
+        mfma_scale_fp8(acc[fm][fn], bfr[fn], afr, csb[fn], csa);
+        // the next A fragment row streams in behind the first three MFMAs of this row
+        if (fm < 7) {
+          if (fn == 0) alo = half(pa, fm + 1, swz_lo);
+          if (fn == 1) ahi = half(pa, fm + 1, swz_hi);
+          if (fn == 2) csn = psa[(fm + 1) * 64];
+        }
+      }
     }
-    if (next_st >= 0) issue(next_st, next_stg);
-#pragma unroll
-    for (int fm = 0; fm < 8; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 8; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[fn], afr[fm], acc[fm][fn], 0, 0, 0,
-                                                                       csb[fn], 0, csa[fm]);
-    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
   issue(0, smem);
+  // the tile's bias (BN2 BF16 values = 512 bytes) goes to LDS with the first step, by waves 0 and 1
+  if (d.has_bias && wave < 2) dma4(d.bias, (uint32_t)(wave * 256 + lane * 4), 0, lds_addr(bias_lds) + wave * 256);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const int nsteps = __builtin_amdgcn_readfirstlane((int)((j.k + BK - 1) / BK));
   const int64_t last_rem = j.k - (int64_t)(nsteps - 1) * BK;
   const bool tail_step = last_rem < BK;
   const int full_steps = tail_step ? nsteps - 1 : nsteps;
@@ -330,11 +513,10 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
     step(smem + (st & 1) * STAGE_BYTES, false, BK, nx, smem + ((st + 1) & 1) * STAGE_BYTES);
   }
   if (tail_step) step(smem + ((nsteps - 1) & 1) * STAGE_BYTES, true, last_rem, -1, nullptr);
-#pragma unroll
-  for (int fm = 0; fm < 8; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 8; ++fn)
-      store_frag(j, ga, wm * 128 + fm * 16 + r16, wn * 128 + fn * 16 + 4 * q, acc[fm][fn]);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_drain();
+  __builtin_amdgcn_sched_barrier(0);
+  epilogue_256(j, ga, acc, bias_lds, wm, wn, q, r16);
 }
 
 // ------------------------------------------------------------------------------------ NVFP4 path
