@@ -415,19 +415,25 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   // count ends at the end of the operand tensor: rows past the tile edge read the following rows or
   // zeros (their outputs are not stored), and a partial last K step reads past the row end (those
   // chunks are zeroed in registers).  Rows 8 apart share the 16-byte chunk swizzle c ^ (row & 7).
-  auto issue = [&](int st, uint8_t* stg) {
+  // Loads are issued one 1 KB instruction at a time: the wave cannot issue past a load the memory
+  // pipeline has no room for, so a burst of them would stall the MFMAs behind it.
+  // instruction n of step st: n < 8: B rows 8n of the wave's 64; 8 <= n < 16: A rows 8(n - 8)
+  auto issue_one = [&](int st, uint8_t* stg, int n) {
     const uint32_t k0 = (uint32_t)st * BK;
     const uint32_t sa = lds_addr(stg) + wave * 8 * 1024;
     const uint32_t sb = sa + BM2 * BK;
+    if (n < 8) dma16(d.bd, d.vob, n * d.b_ld8 + k0, sb + n * 1024);
+    else dma16(d.ad, d.voa, (n - 8) * d.a_ld8 + k0, sa + (n - 8) * 1024);
+  };
+  auto issue_scales = [&](int st, uint8_t* stg) {
     const uint32_t ssa = lds_addr(stg) + DATA_BYTES + wave * 256;
     const uint32_t ssb = ssa + BM2 * 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      dma16(d.ad, d.voa, i * d.a_ld8 + k0, sa + i * 1024);
-      dma16(d.bd, d.vob, i * d.b_ld8 + k0, sb + i * 1024);
-    }
     dma4(d.as, vs, (uint32_t)st * d.a_s4 + d.a_sr, ssa);
     dma4(d.bs, vs, (uint32_t)st * d.b_s4 + d.b_sr, ssb);
+  };
+  auto issue = [&](int st, uint8_t* stg) {
+    for (int n = 0; n < 16; ++n) issue_one(st, stg, n);
+    issue_scales(st, stg);
   };
 
   v4f acc[8][8];
@@ -439,14 +445,17 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   mfma_valu_gap();
   __builtin_amdgcn_sched_barrier(0);
 
-  // One K step from stage buffer `stg`: the direct-to-LDS loads of the next step go into the other
-  // buffer first, so the load engine stays busy through the fragment reads and the 64 MFMAs of this
-  // step.  The eight B fragments of the wave are read up front; A fragments stream: the reads of
-  // fragment row fm + 1 are issued between the first MFMAs of row fm, so half of the LDS reads
-  // overlap the matrix cores and 80 fragment registers are live.  With `tail`, K chunks at or past
-  // `rem` are zeroed.
+  // One K step from stage buffer `stg` while the next step's loads go into the other buffer: four of
+  // its load instructions before the fragment reads, the scales after the first MFMA and the other
+  // twelve after every second MFMA (a pace the load pipeline absorbs without stalling the wave).
+  // A fragment row 0 and the eight B fragments are read up front (the first MFMA waits only for the
+  // first of them); A fragments then stream: the reads of fragment row fm + 1 are issued between the
+  // first MFMAs of row fm, so most LDS reads overlap the matrix cores and 80 fragment registers are
+  // live.  With `tail`, K chunks at or past `rem` are zeroed.
+  constexpr int PRE_LOADS = 4, LOAD_PACE = 2;
   auto step = [&](const uint8_t* stg, bool tail, int64_t rem, int next_st, uint8_t* next_stg) {
-    if (next_st >= 0) issue(next_st, next_stg);
+    if (next_st >= 0)
+      for (int n = 0; n < PRE_LOADS; ++n) issue_one(next_st, next_stg, n);
     const uint8_t* sa = stg;
     const uint8_t* sb = stg + BM2 * BK;
     const uint8_t* ssa = stg + DATA_BYTES;
@@ -466,6 +475,8 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
       return v8i{(int)(x0.x & mlo), (int)(x0.y & mlo), (int)(x0.z & mlo), (int)(x0.w & mlo),
                  (int)(x1.x & mhi), (int)(x1.y & mhi), (int)(x1.z & mhi), (int)(x1.w & mhi)};
     };
+    uint4 alo = half(pa, 0, swz_lo), ahi = half(pa, 0, swz_hi);
+    int csn = psa[0];
     v8i bfr[8];
     int csb[8];
 #pragma unroll
@@ -473,8 +484,6 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
       bfr[f] = join(half(pb, f, swz_lo), half(pb, f, swz_hi));
       csb[f] = psb[f * 64];
     }
-    uint4 alo = half(pa, 0, swz_lo), ahi = half(pa, 0, swz_hi);
-    int csn = psa[0];
 #pragma unroll
     for (int fm = 0; fm < 8; ++fm) {
       const v8i afr = join(alo, ahi);
@@ -487,6 +496,12 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
 #pragma unroll
       for (int fn = 0; fn < 8; ++fn) {
         mfma_scale_fp8(acc[fm][fn], bfr[fn], afr, csb[fn], csa);
+        if (next_st >= 0) {
+          const int m = fm * 8 + fn;
+          if (m == 0) issue_scales(next_st, next_stg);
+          if (m % LOAD_PACE == LOAD_PACE - 1 && PRE_LOADS + m / LOAD_PACE < 16)
+            issue_one(next_st, next_stg, PRE_LOADS + m / LOAD_PACE);
+        }
         // the next A fragment row streams in behind the first three MFMAs of this row
         if (fm < 7) {
           if (fn == 0) alo = half(pa, fm + 1, swz_lo);
