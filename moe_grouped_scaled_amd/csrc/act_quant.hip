@@ -346,65 +346,6 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0.0f;
 }
 
-// Lane placement shared by the tile kernels: workgroup tile t -> (panel, column tile), the lane's
-// first row lr0 and first column col.
-struct TilePos {
-  PanelInfo pi;
-  int ct, lane, wave, lr0;
-};
-
-__device__ __forceinline__ TilePos tile_pos(const GroupTable& gt, int n_ct) {
-  TilePos tp;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int panel = t / n_ct;
-  tp.ct = t - panel * n_ct;
-  tp.pi = find_panel(gt, panel);
-  tp.lane = threadIdx.x & 63;
-  tp.wave = threadIdx.x >> 6;
-  tp.lr0 = 8 * (tp.lane & 3);
-  return tp;
-}
-
-__device__ __forceinline__ int64_t tile_col(const TilePos& tp, int ct) {
-  return (int64_t)ct * TILE_COLS + tp.wave * 128 + 8 * (tp.lane >> 2);
-}
-
-// max over the whole wave, then one unsigned atomic max on the FP32 bit pattern of the non-negative
-// result, which orders like the value itself: the group maximum is order-independent.
-__device__ __forceinline__ void wave_amax_to(float m, int lane, float* dst) {
-  m = quad_max(m);
-  m = row4_max(m);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(m));
-}
-
-// max|y| per group (NVFP4 first pass)
-template <int KIND>
-__global__ __launch_bounds__(256) void act_amax_kernel(ActArgs aa, GroupTable gt,
-                                                       const uint16_t* __restrict__ x,
-                                                       const float* __restrict__ probs,
-                                                       int64_t width_in, int64_t wa, int n_ct,
-                                                       float* __restrict__ amax) {
-  constexpr bool GATED = is_gated<KIND>();
-  const TilePos tp = tile_pos(gt, n_ct);
-  const int64_t col = tile_col(tp, tp.ct);
-  const bool valid = col < wa;
-  const Bf16View xv = bf16_view(x, width_in, tp.pi.row0, gt.total_rows, tp.lr0, col);
-  uint4 xg[8], xu[GATED ? 8 : 1];
-  load_x<GATED>(xv, (uint32_t)wa * 2u, tp.lr0, tp.pi.nrows, valid, xg, xu);
-  float p[8];
-  load_probs(probs, tp.pi, gt.total_rows, tp.lr0, p);
-  float y[8][8];
-  compute_y<KIND>(aa, xg, xu, p, y);
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[i][j]));
-  wave_amax_to(m, tp.lane, amax + tp.pi.g);
-}
-
 // S_dec = 1 / S_enc per group, written once per launch (covers empty groups too)
 __device__ __forceinline__ void write_group_scales(const GroupTable& gt, const QOut& q) {
   if (blockIdx.x != 0 || q.amax == nullptr) return;
@@ -754,55 +695,6 @@ __global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* __restr
   dprobs[r] = s;
 }
 
-// max|dx| per group over the full dx width (NVFP4 first pass of the backward)
-template <int KIND>
-__global__ __launch_bounds__(256) void act_bwd_amax_kernel(ActArgs aa, GroupTable gt,
-                                                           const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ dy,
-                                                           const float* __restrict__ probs,
-                                                           int64_t width_in, int64_t wa, int n_ct,
-                                                           float* __restrict__ amax) {
-  constexpr bool GATED = is_gated<KIND>();
-  const TilePos tp = tile_pos(gt, n_ct);
-  const PanelInfo& pi = tp.pi;
-  const int lr0 = tp.lr0;
-  const int64_t col = tile_col(tp, tp.ct);
-  const bool valid = col < wa;
-  const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, lr0, col);
-  const Bf16View dyv = bf16_view(dy, wa, pi.row0, gt.total_rows, lr0, col);
-  uint4 xg[8], xu[GATED ? 8 : 1], dyt[8];
-  load_x<GATED>(xv, (uint32_t)wa * 2u, lr0, pi.nrows, valid, xg, xu);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool rv = valid && (lr0 + i) < pi.nrows;
-    dyt[i] = bld16(dyv.r, rv ? dyv.vo : MASKED, i * dyv.ld2);
-  }
-  float p[8];
-  load_probs(probs, pi, gt.total_rows, lr0, p);
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float g[8], dd[8];
-    unpack8(xg[i], g);
-    unpack8(dyt[i], dd);
-    if constexpr (GATED) {
-      float u[8];
-      unpack8(xu[i], u);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float a, dg, du;
-        dact_gated<KIND>(g[j], u[j], aa, a, dg, du);
-        m = fmaxf(m, fabsf((dg * dd[j]) * p[i]));
-        m = fmaxf(m, fabsf((du * dd[j]) * p[i]));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((dact_unary<KIND>(g[j], aa) * dd[j]) * p[i]));
-    }
-  }
-  wave_amax_to(m, tp.lane, amax + pi.g);
-}
-
 // Per-group column sums.  A workgroup owns one group x 128 columns; lane (rs = lane / 16,
 // cc = lane % 16) of wave w adds rows 16 t + 4 w + rs (t = 0, 1, ...) of columns 8 cc..8 cc+7 in
 // increasing t, then the 16 partial sums of a column are added in (w, rs) order: a fixed order.
@@ -851,6 +743,109 @@ __global__ __launch_bounds__(256) void col_sum_kernel(GroupTable gt, int64_t wid
   }
 }
 
+// Group amax for NVFP4 (first pass).  A workgroup owns one 128-token block (wave w: panel 4b + w)
+// and a run of `cpw` 128-column chunks, takes max |value| over them in registers (DPP and shuffles
+// over the wave, LDS over the four waves) and adds one unsigned atomic max of the FP32 bits to its
+// group's entry: far fewer atomics on the per-group array (one cache line for all groups) than one
+// per wave.  BWD: the value is dx = (da/dg * dy) * p (both halves for gated kinds); else y = a * p.
+template <int KIND, bool BWD>
+__global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable gt,
+                                                         const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ dy,
+                                                         const float* __restrict__ probs,
+                                                         int64_t width_in, int64_t wa, int n_chunks,
+                                                         int cpw, float* __restrict__ amax) {
+  constexpr bool GATED = is_gated<KIND>();
+  __shared__ float wmax[4];
+  const BlockPos bp = block_pos(gt, (n_chunks + cpw - 1) / cpw);
+  const PanelInfo& pi = bp.pi;
+  const int lr0 = bp.lr0;
+  float p[8];
+  load_probs(probs, pi, gt.total_rows, lr0, p);
+  float m = 0.0f;
+  const int c_end = min(n_chunks, (bp.ct + 1) * cpw);
+  for (int c = bp.ct * cpw; c < c_end; ++c) {
+    const int64_t col = (int64_t)c * BLOCK_COLS + 8 * bp.cc;
+    const bool valid = col < wa;
+    const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, lr0, col);
+    uint4 xg[8], xu[GATED ? 8 : 1];
+    load_x<GATED>(xv, (uint32_t)wa * 2u, lr0, pi.nrows, valid, xg, xu);
+    if constexpr (BWD) {
+      const Bf16View dyv = bf16_view(dy, wa, pi.row0, gt.total_rows, lr0, col);
+      uint4 dyt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool rv = valid && (lr0 + i) < pi.nrows;
+        dyt[i] = bld16(dyv.r, rv ? dyv.vo : MASKED, i * dyv.ld2);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float dd = bf16_at(dyt[i], j), g = bf16_at(xg[i], j);
+          if constexpr (GATED) {
+            const float u = bf16_at(xu[GATED ? i : 0], j);
+            float a, dg, du;
+            dact_gated<KIND>(g, u, aa, a, dg, du);
+            m = fmaxf(m, fabsf((dg * dd) * p[i]));
+            m = fmaxf(m, fabsf((du * dd) * p[i]));
+          } else {
+            m = fmaxf(m, fabsf((dact_unary<KIND>(g, aa) * dd) * p[i]));
+          }
+        }
+      }
+    } else {
+      float y[8][8];
+      compute_y<KIND>(aa, xg, xu, p, y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[i][j]));
+    }
+  }
+  m = quad_max(m);
+  m = row4_max(m);
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (bp.lane == 0) wmax[bp.wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax + pi.g), __float_as_uint(b));
+  }
+}
+
+// chunks per workgroup of the amax pass: about 1024 workgroups in all (at most 32 chunks each)
+int amax_cpw(const GroupTable& gt, int n_chunks) {
+  const int64_t units = (int64_t)(gt.num_panels / 4) * n_chunks;
+  int64_t c = units / 1024;
+  return (int)(c < 1 ? 1 : (c > 32 ? 32 : c));
+}
+
+template <int KIND, bool BWD>
+void launch_group_amax(hipStream_t st, const ActArgs& aa, const GroupTable& gt, const uint16_t* x,
+                       const uint16_t* dy, const float* probs, int64_t width_in, int64_t wa,
+                       float* amax) {
+  const int n_chunks = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
+  const int cpw = amax_cpw(gt, n_chunks);
+  const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * ((n_chunks + cpw - 1) / cpw)));
+  hipLaunchKernelGGL((group_amax_kernel<KIND, BWD>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa,
+                     n_chunks, cpw, amax);
+}
+
+template <bool BWD>
+void group_amax_dispatch(int kind, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
+                         const uint16_t* x, const uint16_t* dy, const float* probs, int64_t width_in,
+                         int64_t wa, float* amax) {
+  switch (kind) {
+    case MGS_ACT_IDENTITY: launch_group_amax<MGS_ACT_IDENTITY, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_SRELU: launch_group_amax<MGS_ACT_SRELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_TANH_SRELU: launch_group_amax<MGS_ACT_TANH_SRELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_SWIGLU: launch_group_amax<MGS_ACT_SWIGLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    default: launch_group_amax<MGS_ACT_CLAMPED_SWIGLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+  }
+}
+
 template <int KIND>
 void fwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
                       const uint16_t* x, const float* probs, int64_t width_in, const QOut& out,
@@ -885,16 +880,8 @@ hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int
   const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
   const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * n_ct));
   if (fmt == MGS_FMT_NVFP4) {
-    const int n_at = (int)((wa + TILE_COLS - 1) / TILE_COLS);
-    const dim3 ag((unsigned)((int64_t)gt.num_panels * n_at));
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, group_amax, gt.num_groups);
-    switch (act.kind) {
-      case MGS_ACT_IDENTITY: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_IDENTITY>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
-      case MGS_ACT_SRELU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_SRELU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
-      case MGS_ACT_TANH_SRELU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_TANH_SRELU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
-      case MGS_ACT_SWIGLU: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_SWIGLU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
-      default: hipLaunchKernelGGL((act_amax_kernel<MGS_ACT_CLAMPED_SWIGLU>), ag, dim3(256), 0, st, aa, gt, x, probs, width_in, wa, n_at, group_amax); break;
-    }
+    group_amax_dispatch<false>(act.kind, st, aa, gt, x, nullptr, probs, width_in, wa, group_amax);
     out.amax = group_amax;
   }
   switch (act.kind) {
@@ -917,16 +904,8 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
   const int64_t wa = gated ? width_in / 2 : width_in;
   const bool quant_dx = dxq.row_data || dxq.col_data;
   if (fmt == MGS_FMT_NVFP4 && quant_dx) {
-    const int n_at = (int)((wa + TILE_COLS - 1) / TILE_COLS);
-    const dim3 g1((unsigned)((int64_t)gt.num_panels * n_at));
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, dx_amax, gt.num_groups);
-    switch (act.kind) {
-      case MGS_ACT_IDENTITY: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_IDENTITY>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
-      case MGS_ACT_SRELU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_SRELU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
-      case MGS_ACT_TANH_SRELU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_TANH_SRELU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
-      case MGS_ACT_SWIGLU: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_SWIGLU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
-      default: hipLaunchKernelGGL((act_bwd_amax_kernel<MGS_ACT_CLAMPED_SWIGLU>), g1, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, n_at, dx_amax); break;
-    }
+    group_amax_dispatch<true>(act.kind, st, aa, gt, x, dy, probs, width_in, wa, dx_amax);
     dxq.amax = dx_amax;
   }
   const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);

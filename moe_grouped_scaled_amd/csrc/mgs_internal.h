@@ -15,8 +15,6 @@ constexpr int PANEL_ROWS = 32;
 // The columnwise (token-contiguous) layout pads each group to a multiple of 128 tokens: a whole
 // number of 128-wide K steps of the weight-gradient GEMM.
 constexpr int COL_ALIGN = 128;
-// Output columns covered by one workgroup of the group-amax passes (4 waves x 128 columns).
-constexpr int TILE_COLS = 512;
 
 // Group bookkeeping passed by value in the kernel arguments.
 //   row_off[g]   = sum_{h<g} m_h                            (E + 1 entries)
