@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MGS_ABI_VERSION 2
+#define MGS_ABI_VERSION 3
 #define MGS_MAX_GROUPS 256
 
 enum mgs_status {
@@ -132,7 +132,7 @@ int64_t mgs_qtensor_nbytes(int32_t fmt, int32_t colwise, const mgs_groups* group
  * [P2] Greptile summary, first bullet (the per-row scale, the activation and the grouped quantization
  * share one pass) and sequence diagram (the forward activation call takes x, the scales, the
  * quantizer and split_sizes and returns the grouped quantized tensor).
- *   x_bf16     [M x width_in] BF16, row-major (required)
+ *   x_bf16     [M x width_in] BF16, row-major (required unless M == 0)
  *   probs      [M] FP32 per-row scale; NULL means 1 for every row
  *   out_row    rowwise qtensor of y [M x W_a] (W_a = width_in, or width_in/2 for gated kinds); nullable
  *   out_col    columnwise qtensor of y; nullable (NULL in the recompute forward, [P1] Description)
@@ -147,40 +147,59 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
 /* Fused backward.  [P2] sequence diagram, backward half: grouped_scaled_d{swiglu,srelu}(grad, input_,
  * scales, quantizer) -> (grouped_dy, dense_dy, grad_scales), where grad = dL/d(act_out * scales);
  * [P1] Description: activation recompute regenerates FC2's input from the saved BF16 FC1 output.
- *   x_bf16        [M x width_in] BF16 saved FC1 output (required)
- *   dy_bf16       [M x W_a] BF16 dL/d(a * p) (required)
+ *   x_bf16        [M x width_in] BF16 saved FC1 output (required unless M == 0)
+ *   dy_bf16       [M x W_a] BF16 dL/d(a * p) (required unless M == 0)
  *   probs         [M] FP32; NULL means 1
  *   dx_bf16       [M x width_in] BF16 dense dL/dx = dy * p * a'(x); nullable
  *   dx_row/dx_col quantized dL/dx (rowwise / columnwise); nullable
  *   dx_group_amax [E] FP32: required when dx is quantized to NVFP4 (receives max|dL/dx| per group)
  *   dprobs        [M] FP32 dL/dp = sum_j dy * a(x); nullable
+ *   dx_col_sum    [E x width_in] FP32 per-group column sums of the dense BF16 dL/dx (the values dx_bf16
+ *                 holds, whether or not it is requested): the FC1 bias gradient.  [P1] Description,
+ *                 second paragraph (bias in the fused step).  Nullable; empty groups give zeros.
  *   act_col       columnwise qtensor of y = a(x) * p regenerated from x (recompute); nullable.  Its bytes
  *                 equal those the forward's out_col would have held.
  *   saved_group_amax [E] FP32 group amax written by the forward; required for an NVFP4 act_col.
  *   workspace     DEVICE scratch of at least mgs_act_bwd_workspace_bytes() bytes, required when dprobs
- *                 is requested (else ignored; may be NULL); owned by the caller, contents undefined
- *                 before and after the call.  The kernel writes one partial sum per row and
- *                 128-column tile there and a second kernel adds them in tile order, so dprobs is
- *                 deterministic.  Calls that share a workspace must not overlap.
- *   workspace_bytes its size; MGS_ERR_INVALID_ARG when dprobs is requested and it is too small. */
+ *                 or dx_col_sum is requested (else ignored; may be NULL); owned by the caller,
+ *                 contents undefined before and after the call.  The kernel writes partial sums there
+ *                 (dprobs: one per row and 128-column tile; column sums: one per 128-token block and
+ *                 column) and second kernels add them in a fixed order, so both are deterministic.
+ *                 Calls that share a workspace must not overlap.
+ *   workspace_bytes its size; MGS_ERR_INVALID_ARG when it is needed and too small. */
 int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
                                int64_t width_in, const void* x_bf16, const void* dy_bf16,
                                const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
                                const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
-                               const mgs_qbuf* act_col, const float* saved_group_amax,
-                               void* workspace, int64_t workspace_bytes, void* stream);
+                               float* dx_col_sum, const mgs_qbuf* act_col,
+                               const float* saved_group_amax, void* workspace,
+                               int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes mgs_grouped_scaled_act_bwd needs for dprobs: 4 * M * ceil(W_a / 128).
+/* Workspace bytes mgs_grouped_scaled_act_bwd needs for dprobs and dx_col_sum:
+ * roundup(4 * M * ceil(W_a / 128), 256) + 4 * (P / 128) * width_in, P = sum_g roundup(m_g, 128).
  * Negative MGS_ERR_* on invalid arguments. */
 int64_t mgs_act_bwd_workspace_bytes(const mgs_act_params* act, const mgs_groups* groups,
                                     int64_t width_in);
 
 /* Plain grouped quantization of a BF16 tensor (weights, upstream gradients, FC1 input): the forward
  * above with act = IDENTITY and p = 1.  [P2] Greptile summary, second bullet (GroupedLinear consumes a
- * pre-quantized grouped tensor); [P3] "A behaviour change worth calling out" (columnwise usage). */
+ * pre-quantized grouped tensor); [P3] "A behaviour change worth calling out" (columnwise usage).
+ *   out_row, out_col, group_amax as in mgs_grouped_scaled_act_fwd (group_amax required for NVFP4 when
+ *              a quantized output is requested)
+ *   col_sum    [E x width] FP32 per-group column sums of x in the same pass (the FC2 bias gradient when
+ *              x is dL/dY2); nullable; empty groups give zeros.  At least one of out_row, out_col,
+ *              col_sum must be requested.
+ *   workspace  DEVICE scratch of at least mgs_grouped_mx_quantize_workspace_bytes() bytes, required
+ *              when col_sum is requested (per-block partial sums, added in block order by a second
+ *              kernel); caller-owned, contents undefined before and after; calls sharing it must not
+ *              overlap.  workspace_bytes: its size (MGS_ERR_INVALID_ARG when needed and too small). */
 int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width, const void* x_bf16,
                             const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
-                            void* stream);
+                            float* col_sum, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of mgs_grouped_mx_quantize's col_sum: 4 * (P / 128) * width,
+ * P = sum_g roundup(m_g, 128).  Negative MGS_ERR_* on invalid arguments. */
+int64_t mgs_grouped_mx_quantize_workspace_bytes(const mgs_groups* groups, int64_t width);
 
 /* Grouped GEMM on quantized operands with FP32 accumulation.  [P2] Greptile summary, second bullet and
  * sequence diagram (GroupedLinear forward / backward on a pre-built grouped tensor).

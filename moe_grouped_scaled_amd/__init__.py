@@ -18,4 +18,5 @@ from ._native import (  # noqa: F401
     grouped_scaled_act_bwd,
     grouped_scaled_act_fwd,
     qtensor_nbytes,
+    quantize_workspace_bytes,
 )

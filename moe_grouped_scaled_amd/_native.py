@@ -59,9 +59,10 @@ def _load():
         "mgs_qtensor_nbytes": (i64, [i32, i32, pgr, i64, i32]),
         "mgs_grouped_scaled_act_fwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, pq, pq, vp, vp]),
         "mgs_grouped_scaled_act_bwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, vp, vp, pq, pq, vp,
-                                                      vp, pq, vp, vp, i64, vp]),
+                                                      vp, vp, pq, vp, vp, i64, vp]),
         "mgs_act_bwd_workspace_bytes": (i64, [pact, pgr, i64]),
-        "mgs_grouped_mx_quantize": (ctypes.c_int, [i32, pgr, i64, vp, pq, pq, vp, vp]),
+        "mgs_grouped_mx_quantize": (ctypes.c_int, [i32, pgr, i64, vp, pq, pq, vp, vp, vp, i64, vp]),
+        "mgs_grouped_mx_quantize_workspace_bytes": (i64, [pgr, i64]),
         "mgs_grouped_gemm_mx": (ctypes.c_int, [i32, i32, pgr, i64, i64, i64, pq, pq, vp, i32, vp, i32,
                                                vp]),
         "mgs_grouped_col_sum": (ctypes.c_int, [pgr, i64, vp, vp, vp]),
@@ -76,7 +77,7 @@ def _load():
 LIB = _load()
 EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
             "mgs_grouped_scaled_act_bwd", "mgs_act_bwd_workspace_bytes", "mgs_grouped_mx_quantize",
-            "mgs_grouped_gemm_mx", "mgs_grouped_col_sum")
+            "mgs_grouped_mx_quantize_workspace_bytes", "mgs_grouped_gemm_mx", "mgs_grouped_col_sum")
 
 
 def _check(rc):
@@ -179,32 +180,47 @@ def act_bwd_workspace_bytes(act, split_sizes, width_in):
 
 
 def grouped_scaled_act_bwd(act, fmt, split_sizes, width_in, x, dy, probs, dx=None, dx_row=None,
-                           dx_col=None, dx_group_amax=None, dprobs=None, act_col=None,
+                           dx_col=None, dx_group_amax=None, dprobs=None, dx_col_sum=None, act_col=None,
                            saved_group_amax=None, workspace=None, stream=None):
-    """`workspace` (a CUDA tensor) is needed with dprobs; when it is None one of the right size is
-    allocated here for the call."""
+    """`workspace` (a CUDA tensor) is needed with dprobs or dx_col_sum; when it is None one of the
+    right size is allocated here for the call."""
     g = _GroupsArg(split_sizes)
     _r, rref = _qref(dx_row)
     _c, cref = _qref(dx_col)
     _a, aref = _qref(act_col)
-    if dprobs is not None and workspace is None:
+    if (dprobs is not None or dx_col_sum is not None) and workspace is None:
         workspace = torch.empty(max(act_bwd_workspace_bytes(act, split_sizes, width_in), 1),
                                 dtype=torch.uint8, device="cuda")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(LIB.mgs_grouped_scaled_act_bwd(ctypes.byref(act), FMT[fmt], g.ref, int(width_in), _ptr(x),
                                           _ptr(dy), _ptr(probs), _ptr(dx), rref, cref,
-                                          _ptr(dx_group_amax), _ptr(dprobs), aref,
+                                          _ptr(dx_group_amax), _ptr(dprobs), _ptr(dx_col_sum), aref,
                                           _ptr(saved_group_amax), _ptr(workspace), int(ws_bytes),
                                           _stream(stream)))
 
 
+def quantize_workspace_bytes(split_sizes, width):
+    g = _GroupsArg(split_sizes)
+    n = LIB.mgs_grouped_mx_quantize_workspace_bytes(g.ref, int(width))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
 def grouped_mx_quantize(fmt, split_sizes, width, x, out_row=None, out_col=None, group_amax=None,
-                        stream=None):
+                        col_sum=None, workspace=None, stream=None):
+    """`workspace` (a CUDA tensor) is needed with col_sum; when it is None one of the right size is
+    allocated here for the call."""
     g = _GroupsArg(split_sizes)
     _r, rref = _qref(out_row)
     _c, cref = _qref(out_col)
+    if col_sum is not None and workspace is None:
+        workspace = torch.empty(max(quantize_workspace_bytes(split_sizes, width), 1), dtype=torch.uint8,
+                                device="cuda")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(LIB.mgs_grouped_mx_quantize(FMT[fmt], g.ref, int(width), _ptr(x), rref, cref,
-                                       _ptr(group_amax), _stream(stream)))
+                                       _ptr(group_amax), _ptr(col_sum), _ptr(workspace), int(ws_bytes),
+                                       _stream(stream)))
 
 
 def grouped_gemm_mx(mode, fmt, split_sizes, m, n, k, a, b, c, bias=None, accumulate=False,

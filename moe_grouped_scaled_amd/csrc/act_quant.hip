@@ -380,6 +380,7 @@ struct Stage {
 
 struct BlockPos {
   PanelInfo pi;   // the wave's panel
+  int gb;         // 128-token block index over all groups (columnwise padded rows / 128)
   int blk;        // 128-token block index within the group
   int ct;         // 128-column tile
   int lane, wave, lr0, cc;
@@ -395,6 +396,7 @@ __device__ __forceinline__ BlockPos block_pos(const GroupTable& gt, int n_ct) {
   bp.lane = threadIdx.x & 63;
   bp.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   bp.pi = find_panel(gt, 4 * b + bp.wave);
+  bp.gb = b;
   bp.blk = bp.pi.lpanel >> 2;
   bp.lr0 = 8 * (bp.lane & 3);
   bp.cc = bp.lane >> 2;
@@ -488,13 +490,42 @@ __device__ __forceinline__ void flush_col(const uint8_t* st, const QOut& q, int6
   }
 }
 
+// Per-group column sums (bias gradients) fused into a block pass.  The lane's sums over its 8 rows
+// (rows in increasing order), then its quad (the four lanes of a column chunk: (l0 + l1) + (l2 + l3)),
+// go to LDS per wave; after a barrier, thread t < 128 adds the four waves' sums of column t in wave
+// order and stores the block's partial sum at part[gb * ld + col].  A second kernel adds a group's
+// blocks in block order.  Every order is fixed: the result is deterministic.
+__device__ __forceinline__ void cs_stage(float (&s)[8], float* lds, const BlockPos& bp) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s[j] += dpp_f<DPP_QUAD_XOR1>(s[j]);
+    s[j] += dpp_f<DPP_QUAD_XOR2>(s[j]);
+  }
+  if ((bp.lane & 3) == 0) {
+    float4* d = reinterpret_cast<float4*>(lds + bp.wave * BLOCK_COLS + 8 * bp.cc);
+    d[0] = make_float4(s[0], s[1], s[2], s[3]);
+    d[1] = make_float4(s[4], s[5], s[6], s[7]);
+  }
+}
+
+__device__ __forceinline__ void cs_flush(const float* lds, float* __restrict__ part, int64_t ld,
+                                         int64_t col0, int64_t w_lim, int64_t out_off, int gb) {
+  const int t = threadIdx.x;
+  if (t < BLOCK_COLS && col0 + t < w_lim) {
+    const float v = ((lds[t] + lds[BLOCK_COLS + t]) + lds[2 * BLOCK_COLS + t]) + lds[3 * BLOCK_COLS + t];
+    part[(int64_t)gb * ld + out_off + col0 + t] = v;
+  }
+}
+
 template <int KIND, int FMT>
 __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
                                                       const uint16_t* __restrict__ x,
                                                       const float* __restrict__ probs,
-                                                      int64_t width_in, QOut out, int n_ct) {
+                                                      int64_t width_in, QOut out, float* __restrict__ cs_part,
+                                                      int n_ct) {
   constexpr bool GATED = is_gated<KIND>();
   __shared__ __attribute__((aligned(16))) uint8_t stage[Stage<FMT>::BYTES];
+  __shared__ __attribute__((aligned(16))) float cs_lds[4 * BLOCK_COLS];
   const int64_t wa = out.width;
   const BlockPos bp = block_pos(gt, n_ct);
   const PanelInfo& pi = bp.pi;
@@ -513,10 +544,21 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
   compute_y<KIND>(aa, xg, xu, p, y);
   if (out.row_data)
     emit_row<FMT>(y, row_dst<FMT>(out, wa, gt.total_rows, pi.row0, bp.lr0, bp.col, bp.lane), bp.lr0, pi.nrows, valid, s_enc);
-  if (out.col_data) {
-    stage_tile<FMT>(y, stage, bp, s_enc);
+  if (cs_part) {
+    float cs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      cs[j] = y[0][j];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) cs[j] += y[i][j];
+    }
+    cs_stage(cs, cs_lds, bp);
+  }
+  if (out.col_data) stage_tile<FMT>(y, stage, bp, s_enc);
+  if (out.col_data || cs_part) {
     __syncthreads();
-    flush_col<FMT>(stage, out, wa, (int64_t)PANEL_ROWS * gt.num_panels, bp);
+    if (out.col_data) flush_col<FMT>(stage, out, wa, (int64_t)PANEL_ROWS * gt.num_panels, bp);
+    if (cs_part) cs_flush(cs_lds, cs_part, wa, bp.col0, wa, 0, bp.gb);
   }
 }
 
@@ -556,11 +598,14 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
                                                       const float* __restrict__ probs,
                                                       int64_t width_in, int64_t wa,
                                                       uint16_t* __restrict__ dx, QOut dxq,
-                                                      float* __restrict__ dp_part, QOut actq, int n_ct) {
+                                                      float* __restrict__ dp_part, float* __restrict__ cs_part,
+                                                      QOut actq, int n_ct) {
   constexpr bool GATED = is_gated<KIND>();
   constexpr int SB = Stage<FMT>::BYTES;
   // stages: dx columnwise (gate half), dx columnwise (up half, gated kinds), recomputed activation
   __shared__ __attribute__((aligned(16))) uint8_t stage[(GATED ? 3 : 2) * SB];
+  // column sums of the dense BF16 dx: gate half (or the only half), up half
+  __shared__ __attribute__((aligned(16))) float cs_lds[(GATED ? 2 : 1) * 4 * BLOCK_COLS];
   uint8_t* st_dx = stage;
   uint8_t* st_up = stage + SB;
   uint8_t* st_act = stage + (GATED ? 2 : 1) * SB;
@@ -594,6 +639,21 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
   const RowDst rd = row_dst<FMT>(dxq, width_in, gt.total_rows, pi.row0, lr0, col, bp.lane);
 
   float d[8][8], dpacc[8];
+  // column sums over the lane's rows (in row order) of the BF16-rounded dx, the values the dense
+  // output holds; taken from the finished tile so that no accumulators live through the row loop
+  auto col_sums = [&](float* lds) {
+    float cs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const uint32_t w = bf16x2(d[i][j], d[i + 1][j]);
+        cs[j] = i == 0 ? bf16lo(w) : cs[j] + bf16lo(w);
+        cs[j] += bf16hi(w);
+      }
+    }
+    cs_stage(cs, lds, bp);
+  };
   // rows: dx (gate half) -> dense store, rowwise codes, dprobs partials
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -610,6 +670,7 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
     if (dx) bst16(pack8_bf16(d[i]), dxv.r, rv ? dxv.vo : MASKED, i * dxv.ld2);
     if (dxq.row_data) quant_row<FMT>(d[i], rd, i, rv, s_dx);
   }
+  if (cs_part) col_sums(cs_lds);
   if (dxq.col_data) stage_tile<FMT>(d, st_dx, bp, s_dx);
   // gated: the up half in the same registers
   if constexpr (GATED) {
@@ -629,6 +690,7 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
       if (dx) bst16(pack8_bf16(d[i]), dxv.r, rv ? dxv.vo + up2 : MASKED, i * dxv.ld2);
       if (dxq.row_data) quant_row<FMT>(d[i], ru, i, rv, s_dx);
     }
+    if (cs_part) col_sums(cs_lds + 4 * BLOCK_COLS);
     if (dxq.col_data) stage_tile<FMT>(d, st_up, bp, s_dx);
   }
   // recompute: y = a * p -> columnwise codes of the activation
@@ -671,8 +733,12 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
     }
   }
 
-  if (dxq.col_data || actq.col_data) {
+  if (dxq.col_data || actq.col_data || cs_part) {
     __syncthreads();
+    if (cs_part) {
+      cs_flush(cs_lds, cs_part, width_in, bp.col0, wa, 0, bp.gb);
+      if constexpr (GATED) cs_flush(cs_lds + 4 * BLOCK_COLS, cs_part, width_in, bp.col0, wa, wa, bp.gb);
+    }
     if (dxq.col_data) {
       flush_col<FMT>(st_dx, dxq, width_in, total_padded, bp);
       if constexpr (GATED) {
@@ -685,14 +751,38 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
   }
 }
 
+// Sum of n partials p[0], p[stride], ... in index order.  The loads go out eight at a time so that a
+// thread waits for one memory round trip per eight partials rather than one per partial.
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_t stride, int n) {
+  float s = 0.0f;
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(i + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; i < n; ++i) s += p[(int64_t)i * stride];
+  return s;
+}
+
 // dprobs[r] = sum over column tiles of the partials, in tile order
 __global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* __restrict__ part, int n_ct,
                                                             int rows, float* __restrict__ dprobs) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= rows) return;
-  float s = 0.0f;
-  for (int c = 0; c < n_ct; ++c) s += part[(int64_t)c * rows + r];
-  dprobs[r] = s;
+  dprobs[r] = ordered_sum(part + r, rows, n_ct);
+}
+
+// out[g, c] = sum of the partial sums of group g's 128-token blocks, in block order.
+__global__ __launch_bounds__(256) void col_sum_reduce_kernel(const float* __restrict__ part, GroupTable gt,
+                                                             int64_t width, float* __restrict__ out) {
+  const int g = blockIdx.y;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= width) return;
+  const int b0 = gt.panel_off[g] >> 2, b1 = gt.panel_off[g + 1] >> 2;
+  out[(int64_t)g * width + c] = ordered_sum(part + (int64_t)b0 * width + c, width, b1 - b0);
 }
 
 // Per-group column sums.  A workgroup owns one group x 128 columns; lane (rs = lane / 16,
@@ -849,22 +939,27 @@ void group_amax_dispatch(int kind, hipStream_t st, const ActArgs& aa, const Grou
 template <int KIND>
 void fwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
                       const uint16_t* x, const float* probs, int64_t width_in, const QOut& out,
-                      int n_ct) {
+                      float* cs_part, int n_ct) {
   if (fmt == MGS_FMT_MXFP8)
-    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, n_ct);
+    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct);
   else
-    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, n_ct);
+    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct);
 }
 
 template <int KIND>
 void bwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
                       const uint16_t* x, const uint16_t* dy, const float* probs, int64_t width_in,
-                      int64_t wa, uint16_t* dx, const QOut& dxq, float* dp_part, const QOut& actq,
-                      int n_ct) {
+                      int64_t wa, uint16_t* dx, const QOut& dxq, float* dp_part, float* cs_part,
+                      const QOut& actq, int n_ct) {
   if (fmt == MGS_FMT_MXFP8)
-    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, actq, n_ct);
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
   else
-    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, actq, n_ct);
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
+}
+
+void launch_col_sum_reduce(const GroupTable& gt, int64_t width, const float* part, float* out, hipStream_t st) {
+  const dim3 grid((unsigned)((width + 255) / 256), (unsigned)gt.num_groups);
+  hipLaunchKernelGGL(col_sum_reduce_kernel, grid, dim3(256), 0, st, part, gt, width, out);
 }
 
 ActArgs to_args(const ActHost& a) { return ActArgs{a.kind, a.s, a.inv_s, a.limit, a.alpha, a.beta}; }
@@ -873,35 +968,49 @@ ActArgs to_args(const ActHost& a) { return ActArgs{a.kind, a.s, a.inv_s, a.limit
 
 hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
                           const uint16_t* x, const float* probs, QOut out, float* group_amax,
-                          hipStream_t st) {
-  if (gt.num_panels == 0) return hipSuccess;
+                          float* col_sum, float* cs_part, hipStream_t st) {
+  if (gt.num_panels == 0) {
+    // every group is empty: its column sums are zeros
+    if (col_sum) launch_col_sum_reduce(gt, out.width, cs_part, col_sum, st);
+    return hipGetLastError();
+  }
   const ActArgs aa = to_args(act);
   const int64_t wa = out.width;
   const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
   const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * n_ct));
+  float* cs = col_sum ? cs_part : nullptr;
+  // column sums alone: no quantized output, so no group amax pass and no format-specific work
+  if (!out.row_data && !out.col_data) fmt = MGS_FMT_MXFP8;
   if (fmt == MGS_FMT_NVFP4) {
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, group_amax, gt.num_groups);
     group_amax_dispatch<false>(act.kind, st, aa, gt, x, nullptr, probs, width_in, wa, group_amax);
     out.amax = group_amax;
   }
   switch (act.kind) {
-    case MGS_ACT_IDENTITY: fwd_dispatch_fmt<MGS_ACT_IDENTITY>(fmt, grid, st, aa, gt, x, probs, width_in, out, n_ct); break;
-    case MGS_ACT_SRELU: fwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, n_ct); break;
-    case MGS_ACT_TANH_SRELU: fwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, n_ct); break;
-    case MGS_ACT_SWIGLU: fwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, n_ct); break;
-    default: fwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, n_ct); break;
+    case MGS_ACT_IDENTITY: fwd_dispatch_fmt<MGS_ACT_IDENTITY>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    case MGS_ACT_SRELU: fwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    case MGS_ACT_TANH_SRELU: fwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    case MGS_ACT_SWIGLU: fwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    default: fwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
   }
+  if (col_sum) launch_col_sum_reduce(gt, wa, cs_part, col_sum, st);
   return hipGetLastError();
 }
 
 hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
                           const uint16_t* x, const uint16_t* dy, const float* probs, uint16_t* dx,
-                          QOut dxq, float* dx_amax, float* dprobs, float* dp_part, QOut actq,
-                          hipStream_t st) {
-  if (gt.num_panels == 0) return hipSuccess;
-  const ActArgs aa = to_args(act);
+                          QOut dxq, float* dx_amax, float* dprobs, float* dx_col_sum, void* workspace,
+                          QOut actq, hipStream_t st) {
   const bool gated = act.kind == MGS_ACT_SWIGLU || act.kind == MGS_ACT_CLAMPED_SWIGLU;
   const int64_t wa = gated ? width_in / 2 : width_in;
+  float* cs_part = dx_col_sum ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                         act_bwd_cs_offset(gt.total_rows, wa))
+                              : nullptr;
+  if (gt.num_panels == 0) {
+    if (dx_col_sum) launch_col_sum_reduce(gt, width_in, cs_part, dx_col_sum, st);
+    return hipGetLastError();
+  }
+  const ActArgs aa = to_args(act);
   const bool quant_dx = dxq.row_data || dxq.col_data;
   if (fmt == MGS_FMT_NVFP4 && quant_dx) {
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, dx_amax, gt.num_groups);
@@ -910,22 +1019,32 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
   }
   const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
   const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * n_ct));
-  float* part = dprobs ? dp_part : nullptr;
+  float* part = dprobs ? static_cast<float*>(workspace) : nullptr;
   switch (act.kind) {
-    case MGS_ACT_IDENTITY: bwd_dispatch_fmt<MGS_ACT_IDENTITY>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
-    case MGS_ACT_SRELU: bwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
-    case MGS_ACT_TANH_SRELU: bwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
-    case MGS_ACT_SWIGLU: bwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
-    default: bwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, actq, n_ct); break;
+    case MGS_ACT_IDENTITY: bwd_dispatch_fmt<MGS_ACT_IDENTITY>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
+    case MGS_ACT_SRELU: bwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
+    case MGS_ACT_TANH_SRELU: bwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
+    case MGS_ACT_SWIGLU: bwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
+    default: bwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
   }
   if (dprobs && gt.total_rows > 0)
     hipLaunchKernelGGL(dprobs_reduce_kernel, dim3((unsigned)((gt.total_rows + 255) / 256)), dim3(256), 0, st,
                        part, n_ct, gt.total_rows, dprobs);
+  if (dx_col_sum) launch_col_sum_reduce(gt, width_in, cs_part, dx_col_sum, st);
   return hipGetLastError();
 }
 
-int64_t act_bwd_workspace_bytes(int64_t rows, int64_t wa) {
-  return 4 * rows * ((wa + BLOCK_COLS - 1) / BLOCK_COLS);
+int64_t act_bwd_cs_offset(int64_t rows, int64_t wa) {
+  const int64_t dp = 4 * rows * ((wa + BLOCK_COLS - 1) / BLOCK_COLS);
+  return (dp + 255) & ~(int64_t)255;
+}
+
+int64_t col_sum_part_bytes(const GroupTable& gt, int64_t width) {
+  return 4 * (int64_t)(gt.num_panels / 4) * width;
+}
+
+int64_t act_bwd_workspace_bytes(const GroupTable& gt, int64_t wa, int64_t width_in) {
+  return act_bwd_cs_offset(gt.total_rows, wa) + col_sum_part_bytes(gt, width_in);
 }
 
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,

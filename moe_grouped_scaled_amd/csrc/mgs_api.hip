@@ -173,7 +173,7 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
   if ((rc = check_extent(gt, wa, "width"))) return rc;
-  if (!x_bf16) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
+  if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
   if (!qbuf_requested(out_row) && !qbuf_requested(out_col))
     return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row and out_col are both empty)");
   if ((rc = check_qbuf(out_row, fmt, "out_row"))) return rc;
@@ -182,15 +182,17 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
     return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
   const mgs::QOut q = make_qout(out_row, out_col, wa);
   return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
-                                        probs, q, group_amax, static_cast<hipStream_t>(stream)));
+                                        probs, q, group_amax, nullptr, nullptr,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
                                int64_t width_in, const void* x_bf16, const void* dy_bf16,
                                const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
                                const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
-                               const mgs_qbuf* act_col, const float* saved_group_amax,
-                               void* workspace, int64_t workspace_bytes, void* stream) {
+                               float* dx_col_sum, const mgs_qbuf* act_col,
+                               const float* saved_group_amax, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
   mgs::ActHost ah;
   int rc = check_act(act, &ah);
   if (rc) return rc;
@@ -202,10 +204,10 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
   if ((rc = check_extent(gt, width_in, "width_in"))) return rc;
-  if (!x_bf16) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
-  if (!dy_bf16) return fail(MGS_ERR_INVALID_ARG, "dy_bf16 is NULL");
+  if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
+  if (!dy_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "dy_bf16 is NULL");
   const bool want_dxq = qbuf_requested(dx_row) || qbuf_requested(dx_col);
-  if (!dx_bf16 && !want_dxq && !dprobs && !qbuf_requested(act_col))
+  if (!dx_bf16 && !want_dxq && !dprobs && !dx_col_sum && !qbuf_requested(act_col))
     return fail(MGS_ERR_INVALID_ARG, "no output requested");
   if ((rc = check_qbuf(dx_row, fmt, "dx_row"))) return rc;
   if ((rc = check_qbuf(dx_col, fmt, "dx_col"))) return rc;
@@ -215,11 +217,12 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
   if (fmt == MGS_FMT_NVFP4 && qbuf_requested(act_col) && !saved_group_amax)
     return fail(MGS_ERR_UNSUPPORTED,
                 "NVFP4 recompute (act_col) needs saved_group_amax, the group amax of the forward");
-  if (dprobs) {
-    const int64_t need = mgs::act_bwd_workspace_bytes(rows, wa);
+  if (dprobs || dx_col_sum) {
+    const int64_t need = mgs::act_bwd_workspace_bytes(gt, wa, width_in);
     if (need > 0 && (!workspace || workspace_bytes < need))
-      return fail(MGS_ERR_INVALID_ARG, "dprobs needs a workspace of %lld bytes (got %lld%s)", (long long)need,
-                  (long long)workspace_bytes, workspace ? "" : ", NULL");
+      return fail(MGS_ERR_INVALID_ARG, "%s needs a workspace of %lld bytes (got %lld%s)",
+                  dprobs ? "dprobs" : "dx_col_sum", (long long)need, (long long)workspace_bytes,
+                  workspace ? "" : ", NULL");
   }
   mgs::QOut dxq = make_qout(dx_row, dx_col, width_in);
   mgs::QOut aq = make_qout(nullptr, act_col, wa);
@@ -227,8 +230,7 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
   return hip_status(mgs::launch_act_bwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
                                         static_cast<const uint16_t*>(dy_bf16), probs,
                                         static_cast<uint16_t*>(dx_bf16), dxq, dx_group_amax, dprobs,
-                                        static_cast<float*>(workspace), aq,
-                                        static_cast<hipStream_t>(stream)));
+                                        dx_col_sum, workspace, aq, static_cast<hipStream_t>(stream)));
 }
 
 int64_t mgs_act_bwd_workspace_bytes(const mgs_act_params* act, const mgs_groups* groups,
@@ -243,15 +245,51 @@ int64_t mgs_act_bwd_workspace_bytes(const mgs_act_params* act, const mgs_groups*
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
   ok();
-  return mgs::act_bwd_workspace_bytes(rows, wa);
+  return mgs::act_bwd_workspace_bytes(gt, wa, width_in);
 }
 
 int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width, const void* x_bf16,
                             const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
-                            void* stream) {
-  mgs_act_params id{MGS_ACT_IDENTITY, 1.0f, 1.0f, 1.0f, 0.0f};
-  return mgs_grouped_scaled_act_fwd(&id, fmt, groups, width, x_bf16, nullptr, out_row, out_col,
-                                    group_amax, stream);
+                            float* col_sum, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  int rc = build_groups(groups, &gt, &rows);
+  if (rc) return rc;
+  if ((rc = check_width(width, "width"))) return rc;
+  if ((rc = check_extent(gt, width, "width"))) return rc;
+  if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
+  if (!qbuf_requested(out_row) && !qbuf_requested(out_col) && !col_sum)
+    return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row, out_col and col_sum are all empty)");
+  if ((rc = check_qbuf(out_row, fmt, "out_row"))) return rc;
+  if ((rc = check_qbuf(out_col, fmt, "out_col"))) return rc;
+  const bool quant = qbuf_requested(out_row) || qbuf_requested(out_col);
+  if (fmt == MGS_FMT_NVFP4 && quant && !group_amax)
+    return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
+  if (col_sum) {
+    const int64_t need = mgs::col_sum_part_bytes(gt, width);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(MGS_ERR_INVALID_ARG, "col_sum needs a workspace of %lld bytes (got %lld%s)", (long long)need,
+                  (long long)workspace_bytes, workspace ? "" : ", NULL");
+  }
+  mgs::ActHost ah{};
+  ah.kind = MGS_ACT_IDENTITY;
+  ah.s = ah.inv_s = ah.limit = ah.alpha = 1.0f;
+  ah.beta = 0.0f;
+  const mgs::QOut q = make_qout(out_row, out_col, width);
+  return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width, static_cast<const uint16_t*>(x_bf16),
+                                        nullptr, q, group_amax, col_sum, static_cast<float*>(workspace),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int64_t mgs_grouped_mx_quantize_workspace_bytes(const mgs_groups* groups, int64_t width) {
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  int rc = build_groups(groups, &gt, &rows);
+  if (rc) return rc;
+  if ((rc = check_width(width, "width"))) return rc;
+  ok();
+  return mgs::col_sum_part_bytes(gt, width);
 }
 
 int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int64_t m, int64_t n,

@@ -72,17 +72,23 @@ struct GemmArgs {
 
 // ---- launchers (return hipGetLastError() after the launches) ----
 
+// col_sum (nullable): per-group column sums of the output values [E x W_a]; cs_part: workspace of
+// col_sum_part_bytes(gt, W_a) bytes for the per-block partial sums (used when col_sum is requested).
 hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
                           const uint16_t* x, const float* probs, QOut out, float* group_amax,
-                          hipStream_t stream);
+                          float* col_sum, float* cs_part, hipStream_t stream);
 
-// dp_part: workspace of act_bwd_workspace_bytes(total rows, activation width) bytes (used when
-// dprobs is requested): per-row partial sums per 128-column tile, added in tile order afterwards.
+// workspace: act_bwd_workspace_bytes(gt, activation width, width_in) bytes, used when dprobs or
+// dx_col_sum is requested: per-row partial sums of dprobs per 128-column tile at offset 0, then (at
+// act_bwd_cs_offset) per-block column partial sums of the dense dx; both are added in a fixed order
+// by a second kernel.
 hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
                           const uint16_t* x, const uint16_t* dy, const float* probs, uint16_t* dx,
-                          QOut dxq, float* dx_amax, float* dprobs, float* dp_part, QOut actq,
-                          hipStream_t stream);
-int64_t act_bwd_workspace_bytes(int64_t rows, int64_t wa);
+                          QOut dxq, float* dx_amax, float* dprobs, float* dx_col_sum, void* workspace,
+                          QOut actq, hipStream_t stream);
+int64_t act_bwd_cs_offset(int64_t rows, int64_t wa);
+int64_t col_sum_part_bytes(const GroupTable& gt, int64_t width);
+int64_t act_bwd_workspace_bytes(const GroupTable& gt, int64_t wa, int64_t width_in);
 
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,
                           hipStream_t stream);

@@ -78,7 +78,8 @@ class ExpertMLP:
 
     # ------------------------------------------------------------------ backward
     def _workspace(self, nbytes):
-        """dprobs partial sums of the activation backward; kept between steps, grown on demand."""
+        """Partial sums of the backward launches (dprobs, bias gradients): one buffer shared by the
+        calls of a step, which run in order on one stream; kept between steps, grown on demand."""
         ws = getattr(self, "_ws", None)
         if ws is None or ws.numel() < nbytes:
             ws = self._ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
@@ -88,11 +89,17 @@ class ExpertMLP:
         c = self.ctx
         splits, m, fmt = c["splits"], c["m"], self.fmt
         e, h, f, f_in = self.e, self.h, self.f, self.f_in
-        dy2_row, dy2_col = self._quant(dy2, splits, h)
+        # dY2 quantized for FC2's dgrad and wgrad; FC2's bias gradient (its column sums) in the same pass
+        dy2_row = N.QTensor(fmt, False, splits, h)
+        dy2_col = N.QTensor(fmt, True, splits, h)
+        db2 = torch.empty((e, h), dtype=torch.float32, device="cuda") if self.b2 is not None else None
+        N.grouped_mx_quantize(fmt, splits, h, dy2, dy2_row, dy2_col, self._amax_buf(e), col_sum=db2,
+                              workspace=self._workspace(N.quantize_workspace_bytes(splits, h)))
         da = torch.empty((m, f), dtype=torch.bfloat16, device="cuda")
         N.grouped_gemm_mx("dgrad", fmt, splits, m, f, h, dy2_row, c["w2_col"], da)
         del dy2_row
-        dy1_dense = torch.empty((m, f_in), dtype=torch.bfloat16, device="cuda") if self.b1 is not None else None
+        # FC1's bias gradient: column sums of the dense BF16 dY1, taken inside the activation backward
+        db1 = torch.empty((e, f_in), dtype=torch.float32, device="cuda") if self.b1 is not None else None
         dy1_row = N.QTensor(fmt, False, splits, f_in)
         dy1_col = N.QTensor(fmt, True, splits, f_in)
         dprobs = torch.empty(m, dtype=torch.float32, device="cuda")
@@ -100,9 +107,9 @@ class ExpertMLP:
         if self.recompute:
             a_col = N.QTensor(fmt, True, splits, f)
             self.trace["bwd_act_col"] += 1
-        N.grouped_scaled_act_bwd(self.act, fmt, splits, f_in, c["y1"], da, c["probs"], dx=dy1_dense,
+        N.grouped_scaled_act_bwd(self.act, fmt, splits, f_in, c["y1"], da, c["probs"],
                                  dx_row=dy1_row, dx_col=dy1_col, dx_group_amax=self._amax_buf(e),
-                                 dprobs=dprobs, act_col=a_col if self.recompute else None,
+                                 dprobs=dprobs, dx_col_sum=db1, act_col=a_col if self.recompute else None,
                                  saved_group_amax=c["a_amax"],
                                  workspace=self._workspace(N.act_bwd_workspace_bytes(self.act, splits, f_in)))
         del da
@@ -110,8 +117,8 @@ class ExpertMLP:
         N.grouped_gemm_mx("dgrad", fmt, splits, m, h, f_in, dy1_row, c["w1_col"], dx1)
         del dy1_row
         # what the weight gradients consume stays alive until backward_dw (possibly delayed)
-        self.pending_wgrad = dict(splits=splits, m=m, dy2=dy2, dy2_col=dy2_col, a_col=a_col,
-                                  dy1_col=dy1_col, x1_col=c["x1_col"], dy1_dense=dy1_dense)
+        self.pending_wgrad = dict(splits=splits, m=m, dy2_col=dy2_col, a_col=a_col,
+                                  dy1_col=dy1_col, x1_col=c["x1_col"], db1=db1, db2=db2)
         self.ctx = None
         grads = {"dx1": dx1, "dprobs": dprobs}
         if not self.delay_wgrad:
@@ -131,14 +138,11 @@ class ExpertMLP:
         N.grouped_gemm_mx("wgrad", fmt, splits, h, f, m, p["dy2_col"], p["a_col"], dw2, accumulate=accumulate)
         N.grouped_gemm_mx("wgrad", fmt, splits, f_in, h, m, p["dy1_col"], p["x1_col"], dw1, accumulate=accumulate)
         out = {"dw1": dw1, "dw2": dw2}
-        if self.b2 is not None:
-            db2 = torch.empty((e, h), dtype=torch.float32, device="cuda")
-            N.grouped_col_sum(splits, h, p["dy2"], db2)
-            out["db2"] = db2
-        if self.b1 is not None:
-            db1 = torch.empty((e, f_in), dtype=torch.float32, device="cuda")
-            N.grouped_col_sum(splits, f_in, p["dy1_dense"], db1)
-            out["db1"] = db1
+        # the bias gradients were taken in the backward's quantize / activation passes
+        if p["db2"] is not None:
+            out["db2"] = p["db2"]
+        if p["db1"] is not None:
+            out["db1"] = p["db1"]
         self.pending_wgrad = None
         return out
 

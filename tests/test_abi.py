@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_symbols():
         assert hasattr(lib, name), name
     assert set(_native.EXPORTED) == set(_declared_symbols())
-    assert _native.abi_version() == 2
+    assert _native.abi_version() == 3
 
 
 def test_qtensor_nbytes_layouts():
@@ -94,15 +94,44 @@ def test_argument_validation_act_bwd_and_recompute():
     small = torch.empty(4 * 32 - 1, dtype=torch.uint8)  # host memory: validation fails before any use
     _expect(-1, b, act, "mxfp8", [32], 256, FAKE, FAKE, FAKE, dprobs=FAKE, workspace=small, stream=0,
             match="workspace")
+    need = N.act_bwd_workspace_bytes(act, [32], 256)
+    short = torch.empty(need - 1, dtype=torch.uint8)
+    _expect(-1, b, act, "mxfp8", [32], 256, FAKE, FAKE, FAKE, dx_col_sum=FAKE, workspace=short, stream=0,
+            match="dx_col_sum needs a workspace")
+
+
+def test_argument_validation_quantize_col_sum():
+    from moe_grouped_scaled_amd import _native as N
+    import torch
+    q = _FakeQ().q
+    f = N.grouped_mx_quantize
+    _expect(-1, f, "mxfp8", [32], 64, FAKE, stream=0, match="no output")
+    need = N.quantize_workspace_bytes([32, 200], 64)
+    short = torch.empty(need - 1, dtype=torch.uint8)
+    _expect(-1, f, "mxfp8", [32, 200], 64, FAKE, out_row=q, col_sum=FAKE, workspace=short, stream=0,
+            match="col_sum needs a workspace")
+    # NVFP4 needs the group amax only when something is quantized
+    _expect(-1, f, "nvfp4", [32], 64, FAKE, out_row=q, stream=0, match="group_amax")
+    _expect(-2, f, "mxfp8", [32], 48, FAKE, out_row=q, stream=0, match="multiple of 32")
+
+
+def _padded_rows(splits):
+    return sum(-(-m // 128) * 128 for m in splits)
 
 
 def test_workspace_bytes():
+    """Closed forms: dprobs partials (one FP32 per row and 128-column tile, rounded up to 256 bytes)
+    followed by one FP32 column partial per 128-token block of the columnwise-padded rows."""
     from moe_grouped_scaled_amd import _native as N
     for kind, w_in, wa in (("srelu", 4096, 4096), ("swiglu", 4096, 2048), ("identity", 96, 96)):
-        for splits in ([64, 128, 32, 32], [0, 1, 31, 33, 64], [2048] * 16):
+        for splits in ([64, 128, 32, 32], [0, 1, 31, 33, 64], [2048] * 16, [0, 0]):
             m = sum(splits)
-            assert N.act_bwd_workspace_bytes(N.act_params(kind), splits, w_in) == 4 * m * -(-wa // 128)
+            dp = -(-(4 * m * -(-wa // 128)) // 256) * 256
+            cs = 4 * (_padded_rows(splits) // 128) * w_in
+            assert N.act_bwd_workspace_bytes(N.act_params(kind), splits, w_in) == dp + cs
+            assert N.quantize_workspace_bytes(splits, wa) == 4 * (_padded_rows(splits) // 128) * wa
     _expect(-2, N.act_bwd_workspace_bytes, N.act_params("swiglu"), [32], 96)
+    _expect(-2, N.quantize_workspace_bytes, [32], 40)
 
 
 def test_size_limits():

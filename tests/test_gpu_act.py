@@ -196,7 +196,7 @@ def test_act_fwd_edge_values(N):
 # ------------------------------------------------------------------------------------------ bwd
 
 def gpu_bwd(N, kind, fmt, splits, width_in, x_bits, dy_bits, p, dense=True, row=True, col=True,
-            dprobs=True, recompute=True, saved_amax=None, **kw):
+            dprobs=True, recompute=True, saved_amax=None, col_sum=False, **kw):
     import torch
     wa = A.out_width(kind, width_in)
     m = int(np.sum(splits))
@@ -207,12 +207,15 @@ def gpu_bwd(N, kind, fmt, splits, width_in, x_bits, dy_bits, p, dense=True, row=
     dxa = torch.empty(len(splits), dtype=torch.float32, device="cuda") if fmt == "nvfp4" else None
     dp = torch.empty(m, dtype=torch.float32, device="cuda") if dprobs else None
     sa = to_dev(saved_amax.astype(np.float32)) if saved_amax is not None else None
+    cs = torch.empty((len(splits), width_in), dtype=torch.float32, device="cuda") if col_sum else None
     N.grouped_scaled_act_bwd(N.act_params(kind, **_params(kind, **kw)), fmt, splits, width_in,
                              to_dev_bf16(x_bits), to_dev_bf16(dy_bits), None if p is None else to_dev(p),
-                             dx=dx, dx_row=qr, dx_col=qc, dx_group_amax=dxa, dprobs=dp, act_col=qa,
-                             saved_group_amax=sa)
+                             dx=dx, dx_row=qr, dx_col=qc, dx_group_amax=dxa, dprobs=dp, dx_col_sum=cs,
+                             act_col=qa, saved_group_amax=sa)
     torch.cuda.synchronize()
     out = {}
+    if col_sum:
+        out["cs"] = f32(cs)
     if dense:
         out["dx"] = bf16_host(dx)
     if row:
@@ -255,7 +258,7 @@ def test_act_bwd_parity(N, kind, fmt, splits, width_in, std):
     dy = bf16_f64(d["dy"])
     y = A.scaled_act_fwd(kind, x, p, **params)
     saved = Q.quantize_grouped(y, splits, fmt, rowwise=False)["group_amax"] if fmt == "nvfp4" else None
-    got = gpu_bwd(N, kind, fmt, splits, width_in, d["x"], d["dy"], d["p"], saved_amax=saved)
+    got = gpu_bwd(N, kind, fmt, splits, width_in, d["x"], d["dy"], d["p"], saved_amax=saved, col_sum=True)
     dx32, dp = A.scaled_act_bwd(kind, x, dy, p, **params)
     exact = kind in EXACT_KINDS
     # dense BF16 dL/dx
@@ -268,6 +271,16 @@ def test_act_bwd_parity(N, kind, fmt, splits, width_in, std):
         assert diff.mean() <= 1e-3
         gv, rv = bf16_f64(got["dx"][diff]), bf16_f64(ref_dx[diff])
         assert np.all(np.abs(gv - rv) <= np.abs(rv) * 2.0 ** -7 * 1.0001 + 1e-30)
+    # per-group column sums of the dense BF16 dL/dx (bias gradient): any FP32 summation order of the
+    # oracle's BF16 values lies within (m_g + 1) * 2^-24 * sum |v|; where the dense values may differ
+    # by one BF16 step (non-exact kinds), at most 2^-7 * sum |v| more
+    ref_v = bf16_f64(ref_dx)
+    off = Q.group_offsets(splits)
+    for g in range(len(splits)):
+        blk = ref_v[off[g]:off[g + 1]]
+        mag = np.abs(blk).sum(axis=0)
+        bound = (splits[g] + 1) * 2.0 ** -24 * mag + (0 if exact else 2.0 ** -7 * mag) + 1e-30
+        assert np.all(np.abs(got["cs"][g] - blk.sum(axis=0)) <= bound), g
     # quantized dL/dx (row + col) against the oracle quantizer on the oracle's FP32 dx
     ref_q = Q.quantize_grouped(dx32, splits, fmt)
     check_fwd(fmt, kind, got, ref_q, splits, width_in, exact)
@@ -315,6 +328,63 @@ def test_bwd_outputs_independent_of_requests(N):
     only_q = gpu_bwd(N, "swiglu", "mxfp8", splits, 1024, d["x"], d["dy"], d["p"], dense=False,
                      dprobs=False, recompute=False)
     assert np.array_equal(only_q["row_data"], full["row_data"]) and np.array_equal(only_q["col_data"], full["col_data"])
+    # the fused column sums change nothing else, and need neither the dense output nor dprobs
+    with_cs = gpu_bwd(N, "swiglu", "mxfp8", splits, 1024, d["x"], d["dy"], d["p"], col_sum=True)
+    for k in ("dp", "dx", "row_data", "col_data", "act_col_data"):
+        assert np.array_equal(with_cs[k], full[k]), k
+    only_cs = gpu_bwd(N, "swiglu", "mxfp8", splits, 1024, d["x"], d["dy"], d["p"], dense=False, row=False,
+                      col=False, dprobs=False, recompute=False, col_sum=True)
+    assert np.array_equal(only_cs["cs"], with_cs["cs"])
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_quantize_col_sum(N, fmt):
+    """Column sums taken in the quantize pass (the FC2 bias gradient of dL/dY2): within the FP32
+    summation bound of the oracle's sums; the quantized outputs are the same bytes as without them;
+    a call that asks only for the sums runs without a group amax."""
+    import torch
+    rng = np.random.default_rng(17)
+    splits, w = [5, 0, 300, 64, 129], 1056
+    x = workloads.normal_bf16(rng, (sum(splits), w))
+    xd = to_dev_bf16(x)
+    e = len(splits)
+
+    def run(col_sum, quant=True):
+        qr = N.QTensor(fmt, False, splits, w) if quant else None
+        qc = N.QTensor(fmt, True, splits, w) if quant else None
+        amax = torch.empty(e, dtype=torch.float32, device="cuda") if fmt == "nvfp4" and quant else None
+        cs = torch.full((e, w), 7.0, dtype=torch.float32, device="cuda") if col_sum else None
+        N.grouped_mx_quantize(fmt, splits, w, xd, qr, qc, amax, col_sum=cs)
+        torch.cuda.synchronize()
+        out = {"cs": f32(cs)} if col_sum else {}
+        if quant:
+            out.update(rd=u8(qr.data), rs=u8(qr.scales), cd=u8(qc.data), cs_=u8(qc.scales))
+        return out
+
+    a, b, c = run(True), run(False), run(True, quant=False)
+    for k in ("rd", "rs", "cd", "cs_"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["cs"], c["cs"])
+    xv = bf16_f64(x)
+    off = Q.group_offsets(splits)
+    for g in range(e):
+        blk = xv[off[g]:off[g + 1]]
+        bound = (splits[g] + 1) * 2.0 ** -24 * np.abs(blk).sum(axis=0) + 1e-30
+        assert np.all(np.abs(a["cs"][g] - blk.sum(axis=0)) <= bound), g
+    assert np.all(a["cs"][1] == 0.0)
+
+
+def test_col_sums_of_all_empty_groups_are_zero(N):
+    import torch
+    splits, w = [0, 0, 0], 64
+    cs = torch.full((3, w), 7.0, dtype=torch.float32, device="cuda")
+    N.grouped_mx_quantize("mxfp8", splits, w, torch.empty((0, w), dtype=torch.bfloat16, device="cuda"),
+                          col_sum=cs)
+    cs2 = torch.full((3, w), 7.0, dtype=torch.float32, device="cuda")
+    empty = torch.empty((0, w), dtype=torch.bfloat16, device="cuda")
+    N.grouped_scaled_act_bwd(N.act_params("srelu"), "mxfp8", splits, w, empty, empty, None, dx_col_sum=cs2)
+    torch.cuda.synchronize()
+    assert np.all(f32(cs) == 0.0) and np.all(f32(cs2) == 0.0)
 
 
 def test_col_sum(N):
