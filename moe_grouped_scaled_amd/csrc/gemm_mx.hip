@@ -33,6 +33,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int LDS_STRIDE16 = BK + 8;     // halfs per LDS row, FP16 tiles
@@ -571,7 +572,6 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable 
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int q = lane >> 4, r16 = lane & 15;
   const int nsteps = (int)((j.k + BK - 1) / BK);
 
   // staging: a K step is 64 packed bytes per row; thread handles rows (tid / 8) + 32 i and the
@@ -607,11 +607,18 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable 
     }
   };
 
-  v4f acc[4][4];
+  // Each wave computes 64 x 64 outputs as 2 x 2 fragments of 32 x 32 with V_MFMA_F32_32X32X16_F16
+  // (on this GPU the 16 x 16 x 32 FP16 form runs at half the rate).  Measured lane layout: lane l
+  // holds row l % 32 of each operand with K elements 8 (l / 32) .. + 7, and accumulator register r
+  // holds D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], D's rows indexed by the first operand.  B (the
+  // weight rows = output columns) is the first operand, so register group g of a lane holds the four
+  // consecutive output columns 8 g + 4 (l / 32) .. + 3 of output row l % 32.
+  const int r32 = lane & 31, h32 = lane >> 5;
+  v16f acc[2][2];
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = v16f{};
 
   gload(0);
   lstore();
@@ -619,18 +626,18 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable 
   for (int step = 0; step < nsteps; ++step) {
     if (step + 1 < nsteps) gload(step + 1);
 #pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      v8h af[4], bfr[4];
+    for (int s = 0; s < BK / 16; ++s) {
+      v8h af[2], bfr[2];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        af[f] = *reinterpret_cast<const v8h*>(lds_a + (wm * 64 + f * 16 + r16) * LDS_STRIDE16 + s * 32 + q * 8);
-        bfr[f] = *reinterpret_cast<const v8h*>(lds_b + (wn * 64 + f * 16 + r16) * LDS_STRIDE16 + s * 32 + q * 8);
+      for (int f = 0; f < 2; ++f) {
+        af[f] = *reinterpret_cast<const v8h*>(lds_a + (wm * 64 + f * 32 + r32) * LDS_STRIDE16 + s * 16 + h32 * 8);
+        bfr[f] = *reinterpret_cast<const v8h*>(lds_b + (wn * 64 + f * 32 + r32) * LDS_STRIDE16 + s * 16 + h32 * 8);
       }
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
+      for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
     }
     __syncthreads();
     if (step + 1 < nsteps) {
@@ -639,10 +646,13 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable 
     }
   }
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
-      store_frag(j, ga, wm * 64 + fm * 16 + r16, wn * 64 + fn * 16 + 4 * q, acc[fm][fn]);
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store_frag(j, ga, wm * 64 + fm * 32 + r32, wn * 64 + fn * 32 + 8 * g + 4 * h32,
+                   v4f{acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]});
 }
 
 }  // namespace
