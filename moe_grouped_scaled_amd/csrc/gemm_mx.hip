@@ -14,14 +14,15 @@
 // q = l / 16; the scale VGPR of lane l applies to K block q (K[32q, 32q + 32)) of row l % 16.
 //
 // NVFP4 operands (E2M1 with an E4M3 scale per 16) cannot use the E8M0-scaled MFMA: the product of
-// an E2M1 value and an E4M3 scale needs up to 6 significant bits.  They are dequantized exactly to
-// FP16 while staging into LDS (e2m1 * s_b is exact in FP16) and multiplied with the FP16 MFMA; the
-// two per-group FP32 factors are applied in the epilogue.
+// an E2M1 value and an E4M3 scale needs up to 6 significant bits.  The packed codes and scales are
+// staged in LDS as they are; each wave dequantizes its fragments exactly to FP16 in registers
+// (e2m1 * s_b is exact in FP16) and multiplies them with V_MFMA_F32_32X32X16_F16; the two per-group
+// FP32 factors are applied in the epilogue.
 //
-// Tile: 128 x 128 per workgroup (4 waves in 2 x 2, each 64 x 64 = 4 x 4 MFMA fragments), K step 128.
-// Global -> registers (prefetch of the next K step) -> LDS (rows padded to spread the banks) ->
-// fragments.  The MFMA is issued with B as its first operand so each lane's accumulator holds 4
-// consecutive output columns of one row (one 16-byte FP32 / 8-byte BF16 store per fragment).
+// Both formats use 256 x 256 tiles per workgroup (4 waves in 2 x 2, each 128 x 128 with 256 FP32
+// accumulators per lane in AGPRs), K steps of 128 and double-buffered direct-to-LDS loads.  The MFMA
+// is issued with B as its first operand so each lane's accumulator holds runs of 4 consecutive output
+// columns of one row (one 16-byte FP32 / 8-byte BF16 store each).
 #include <type_traits>
 
 #include "mgs_device.h"
@@ -31,12 +32,10 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int LDS_STRIDE16 = BK + 8;     // halfs per LDS row, FP16 tiles
+constexpr int BK = 128;                  // K elements per step
 
 // One operand of a tile: `rows` valid rows starting at `data` (row stride `ld` bytes).  Scales:
 // MXFP8 keeps them grouped per 128-wide K step -- the byte of (row r, 32-block kb) of the scale
@@ -201,21 +200,6 @@ __device__ __forceinline__ void store_values(const TileJob& j, int row, int col,
     w.y = bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + gc) = w;
   }
-}
-
-// Epilogue for one 16 x 16 fragment (used by the NVFP4 kernel): bias and accumulation read directly.
-__device__ __forceinline__ void store_frag(const TileJob& j, const GemmArgs& ga, int row, int col,
-                                           v4f acc) {
-  if (row >= j.a.rows || col >= j.b.rows) return;
-  uint2 bw = make_uint2(0, 0);
-  if (j.bias) bw = *reinterpret_cast<const uint2*>(j.bias + j.ccol0 + col);
-  float v[4];
-  frag_values(j, acc, bw, v);
-  if (j.c32 && ga.accumulate) {
-    const float4 o = *reinterpret_cast<const float4*>(j.c32 + (j.crow0 + row) * j.ldc + j.ccol0 + col);
-    v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
-  }
-  store_values(j, row, col, v);
 }
 
 template <int TM, int TN>
@@ -562,97 +546,260 @@ __device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, v2h scale) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void gemm_nvfp4_kernel(GemmArgs ga, GemmTable tt) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds_a[BM * LDS_STRIDE16];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_b[BN * LDS_STRIDE16];
-  const TileJob j = make_job<BM, BN>(ga, tt, blockIdx.x);
+// ------------------------------------------------------------------------------------ NVFP4, large tile
+//
+// 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (4 x 4 fragments of 32 x 32, 256 FP32
+// accumulators per lane in AGPRs), K step 128 elements.  The packed E2M1 codes (64 bytes per row and
+// step) and the E4M3 block scales (8 bytes per row and step) go from global memory straight into LDS
+// with direct-to-LDS loads, double-buffered (36 KiB per stage); each wave dequantizes its own
+// fragments to FP16 in registers (exact, as in the staging path above) and feeds
+// V_MFMA_F32_32X32X16_F16.  Fragment reads are 4x smaller than FP16 tiles in LDS would need.
+//
+// K order inside a step: the MFMA's K slots are a permutation of the step's 128 K indices, the same
+// for both operands, so the dot products are unchanged.  Lane half h = l / 32 takes the contiguous
+// K range [64 h, 64 h + 64) of the step, 8 elements per 16-wide MFMA (substep s: 64 h + 8 s .. + 7).
+// A lane's codes for a whole step are then 32 contiguous bytes of its row (two 16-byte LDS reads)
+// and its four block scales one dword.  Data rows are 64 bytes in LDS with the 16-byte chunk c of
+// row r stored at slot c ^ ((r >> 1) & 3), so the 32 rows a fragment read touches fall on distinct
+// banks; the direct-to-LDS loads realise the swizzle by loading the permuted chunk per lane.
+// Scales: a row's 8 bytes of a step start at byte row * (K / 16) + 8 st, which is only 2-byte
+// aligned when K % 64 != 0; each row therefore stages the 16 aligned bytes around them (one
+// dwordx4 load per lane) and the reader extracts its dword at the row's byte misalignment (0 or 2).
+constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int NV_ROWB = BK / 2;                   // code bytes per row and step
+constexpr int NV_DATA = BM2 * NV_ROWB;             // per operand and stage
+constexpr int NV_SCB = BK / 16;                    // scale bytes per row and step
+constexpr int NV_SCROW = 16;                       // staged scale bytes per row
+constexpr int NV_SC = BM2 * NV_SCROW;
+constexpr int NV_STAGE = 2 * (NV_DATA + NV_SC);    // A data, B data, A scales, B scales
+
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mfma_f16_32(v16f& acc, const uint4& b, const uint4& a) {
+  const v4i32 vb = v4i32{(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  const v4i32 va = v4i32{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(vb), "v"(va));
+}
+
+// E4M3 block scales (four bytes of a dword) as exact FP16 pairs: the code's bits shifted into an
+// FP16 are its value times 2^-8 (the exponent bias differs by 8; E4M3 subnormals land on FP16
+// subnormals consistently), so one multiplication by 256 makes them exact normal FP16 numbers.
+__device__ __forceinline__ void nv_scales_f16(uint32_t w, v2h& s01, v2h& s23) {
+  const uint32_t lo = ((w & 0x7fu) << 7) | ((w & 0x7f00u) << 15);
+  const uint32_t hi = ((w >> 9) & 0x3f80u) | ((w >> 1) & 0x3f800000u);
+  const v2h k256 = v2h{(_Float16)256.0f, (_Float16)256.0f};
+  s01 = __builtin_bit_cast(v2h, lo) * k256;
+  s23 = __builtin_bit_cast(v2h, hi) * k256;
+}
+
+__device__ __forceinline__ v2h scale_pair(const v2h& s01, const v2h& s23, int blk) {
+  const _Float16 v = blk == 0 ? s01[0] : blk == 1 ? s01[1] : blk == 2 ? s23[0] : s23[1];
+  return v2h{v, v};
+}
+
+// Epilogue of the NVFP4 256 x 256 tile: lane (r32, h32) of wave (wm, wn) holds, for fragment
+// (fm, fn) and register group g, output row 128 wm + 32 fm + r32 and the four columns
+// 128 wn + 32 fn + 8 g + 4 h32 .. + 3.
+__device__ __forceinline__ void epilogue_nv256(const TileJob& j, const GemmArgs& ga, v16f (&acc)[4][4],
+                                               const uint2* bias_lds, int wm, int wn, int r32, int h32) {
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) {
+    const int row = wm * 128 + fm * 32 + r32;
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * 128 + fn * 32 + 8 * g + 4 * h32;
+        const uint2 bw = j.bias ? bias_lds[col >> 2] : make_uint2(0, 0);
+        float v[4];
+        frag_values(j, v4f{acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]},
+                    bw, v);
+        if (j.c32 && ga.accumulate && row < j.a.rows && col < j.b.rows) {
+          const float4 o = *reinterpret_cast<const float4*>(j.c32 + (j.crow0 + row) * j.ldc + j.ccol0 + col);
+          v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+        }
+        store_values(j, row, col, v);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_STAGE];
+  __shared__ __attribute__((aligned(16))) uint2 bias_lds[BN2 / 4];
+  const int tile = xcd_remap_gemm(blockIdx.x, gridDim.x);
+  const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
   if (j.k == 0) {
-    write_zero_tile<BM, BN>(j, ga);
+    write_zero_tile<BM2, BN2>(j, ga);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int nsteps = (int)((j.k + BK - 1) / BK);
-
-  // staging: a K step is 64 packed bytes per row; thread handles rows (tid / 8) + 32 i and the
-  // 8-byte chunk tid % 8 (16 elements = one scale block)
-  const int srow = tid >> 3, schunk = tid & 7;
-  uint2 ra[4], rb[4];
-  uint32_t sa[4], sb[4];
-  auto gload = [&](int step) {
-    const int64_t e0 = (int64_t)step * BK + schunk * 16;  // first element of the chunk
-    const bool kok = e0 < j.k;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = srow + 32 * i;
-      const bool av = kok && row < j.a.rows, bv = kok && row < j.b.rows;
-      ra[i] = av ? *reinterpret_cast<const uint2*>(j.a.data + row * j.a.ld + e0 / 2) : make_uint2(0, 0);
-      rb[i] = bv ? *reinterpret_cast<const uint2*>(j.b.data + row * j.b.ld + e0 / 2) : make_uint2(0, 0);
-      sa[i] = av ? j.a.sbase[(j.a.srow0 + row) * j.a.sld + e0 / 16] : 0u;
-      sb[i] = bv ? j.b.sbase[(j.b.srow0 + row) * j.b.sld + e0 / 16] : 0u;
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = srow + 32 * i;
-      const _Float16 ha = (_Float16)e4m3_value(sa[i] & 0x7f), hb = (_Float16)e4m3_value(sb[i] & 0x7f);
-      const v2h fa = v2h{ha, ha}, fb = v2h{hb, hb};
-      const uint4 a0 = fp4x8_to_f16(ra[i].x, fa), a1 = fp4x8_to_f16(ra[i].y, fa);
-      const uint4 b0 = fp4x8_to_f16(rb[i].x, fb), b1 = fp4x8_to_f16(rb[i].y, fb);
-      uint4* pa = reinterpret_cast<uint4*>(lds_a + row * LDS_STRIDE16 + schunk * 16);
-      uint4* pb = reinterpret_cast<uint4*>(lds_b + row * LDS_STRIDE16 + schunk * 16);
-      pa[0] = a0; pa[1] = a1;
-      pb[0] = b0; pb[1] = b1;
-    }
-  };
-
-  // Each wave computes 64 x 64 outputs as 2 x 2 fragments of 32 x 32 with V_MFMA_F32_32X32X16_F16
-  // (on this GPU the 16 x 16 x 32 FP16 form runs at half the rate).  Measured lane layout: lane l
-  // holds row l % 32 of each operand with K elements 8 (l / 32) .. + 7, and accumulator register r
-  // holds D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32], D's rows indexed by the first operand.  B (the
-  // weight rows = output columns) is the first operand, so register group g of a lane holds the four
-  // consecutive output columns 8 g + 4 (l / 32) .. + 3 of output row l % 32.
   const int r32 = lane & 31, h32 = lane >> 5;
-  v16f acc[2][2];
-#pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = v16f{};
 
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    if (step + 1 < nsteps) gload(step + 1);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      v8h af[2], bfr[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        af[f] = *reinterpret_cast<const v8h*>(lds_a + (wm * 64 + f * 32 + r32) * LDS_STRIDE16 + s * 16 + h32 * 8);
-        bfr[f] = *reinterpret_cast<const v8h*>(lds_b + (wn * 64 + f * 32 + r32) * LDS_STRIDE16 + s * 16 + h32 * 8);
-      }
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
+  // load descriptors: data based at the tile's first row (record count to the end of the tensor),
+  // scales at the tile's first scale row
+  const sdesc_t ad = gemm_view(j.a.data, j.a.avail), bd = gemm_view(j.b.data, j.b.avail);
+  // scale arrays viewed from their 4-aligned base; `sa0` / `sb0` is the array start's offset from it
+  const int64_t sa0 = (int64_t)(reinterpret_cast<uintptr_t>(j.a.sbase) & 3u);
+  const int64_t sb0 = (int64_t)(reinterpret_cast<uintptr_t>(j.b.sbase) & 3u);
+  const sdesc_t as = gemm_view(j.a.sbase - sa0, j.a.savail + sa0), bs = gemm_view(j.b.sbase - sb0, j.b.savail + sb0);
+  const sdesc_t biasd = gemm_view(reinterpret_cast<const uint8_t*>(j.bias + j.ccol0), 2 * (int64_t)j.b.rows);
+  // data instruction n (0..3) of wave w: rows 64 w + 16 n + lane / 4, LDS slot lane % 4 holding chunk
+  // (lane % 4) ^ ((row >> 1) & 3) = (lane % 4) ^ ((lane >> 3) & 3)
+  const uint32_t dchunk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+  const uint32_t voa = (uint32_t)((wave * 64 + (lane >> 2)) * j.a.ld) + dchunk;
+  const uint32_t vob = (uint32_t)((wave * 64 + (lane >> 2)) * j.b.ld) + dchunk;
+  const uint32_t a16 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * j.a.ld));
+  const uint32_t b16 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * j.b.ld));
+  // scale load of wave w: lane l stages the 16 aligned bytes around the step's 8 scale bytes of row
+  // 64 w + l (the step offset 8 st keeps the alignment)
+  const uint32_t vsa = (uint32_t)((sa0 + (j.a.srow0 + wave * 64 + lane) * j.a.sld) & ~(int64_t)3);
+  const uint32_t vsb = (uint32_t)((sb0 + (j.b.srow0 + wave * 64 + lane) * j.b.sld) & ~(int64_t)3);
+
+  // load instruction n (0..9) of step st into stage `stg`: 0..3 A data, 4..7 B data, 8 A scales,
+  // 9 B scales
+  constexpr int NLOADS = 10;
+  auto issue_one = [&](int st, uint8_t* stg, int n) {
+    const uint32_t base = lds_addr(stg);
+    if (n < 4) {
+      dma16(ad, voa, n * a16 + (uint32_t)st * NV_ROWB, base + (wave * 64 + 16 * n) * NV_ROWB);
+    } else if (n < 8) {
+      dma16(bd, vob, (n - 4) * b16 + (uint32_t)st * NV_ROWB, base + NV_DATA + (wave * 64 + 16 * (n - 4)) * NV_ROWB);
+    } else if (n == 8) {
+      dma16(as, vsa, (uint32_t)st * NV_SCB, base + 2 * NV_DATA + wave * 64 * NV_SCROW);
+    } else {
+      dma16(bs, vsb, (uint32_t)st * NV_SCB, base + 2 * NV_DATA + NV_SC + wave * 64 * NV_SCROW);
     }
-    __syncthreads();
-    if (step + 1 < nsteps) {
-      lstore();
-      __syncthreads();
-    }
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = v16f{};
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_valu_gap();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the lane's fragment rows: A 128 wm + 32 f + r32, B 128 wn + 32 f + r32 (f = 0..3)
+  const int sw = (r32 >> 1) & 3;
+  const uint32_t c0 = (uint32_t)(((2 * h32) ^ sw) << 4), c1 = (uint32_t)(((2 * h32 + 1) ^ sw) << 4);
+  // byte misalignment (0 or 2) of the scale bytes of the lane's fragment rows
+  uint32_t misa[4], misb[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    misa[f] = (uint32_t)(sa0 + (j.a.srow0 + wm * 128 + f * 32 + r32) * j.a.sld) & 3u;
+    misb[f] = (uint32_t)(sb0 + (j.b.srow0 + wn * 128 + f * 32 + r32) * j.b.sld) & 3u;
   }
+  // the lane's scale dword (bytes 4 h .. 4 h + 3 of the row's step) from its staged 16 bytes
+  auto scale_word = [&](const uint8_t* row16, uint32_t mis) {
+    const uint4 d = *reinterpret_cast<const uint4*>(row16);
+    const uint32_t lo = h32 ? d.y : d.x, hi = h32 ? d.z : d.y;
+    return __builtin_amdgcn_alignbyte(hi, lo, mis);
+  };
+  // In a partial last step (K % 128 != 0) the scale array can end inside a dword, which a dword load
+  // returns as zero; there the lane reads its bytes directly, two 2-byte loads each fully in or out
+  // of the array (the bytes past it belong to K indices the step masks anyway).
+  const __amdgpu_buffer_rsrc_t sra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(j.a.sbase), 0, (int)std::min<int64_t>(j.a.savail, 0x7fffffff), RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t srb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(j.b.sbase), 0, (int)std::min<int64_t>(j.b.savail, 0x7fffffff), RSRC_WORD3);
+  auto scale_word_direct = [&](const __amdgpu_buffer_rsrc_t& r, int64_t srow, int64_t sld, int st) {
+    const uint32_t o = (uint32_t)(srow * sld) + (uint32_t)(st * NV_SCB + 4 * h32);
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, (int)o, 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(o + 2), 0, 0);
+    return lo | (hi << 16);
+  };
+  constexpr int PRE = 2, PACE = 16;
+  auto step = [&](const uint8_t* stg, bool tail, int64_t rem, int next_st, uint8_t* next_stg, int st) {
+    if (next_st >= 0)
+      for (int n = 0; n < PRE; ++n) issue_one(next_st, next_stg, n);
+    const uint8_t* pa = stg + (wm * 128 + r32) * NV_ROWB;
+    const uint8_t* pb = stg + NV_DATA + (wn * 128 + r32) * NV_ROWB;
+    const uint8_t* psa = stg + 2 * NV_DATA + (wm * 128 + r32) * NV_SCROW;
+    const uint8_t* psb = stg + 2 * NV_DATA + NV_SC + (wn * 128 + r32) * NV_SCROW;
+    // raw codes (8 dwords per fragment: dword s = substep s) and scales of the step
+    uint32_t ra[4][8], rb[4][8];
+    v2h sa01[4], sa23[4], sb01[4], sb23[4];
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
+    for (int f = 0; f < 4; ++f) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(pa + f * 32 * NV_ROWB + c0);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(pa + f * 32 * NV_ROWB + c1);
+      const uint4 y0 = *reinterpret_cast<const uint4*>(pb + f * 32 * NV_ROWB + c0);
+      const uint4 y1 = *reinterpret_cast<const uint4*>(pb + f * 32 * NV_ROWB + c1);
+      ra[f][0] = x0.x; ra[f][1] = x0.y; ra[f][2] = x0.z; ra[f][3] = x0.w;
+      ra[f][4] = x1.x; ra[f][5] = x1.y; ra[f][6] = x1.z; ra[f][7] = x1.w;
+      rb[f][0] = y0.x; rb[f][1] = y0.y; rb[f][2] = y0.z; rb[f][3] = y0.w;
+      rb[f][4] = y1.x; rb[f][5] = y1.y; rb[f][6] = y1.z; rb[f][7] = y1.w;
+      const uint32_t wa = tail ? scale_word_direct(sra, j.a.srow0 + wm * 128 + f * 32 + r32, j.a.sld, st)
+                               : scale_word(psa + f * 32 * NV_SCROW, misa[f]);
+      const uint32_t wb = tail ? scale_word_direct(srb, j.b.srow0 + wn * 128 + f * 32 + r32, j.b.sld, st)
+                               : scale_word(psb + f * 32 * NV_SCROW, misb[f]);
+      nv_scales_f16(wa, sa01[f], sa23[f]);
+      nv_scales_f16(wb, sb01[f], sb23[f]);
+    }
+    // operands of substep s, zeroed where the K index is past the end (partial last step)
+    auto dq = [&](const uint32_t (&r)[8], const v2h& s01, const v2h& s23, int sub) {
+      uint4 v = fp4x8_to_f16(r[sub], scale_pair(s01, s23, sub >> 1));
+      if (tail && !(64 * h32 + 8 * sub < rem)) v = make_uint4(0, 0, 0, 0);
+      return v;
+    };
+    uint4 fa[2][4], fb[2][4];
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
+    for (int f = 0; f < 4; ++f) {
+      fa[0][f] = dq(ra[f], sa01[f], sa23[f], 0);
+      fb[0][f] = dq(rb[f], sb01[f], sb23[f], 0);
+    }
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store_frag(j, ga, wm * 64 + fm * 32 + r32, wn * 64 + fn * 32 + 8 * g + 4 * h32,
-                   v4f{acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]});
+    for (int sub = 0; sub < BK / 16; ++sub) {
+      const int cur = sub & 1, nxt = cur ^ 1;
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_valu_gap();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+          mfma_f16_32(acc[fm][fn], fb[cur][fn], fa[cur][fm]);
+          const int m = sub * 16 + fm * 4 + fn;
+          // one fragment of the next substep is dequantized after every second MFMA
+          // (the empty asm pins the result here: the compiler would otherwise sink the
+          // dequantization to just before the next substep and serialize it with the MFMAs)
+          if (sub + 1 < BK / 16 && (m & 1)) {
+            const int f = (fm * 4 + fn) >> 1;  // 0..7
+            uint4& dst = f < 4 ? fa[nxt][f] : fb[nxt][f - 4];
+            dst = f < 4 ? dq(ra[f], sa01[f], sa23[f], sub + 1) : dq(rb[f - 4], sb01[f - 4], sb23[f - 4], sub + 1);
+            asm volatile("" : "+v"(dst.x), "+v"(dst.y), "+v"(dst.z), "+v"(dst.w));
+          }
+          if (next_st >= 0 && m % PACE == PACE - 1 && PRE + m / PACE < NLOADS)
+            issue_one(next_st, next_stg, PRE + m / PACE);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  for (int n = 0; n < NLOADS; ++n) issue_one(0, smem, n);
+  if (j.bias && wave < 2) dma4(biasd, (uint32_t)(wave * 256 + lane * 4), 0, lds_addr(bias_lds) + wave * 256);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int nsteps = __builtin_amdgcn_readfirstlane((int)((j.k + BK - 1) / BK));
+  const int64_t last_rem = j.k - (int64_t)(nsteps - 1) * BK;
+  const bool tail_step = last_rem < BK;
+  const int full_steps = tail_step ? nsteps - 1 : nsteps;
+  for (int st = 0; st < full_steps; ++st) {
+    const int nx = st + 1 < nsteps ? st + 1 : -1;
+    step(smem + (st & 1) * NV_STAGE, false, BK, nx, smem + ((st + 1) & 1) * NV_STAGE, st);
+  }
+  if (tail_step) step(smem + ((nsteps - 1) & 1) * NV_STAGE, true, last_rem, -1, nullptr, nsteps - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_drain();
+  __builtin_amdgcn_sched_barrier(0);
+  epilogue_nv256(j, ga, acc, bias_lds, wm, wn, r32, h32);
 }
 
 }  // namespace
@@ -687,8 +834,7 @@ GemmTable make_table(const GemmArgs& ga, const GroupTable& gt, int tm, int tn) {
 }  // namespace
 
 int64_t gemm_tile_count(const GemmArgs& ga, const GroupTable& gt) {
-  const int t = ga.fmt == MGS_FMT_MXFP8 ? BM2 : BM;
-  return make_table(ga, gt, t, t).total_tiles;
+  return make_table(ga, gt, BM2, BN2).total_tiles;
 }
 
 hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t st) {
@@ -697,9 +843,9 @@ hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t st)
     if (tt.total_tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(gemm_mxfp8_256_kernel, dim3((unsigned)tt.total_tiles), dim3(256), 0, st, ga, tt);
   } else {
-    const GemmTable tt = make_table(ga, gt, BM, BN);
+    const GemmTable tt = make_table(ga, gt, BM2, BN2);
     if (tt.total_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_nvfp4_kernel, dim3((unsigned)tt.total_tiles), dim3(256), 0, st, ga, tt);
+    hipLaunchKernelGGL(gemm_nvfp4_256_kernel, dim3((unsigned)tt.total_tiles), dim3(256), 0, st, ga, tt);
   }
   return hipGetLastError();
 }
