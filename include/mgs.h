@@ -76,13 +76,21 @@ enum mgs_status {
  *   TANH_SRELU      a = (s * tanh(relu(x) / s))^2               (bounded at s^2, [P1] reviewer comment)
  *   SWIGLU          x = [gate | up], a = silu(gate) * up        (output width = width_in / 2)
  *   CLAMPED_SWIGLU  g = min(gate, limit), u = clamp(up, -limit, limit), a = g * sigmoid(alpha g) * (u + beta)
- * and the forward output is y = a * p, kept in FP32 until it is quantized. */
+ * and, through the same fused kernels and recompute path ([P1] review discussion: nothing in the
+ * fused recompute is specific to SReLU; GeLU, sigmoid and the GLU family fit the same scheme):
+ *   GELU            a = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2)))   (the exact form, not tanh-approximated)
+ *   SIGMOID         a = 1 / (1 + exp(-x))
+ *   GLU             x = [gate | up], a = sigmoid(gate) * up          (output width = width_in / 2)
+ * The forward output is y = a * p, kept in FP32 until it is quantized. */
 typedef enum {
   MGS_ACT_IDENTITY = 0,
   MGS_ACT_SRELU = 1,
   MGS_ACT_TANH_SRELU = 2,
   MGS_ACT_SWIGLU = 3,
-  MGS_ACT_CLAMPED_SWIGLU = 4
+  MGS_ACT_CLAMPED_SWIGLU = 4,
+  MGS_ACT_GELU = 5,
+  MGS_ACT_SIGMOID = 6,
+  MGS_ACT_GLU = 7
 } mgs_act_kind;
 
 typedef enum { MGS_FMT_MXFP8 = 0, MGS_FMT_NVFP4 = 1 } mgs_fmt;

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libmgs.so")
 MGS_OK = 0
 ERRORS = {-1: "MGS_ERR_INVALID_ARG", -2: "MGS_ERR_SHAPE", -3: "MGS_ERR_UNSUPPORTED", -4: "MGS_ERR_HIP"}
 
-ACT = {"identity": 0, "srelu": 1, "tanh_srelu": 2, "swiglu": 3, "clamped_swiglu": 4}
+ACT = {"identity": 0, "srelu": 1, "tanh_srelu": 2, "swiglu": 3, "clamped_swiglu": 4, "gelu": 5, "sigmoid": 6,
+       "glu": 7}
 FMT = {"mxfp8": 0, "nvfp4": 1}
 GEMM_MODE = {"fprop": 0, "dgrad": 1, "wgrad": 2}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}

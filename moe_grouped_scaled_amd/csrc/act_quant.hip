@@ -289,7 +289,7 @@ __device__ __forceinline__ void launder(uint4& v) {
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 
 template <int KIND>
-constexpr bool is_gated() { return KIND == MGS_ACT_SWIGLU || KIND == MGS_ACT_CLAMPED_SWIGLU; }
+constexpr bool is_gated() { return KIND == MGS_ACT_SWIGLU || KIND == MGS_ACT_CLAMPED_SWIGLU || KIND == MGS_ACT_GLU; }
 
 // probs of the lane's 8 rows (0 for rows outside the panel, 1 when probs is null)
 __device__ __forceinline__ void load_probs(const float* __restrict__ probs, const PanelInfo& pi,
@@ -932,6 +932,9 @@ void group_amax_dispatch(int kind, hipStream_t st, const ActArgs& aa, const Grou
     case MGS_ACT_SRELU: launch_group_amax<MGS_ACT_SRELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
     case MGS_ACT_TANH_SRELU: launch_group_amax<MGS_ACT_TANH_SRELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
     case MGS_ACT_SWIGLU: launch_group_amax<MGS_ACT_SWIGLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_GELU: launch_group_amax<MGS_ACT_GELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_SIGMOID: launch_group_amax<MGS_ACT_SIGMOID, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_GLU: launch_group_amax<MGS_ACT_GLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
     default: launch_group_amax<MGS_ACT_CLAMPED_SWIGLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
   }
 }
@@ -991,6 +994,9 @@ hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int
     case MGS_ACT_SRELU: fwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
     case MGS_ACT_TANH_SRELU: fwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
     case MGS_ACT_SWIGLU: fwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    case MGS_ACT_GELU: fwd_dispatch_fmt<MGS_ACT_GELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    case MGS_ACT_SIGMOID: fwd_dispatch_fmt<MGS_ACT_SIGMOID>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    case MGS_ACT_GLU: fwd_dispatch_fmt<MGS_ACT_GLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
     default: fwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
   }
   if (col_sum) launch_col_sum_reduce(gt, wa, cs_part, col_sum, st);
@@ -1001,7 +1007,7 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
                           const uint16_t* x, const uint16_t* dy, const float* probs, uint16_t* dx,
                           QOut dxq, float* dx_amax, float* dprobs, float* dx_col_sum, void* workspace,
                           QOut actq, hipStream_t st) {
-  const bool gated = act.kind == MGS_ACT_SWIGLU || act.kind == MGS_ACT_CLAMPED_SWIGLU;
+  const bool gated = act.kind == MGS_ACT_SWIGLU || act.kind == MGS_ACT_CLAMPED_SWIGLU || act.kind == MGS_ACT_GLU;
   const int64_t wa = gated ? width_in / 2 : width_in;
   float* cs_part = dx_col_sum ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                                          act_bwd_cs_offset(gt.total_rows, wa))
@@ -1025,6 +1031,9 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
     case MGS_ACT_SRELU: bwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
     case MGS_ACT_TANH_SRELU: bwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
     case MGS_ACT_SWIGLU: bwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
+    case MGS_ACT_GELU: bwd_dispatch_fmt<MGS_ACT_GELU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
+    case MGS_ACT_SIGMOID: bwd_dispatch_fmt<MGS_ACT_SIGMOID>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
+    case MGS_ACT_GLU: bwd_dispatch_fmt<MGS_ACT_GLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
     default: bwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
   }
   if (dprobs && gt.total_rows > 0)

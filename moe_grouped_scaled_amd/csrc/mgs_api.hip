@@ -30,7 +30,7 @@ int ok() {
 
 bool valid_fmt(int32_t fmt) { return fmt == MGS_FMT_MXFP8 || fmt == MGS_FMT_NVFP4; }
 
-bool is_gated(int kind) { return kind == MGS_ACT_SWIGLU || kind == MGS_ACT_CLAMPED_SWIGLU; }
+bool is_gated(int kind) { return kind == MGS_ACT_SWIGLU || kind == MGS_ACT_CLAMPED_SWIGLU || kind == MGS_ACT_GLU; }
 
 // Validates the groups and fills the panel table.  Returns MGS_OK or an error code.
 int build_groups(const mgs_groups* groups, mgs::GroupTable* gt, int64_t* total_rows) {
@@ -92,7 +92,7 @@ int check_qbuf(const mgs_qbuf* q, int32_t fmt, const char* what) {
 
 int check_act(const mgs_act_params* act, mgs::ActHost* out) {
   if (!act) return fail(MGS_ERR_INVALID_ARG, "act is NULL");
-  if (act->kind < MGS_ACT_IDENTITY || act->kind > MGS_ACT_CLAMPED_SWIGLU)
+  if (act->kind < MGS_ACT_IDENTITY || act->kind > MGS_ACT_GLU)
     return fail(MGS_ERR_INVALID_ARG, "unknown activation kind %d", act->kind);
   if (act->kind == MGS_ACT_TANH_SRELU && !(act->s > 0.0f && std::isfinite(act->s)))
     return fail(MGS_ERR_INVALID_ARG, "TANH_SRELU needs a finite s > 0 (got %g)", (double)act->s);

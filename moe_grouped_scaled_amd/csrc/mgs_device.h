@@ -150,6 +150,9 @@ struct ActArgs {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+constexpr float INV_SQRT2 = 0.70710678118654752f;    // 1 / sqrt(2)
+constexpr float INV_SQRT2PI = 0.39894228040143268f;  // 1 / sqrt(2 pi)
+
 // a(x) for unary kinds
 template <int KIND>
 __device__ __forceinline__ float act_unary(float x, const ActArgs& aa) {
@@ -158,6 +161,10 @@ __device__ __forceinline__ float act_unary(float x, const ActArgs& aa) {
   } else if constexpr (KIND == MGS_ACT_SRELU) {
     float r = fmaxf(x, 0.0f);
     return r * r;
+  } else if constexpr (KIND == MGS_ACT_GELU) {
+    return 0.5f * x * (1.0f + erff(x * INV_SQRT2));
+  } else if constexpr (KIND == MGS_ACT_SIGMOID) {
+    return sigmoidf_(x);
   } else {
     float r = fmaxf(x, 0.0f);
     float t = aa.s * tanhf(r * aa.inv_s);
@@ -165,7 +172,7 @@ __device__ __forceinline__ float act_unary(float x, const ActArgs& aa) {
   }
 }
 
-// a'(x) * dy for unary kinds (dy already multiplied by nothing); returns da/dx
+// da/dx for unary kinds
 template <int KIND>
 __device__ __forceinline__ float dact_unary(float x, const ActArgs& aa) {
   if constexpr (KIND == MGS_ACT_IDENTITY) {
@@ -173,6 +180,12 @@ __device__ __forceinline__ float dact_unary(float x, const ActArgs& aa) {
   } else if constexpr (KIND == MGS_ACT_SRELU) {
     float r = fmaxf(x, 0.0f);
     return r + r;
+  } else if constexpr (KIND == MGS_ACT_GELU) {
+    // Phi(x) + x phi(x)
+    return 0.5f * (1.0f + erff(x * INV_SQRT2)) + x * (INV_SQRT2PI * __expf(-0.5f * x * x));
+  } else if constexpr (KIND == MGS_ACT_SIGMOID) {
+    float sg = sigmoidf_(x);
+    return sg * (1.0f - sg);
   } else {
     float r = fmaxf(x, 0.0f);
     float t = tanhf(r * aa.inv_s);
@@ -186,6 +199,8 @@ template <int KIND>
 __device__ __forceinline__ float act_gated(float g, float u, const ActArgs& aa) {
   if constexpr (KIND == MGS_ACT_SWIGLU) {
     return g * sigmoidf_(g) * u;
+  } else if constexpr (KIND == MGS_ACT_GLU) {
+    return sigmoidf_(g) * u;
   } else {
     float gc = fminf(g, aa.limit);
     float uc = fminf(fmaxf(u, -aa.limit), aa.limit);
@@ -203,6 +218,11 @@ __device__ __forceinline__ void dact_gated(float g, float u, const ActArgs& aa, 
     a = silu * u;
     dg = u * sg * (1.0f + g * (1.0f - sg));
     du = silu;
+  } else if constexpr (KIND == MGS_ACT_GLU) {
+    float sg = sigmoidf_(g);
+    a = sg * u;
+    dg = u * (sg * (1.0f - sg));
+    du = sg;
   } else {
     float gc = fminf(g, aa.limit);
     float uc = fminf(fmaxf(u, -aa.limit), aa.limit);

@@ -21,7 +21,7 @@ import torch
 
 from . import _native as N
 
-GATED = ("swiglu", "clamped_swiglu")
+GATED = ("swiglu", "clamped_swiglu", "glu")
 
 
 class ExpertMLP:

@@ -20,17 +20,27 @@ Readings where the pages print no formula (each listed in the design notes):
                       default alpha = 1, beta = 0.  Gradients pass where gate <= L and -L <= up <= L
                       (inclusive), and are zero elsewhere.
   * relu'(0) = 0.
+  * GeLU / sigmoid / GLU ([P1] review discussion: nothing in the fused recompute is specific to
+    SReLU, and GeLU, sigmoid and the GLU family would use the same scheme; no formula is printed):
+                      GeLU:    a(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), the exact form
+                               (the reading that needs no approximation choice);
+                      sigmoid: a(x) = 1 / (1 + exp(-x));
+                      GLU:     [gate | up], a = sigmoid(gate) * up.
 Output of the forward: y = a(x) * p, evaluated in float64 and rounded once to float32 (the value that
 is then block-quantized; it is never rounded to BF16 first).
 Backward: dp[r] = sum_j dy[r, j] * a(x[r])_j ;  dx = dy * p * da/dx, rounded once to float32.
 
 Parity: SReLU forward and backward are exact closed forms (pinned by exact representable inputs);
 TanhSReLU, SwiGLU and ClampedSwiGLU gradients are pinned by central finite differences and limits;
-the formulas of TanhSReLU / SwiGLU / ClampedSwiGLU themselves are readings (parity unpinned as to
-the formula, since the pages print none).
+GeLU by the textbook value Phi(1), the odd-part identity GeLU(x) - GeLU(-x) = x and its limits;
+sigmoid by sigmoid(ln 3) = 3/4 and the symmetry sigmoid(x) + sigmoid(-x) = 1; GLU by its values at
+gate = 0 and gate = ln 3; all gradients by central differences.  The formulas of TanhSReLU / SwiGLU /
+ClampedSwiGLU / GeLU / sigmoid / GLU themselves are readings (parity unpinned as to the formula,
+since the pages print none).
 """
 
 import numpy as np
+from scipy.special import erf
 
 from .codecs import f32
 
@@ -39,8 +49,11 @@ TANH_SRELU = "tanh_srelu"
 SWIGLU = "swiglu"
 CLAMPED_SWIGLU = "clamped_swiglu"
 IDENTITY = "identity"
+GELU = "gelu"
+SIGMOID = "sigmoid"
+GLU = "glu"
 
-GATED = (SWIGLU, CLAMPED_SWIGLU)
+GATED = (SWIGLU, CLAMPED_SWIGLU, GLU)
 
 
 def out_width(kind, width_in):
@@ -63,10 +76,16 @@ def act(kind, x, s=2.0, limit=7.0, alpha=1.0, beta=0.0):
         r = np.maximum(x, 0.0)
         t = s * np.tanh(r / s)
         return t * t
+    if kind == GELU:
+        return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+    if kind == SIGMOID:
+        return _sigmoid(x)
     w = x.shape[-1] // 2
     g, u = x[..., :w], x[..., w:]
     if kind == SWIGLU:
         return g * _sigmoid(g) * u
+    if kind == GLU:
+        return _sigmoid(g) * u
     if kind == CLAMPED_SWIGLU:
         gc = np.minimum(g, limit)
         uc = np.clip(u, -limit, limit)
@@ -89,11 +108,20 @@ def act_grad(kind, x, s=2.0, limit=7.0, alpha=1.0, beta=0.0):
         r = np.maximum(x, 0.0)
         t = np.tanh(r / s)
         return np.where(x > 0.0, 2.0 * s * t * (1.0 - t * t), 0.0)
+    if kind == GELU:
+        # Phi(x) + x phi(x)
+        return 0.5 * (1.0 + erf(x / np.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+    if kind == SIGMOID:
+        sg = _sigmoid(x)
+        return sg * (1.0 - sg)
     w = x.shape[-1] // 2
     g, u = x[..., :w], x[..., w:]
     if kind == SWIGLU:
         sg = _sigmoid(g)
         return u * sg * (1.0 + g * (1.0 - sg)), g * sg
+    if kind == GLU:
+        sg = _sigmoid(g)
+        return u * sg * (1.0 - sg), sg
     if kind == CLAMPED_SWIGLU:
         gc = np.minimum(g, limit)
         uc = np.clip(u, -limit, limit)

@@ -144,6 +144,13 @@ FWD_CASES = [
     ("swiglu", "nvfp4", [17, 250], 1024, 1.0),
     ("clamped_swiglu", "mxfp8", [0, 300, 1, 700, 23], 4096, 3.0),
     ("clamped_swiglu", "nvfp4", [64, 100], 512, 3.0),
+    # the other activations through the same kernels
+    ("gelu", "mxfp8", [37, 0, 200, 91], 1024, 1.5),
+    ("gelu", "nvfp4", [64, 100], 512, 1.5),
+    ("sigmoid", "mxfp8", [5, 250], 512, 2.0),
+    ("sigmoid", "nvfp4", [128, 0, 30], 512, 2.0),
+    ("glu", "mxfp8", [100, 0, 61], 2048, 1.0),
+    ("glu", "nvfp4", [70, 58], 1024, 1.0),
 ]
 
 
@@ -246,6 +253,10 @@ BWD_CASES = [
     ("swiglu", "mxfp8", [300, 0, 212], 4096, 1.0),
     ("swiglu", "nvfp4", [70, 58], 1024, 1.0),
     ("clamped_swiglu", "mxfp8", [0, 200, 56], 2048, 3.0),
+    ("gelu", "mxfp8", [50, 0, 170], 1024, 1.5),
+    ("gelu", "nvfp4", [64, 64], 512, 1.5),
+    ("sigmoid", "nvfp4", [96, 32], 512, 2.0),
+    ("glu", "mxfp8", [300, 0, 212], 2048, 1.0),
 ]
 
 
@@ -270,7 +281,17 @@ def test_act_bwd_parity(N, kind, fmt, splits, width_in, std):
         diff = got["dx"] != ref_dx
         assert diff.mean() <= 1e-3
         gv, rv = bf16_f64(got["dx"][diff]), bf16_f64(ref_dx[diff])
-        assert np.all(np.abs(gv - rv) <= np.abs(rv) * 2.0 ** -7 * 1.0001 + 1e-30)
+        # one BF16 step of the result, or (near a root of the derivative, where its FP32 terms
+        # cancel: GeLU' = Phi + x phi near x = -0.75, SwiGLU's 1 + g (1 - sigmoid g) near g = -1.28)
+        # an FP32-level error of those terms: 2^-20 of their magnitude, bounded by (1 + |x|) per
+        # operand of the derivative, times |dy| p
+        wa = A.out_width(kind, width_in)
+        xg = np.abs(x[:, :wa])
+        xu = np.abs(x[:, wa:]) if kind in A.GATED else np.zeros_like(xg)
+        mag = np.abs(dy) * p[:, None] * (1.0 + xg) * (1.0 + xu)
+        mag = np.concatenate([mag, mag], axis=1) if kind in A.GATED else mag
+        tol = np.abs(rv) * 2.0 ** -7 * 1.0001 + 2.0 ** -20 * mag[diff] + 1e-30
+        assert np.all(np.abs(gv - rv) <= tol), np.max(np.abs(gv - rv) / tol)
     # per-group column sums of the dense BF16 dL/dx (bias gradient): any FP32 summation order of the
     # oracle's BF16 values lies within (m_g + 1) * 2^-24 * sum |v|; where the dense values may differ
     # by one BF16 step (non-exact kinds), at most 2^-7 * sum |v| more
@@ -299,7 +320,8 @@ def test_act_bwd_parity(N, kind, fmt, splits, width_in, std):
 
 @pytest.mark.parametrize("kind,fmt", [("srelu", "mxfp8"), ("tanh_srelu", "mxfp8"), ("swiglu", "mxfp8"),
                                       ("clamped_swiglu", "mxfp8"), ("srelu", "nvfp4"),
-                                      ("tanh_srelu", "nvfp4")])
+                                      ("tanh_srelu", "nvfp4"), ("gelu", "mxfp8"),
+                                      ("sigmoid", "nvfp4"), ("glu", "mxfp8")])
 def test_recompute_is_bitwise_equal_to_forward_columnwise(N, kind, fmt):
     """The backward's regenerated FC2 input (act_col) is byte-identical to what the forward's
     columnwise output would have stored (recompute changes only what is kept)."""

@@ -24,7 +24,7 @@ def torch_mod():
 
 def _inputs(kind, e, splits, h, f, seed):
     rng = np.random.default_rng(seed)
-    f_in = 2 * f if kind in ("swiglu", "clamped_swiglu") else f
+    f_in = 2 * f if kind in ("swiglu", "clamped_swiglu", "glu") else f
     m = int(np.sum(splits))
     return dict(x1=workloads.normal_bf16(rng, (m, h)), w1=workloads.normal_bf16(rng, (e, f_in, h), 0.05),
                 w2=workloads.normal_bf16(rng, (e, h, f), 0.05), b1=workloads.normal_bf16(rng, (e, f_in), 0.05),
@@ -58,7 +58,8 @@ def _run_gpu(kind, fmt, d, recompute, delay, bias=True):
 
 
 @pytest.mark.parametrize("kind,fmt", [("srelu", "mxfp8"), ("tanh_srelu", "mxfp8"), ("srelu", "nvfp4"),
-                                      ("tanh_srelu", "nvfp4"), ("swiglu", "mxfp8")])
+                                      ("tanh_srelu", "nvfp4"), ("swiglu", "mxfp8"), ("gelu", "mxfp8"),
+                                      ("glu", "nvfp4")])
 def test_mlp_step_matches_oracle(torch_mod, kind, fmt):
     e, splits, h, f = 4, [64, 0, 96, 37], 128, 128
     d = _inputs(kind, e, splits, h, f, seed=3)

@@ -8,7 +8,7 @@ import pytest
 from oracle import activations as A
 from oracle.codecs import f32
 
-KINDS = [A.SRELU, A.TANH_SRELU, A.SWIGLU, A.CLAMPED_SWIGLU]
+KINDS = [A.SRELU, A.TANH_SRELU, A.SWIGLU, A.CLAMPED_SWIGLU, A.GELU, A.SIGMOID, A.GLU]
 
 
 def test_srelu_exact_values():
@@ -71,6 +71,39 @@ def test_clamped_swiglu_regions():
     # alpha/beta variant reduces to plain SwiGLU far from the limits when alpha = 1, beta = 0
     z = np.array([[0.3, -1.2, 0.7, 2.5]])
     assert np.allclose(A.act(A.CLAMPED_SWIGLU, z, limit=L), A.act(A.SWIGLU, z), rtol=0, atol=1e-15)
+
+
+def test_gelu_values_and_identities():
+    """GeLU(x) = x Phi(x): the tabulated standard normal CDF Phi(1) = 0.841344746068543, GeLU(0) = 0,
+    the odd-part identity GeLU(x) - GeLU(-x) = x (Phi(x) + Phi(-x) = 1), and the limits x and 0."""
+    x = np.array([[1.0, -1.0, 0.0, 8.0, -8.0]])
+    a = A.act(A.GELU, x)[0]
+    assert abs(a[0] - 0.841344746068543) < 1e-14
+    assert abs(a[1] + (1.0 - 0.841344746068543)) < 1e-14
+    assert a[2] == 0.0
+    assert abs(a[3] - 8.0) < 1e-12 and abs(a[4]) < 1e-12
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((3, 64)) * 3
+    assert np.allclose(A.act(A.GELU, z) - A.act(A.GELU, -z), z, rtol=0, atol=1e-14)
+    # the slope at 0 is Phi(0) = 1/2
+    assert abs(A.act_grad(A.GELU, np.zeros((1, 1)))[0, 0] - 0.5) < 1e-15
+
+
+def test_sigmoid_and_glu_values():
+    """sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4 exactly in exact arithmetic, sigmoid(x) + sigmoid(-x) = 1;
+    GLU = sigmoid(gate) * up at those gates; its up-gradient is sigmoid(gate)."""
+    l3 = np.log(3.0)
+    s = A.act(A.SIGMOID, np.array([[0.0, l3, -l3]]))[0]
+    assert s[0] == 0.5 and abs(s[1] - 0.75) < 1e-15 and abs(s[2] - 0.25) < 1e-15
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((2, 32)) * 4
+    assert np.allclose(A.act(A.SIGMOID, z) + A.act(A.SIGMOID, -z), 1.0, rtol=0, atol=1e-15)
+    x = np.array([[0.0, l3, 2.0, -4.0]])   # gates 0, ln 3; ups 2, -4
+    a = A.act(A.GLU, x)[0]
+    assert a[0] == 1.0 and abs(a[1] + 3.0) < 1e-14
+    dg, du = A.act_grad(A.GLU, x)
+    assert du[0, 0] == 0.5 and abs(du[0, 1] - 0.75) < 1e-15
+    assert abs(dg[0, 0] - 2.0 * 0.25) < 1e-15 and abs(dg[0, 1] + 4.0 * 0.75 * 0.25) < 1e-14
 
 
 @pytest.mark.parametrize("kind", KINDS)

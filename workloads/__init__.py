@@ -122,7 +122,7 @@ def act_case(kind, splits, width_in, seed=0, std=1.0, with_dy=True):
     rng = np.random.default_rng(seed)
     splits = np.asarray(splits, dtype=np.int64)
     m = int(splits.sum())
-    wa = width_in // 2 if kind in ("swiglu", "clamped_swiglu") else width_in
+    wa = width_in // 2 if kind in ("swiglu", "clamped_swiglu", "glu") else width_in
     d = dict(kind=kind, splits=splits, width_in=width_in, x=normal_bf16(rng, (m, width_in), std),
              p=uniform_f32(rng, m))
     if with_dy:
