@@ -163,7 +163,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--fmt", default="mxfp8", choices=["mxfp8", "nvfp4"])
-    ap.add_argument("--act", default="srelu", choices=["srelu", "tanh_srelu"])
+    ap.add_argument("--act", default="srelu", choices=["srelu", "tanh_srelu", "gelu", "sigmoid"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
