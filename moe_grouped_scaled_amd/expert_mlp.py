@@ -5,6 +5,11 @@ Sources:
     activation + grouped quantize, then the FC2 grouped GEMM, saving (input_, scales); backward = FC2
     backward giving dL/d(act_out * scales), then the fused activation backward giving (grouped_dy,
     dense_dy, grad_scales), then FC1's backward.
+  * same page, review finding on the fused backward: with FC1's weights frozen while the per-row
+    scales (and the module input) still need gradients, the fused backward must run without FC1's
+    weight-gradient state.  Here every gradient is requested separately (`grad_x1`, `grad_probs`,
+    `grad_fc1`, `grad_fc2`); an unrequested one is a NULL output of the fused launches, and the
+    quantized copies only it would consume are neither made nor kept.
   * page "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU", Description: with
     activation recompute the forward keeps only the BF16 FC1 output and the backward regenerates FC2's
     input from it; forward, dgrad, dprobs and FC1 wgrad are unchanged; memory drops between forward and
@@ -26,7 +31,8 @@ GATED = ("swiglu", "clamped_swiglu", "glu")
 
 class ExpertMLP:
     def __init__(self, kind, fmt, w1, w2, b1=None, b2=None, recompute=False, delay_wgrad=False,
-                 s=2.0, limit=7.0, alpha=1.0, beta=0.0):
+                 s=2.0, limit=7.0, alpha=1.0, beta=0.0, grad_x1=True, grad_probs=True, grad_fc1=True,
+                 grad_fc2=True):
         self.kind, self.fmt = kind, fmt
         self.w1, self.w2, self.b1, self.b2 = w1, w2, b1, b2
         self.e, self.f_in, self.h = w1.shape
@@ -34,6 +40,11 @@ class ExpertMLP:
         assert w2.shape == (self.e, self.h, self.f)
         assert self.f_in == (2 * self.f if kind in GATED else self.f)
         self.recompute, self.delay_wgrad = recompute, delay_wgrad
+        # which gradients the backward produces (parameters of FC1 / FC2 = weight and bias)
+        self.grad_x1, self.grad_probs = grad_x1, grad_probs
+        self.grad_fc1, self.grad_fc2 = grad_fc1, grad_fc2
+        # anything below FC2's output needs FC2's dgrad and the activation backward
+        self.grad_below_fc2 = grad_x1 or grad_probs or grad_fc1
         self.act = N.act_params(kind, s=s, limit=limit, alpha=alpha, beta=beta)
         self.ctx = None
         self.pending_wgrad = None
@@ -58,17 +69,18 @@ class ExpertMLP:
         m = x1.shape[0]
         fmt = self.fmt
         wsplit1, wsplit2 = [f_in] * e, [h] * e
-        x1_row, x1_col = self._quant(x1, splits, h)                         # FC1 fprop / FC1 wgrad
-        w1_row, w1_col = self._quant(self.w1.view(e * f_in, h), wsplit1, h)  # fprop / dgrad copies
+        x1_row, x1_col = self._quant(x1, splits, h, col=self.grad_fc1)       # FC1 fprop / FC1 wgrad
+        w1_row, w1_col = self._quant(self.w1.view(e * f_in, h), wsplit1, h,  # fprop / dgrad copies
+                                     col=self.grad_x1)
         y1 = torch.empty((m, f_in), dtype=torch.bfloat16, device="cuda")
         N.grouped_gemm_mx("fprop", fmt, splits, m, f_in, h, x1_row, w1_row, y1, bias=self.b1)
         del x1_row, w1_row
         a_row = N.QTensor(fmt, False, splits, f)
-        a_col = None if self.recompute else N.QTensor(fmt, True, splits, f)
+        a_col = None if (self.recompute or not self.grad_fc2) else N.QTensor(fmt, True, splits, f)
         a_amax = self._amax_buf(e)
         N.grouped_scaled_act_fwd(self.act, fmt, splits, f_in, y1, probs, a_row, a_col, a_amax)
         self.trace["fwd_act_col"] += a_col is not None
-        w2_row, w2_col = self._quant(self.w2.view(e * h, f), wsplit2, f)
+        w2_row, w2_col = self._quant(self.w2.view(e * h, f), wsplit2, f, col=self.grad_below_fc2)
         y2 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
         N.grouped_gemm_mx("fprop", fmt, splits, m, h, f, a_row, w2_row, y2, bias=self.b2)
         del a_row, w2_row
@@ -89,38 +101,55 @@ class ExpertMLP:
         c = self.ctx
         splits, m, fmt = c["splits"], c["m"], self.fmt
         e, h, f, f_in = self.e, self.h, self.f, self.f_in
+        g1, g2, below = self.grad_fc1, self.grad_fc2, self.grad_below_fc2
         # dY2 quantized for FC2's dgrad and wgrad; FC2's bias gradient (its column sums) in the same pass
-        dy2_row = N.QTensor(fmt, False, splits, h)
-        dy2_col = N.QTensor(fmt, True, splits, h)
-        db2 = torch.empty((e, h), dtype=torch.float32, device="cuda") if self.b2 is not None else None
-        N.grouped_mx_quantize(fmt, splits, h, dy2, dy2_row, dy2_col, self._amax_buf(e), col_sum=db2,
-                              workspace=self._workspace(N.quantize_workspace_bytes(splits, h)))
-        da = torch.empty((m, f), dtype=torch.bfloat16, device="cuda")
-        N.grouped_gemm_mx("dgrad", fmt, splits, m, f, h, dy2_row, c["w2_col"], da)
-        del dy2_row
-        # FC1's bias gradient: column sums of the dense BF16 dY1, taken inside the activation backward
-        db1 = torch.empty((e, f_in), dtype=torch.float32, device="cuda") if self.b1 is not None else None
-        dy1_row = N.QTensor(fmt, False, splits, f_in)
-        dy1_col = N.QTensor(fmt, True, splits, f_in)
-        dprobs = torch.empty(m, dtype=torch.float32, device="cuda")
+        dy2_row = N.QTensor(fmt, False, splits, h) if below else None
+        dy2_col = N.QTensor(fmt, True, splits, h) if g2 else None
+        db2 = torch.empty((e, h), dtype=torch.float32, device="cuda") if (g2 and self.b2 is not None) else None
+        if below or g2:
+            N.grouped_mx_quantize(fmt, splits, h, dy2, dy2_row, dy2_col, self._amax_buf(e), col_sum=db2,
+                                  workspace=self._workspace(N.quantize_workspace_bytes(splits, h)))
         a_col = c["a_col"]
-        if self.recompute:
+        grads = {}
+        dy1_col = db1 = None
+        if below:
+            da = torch.empty((m, f), dtype=torch.bfloat16, device="cuda")
+            N.grouped_gemm_mx("dgrad", fmt, splits, m, f, h, dy2_row, c["w2_col"], da)
+            del dy2_row
+            # FC1's bias gradient: column sums of the dense BF16 dY1, taken inside the activation backward
+            db1 = torch.empty((e, f_in), dtype=torch.float32, device="cuda") if (g1 and self.b1 is not None) else None
+            dy1_row = N.QTensor(fmt, False, splits, f_in) if self.grad_x1 else None
+            dy1_col = N.QTensor(fmt, True, splits, f_in) if g1 else None
+            dprobs = torch.empty(m, dtype=torch.float32, device="cuda") if self.grad_probs else None
+            if self.recompute and g2:
+                a_col = N.QTensor(fmt, True, splits, f)
+                self.trace["bwd_act_col"] += 1
+            N.grouped_scaled_act_bwd(self.act, fmt, splits, f_in, c["y1"], da, c["probs"],
+                                     dx_row=dy1_row, dx_col=dy1_col,
+                                     dx_group_amax=self._amax_buf(e) if (dy1_row is not None or dy1_col is not None) else None,
+                                     dprobs=dprobs, dx_col_sum=db1,
+                                     act_col=a_col if (self.recompute and g2) else None,
+                                     saved_group_amax=c["a_amax"],
+                                     workspace=self._workspace(N.act_bwd_workspace_bytes(self.act, splits, f_in)))
+            del da
+            if self.grad_x1:
+                dx1 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
+                N.grouped_gemm_mx("dgrad", fmt, splits, m, h, f_in, dy1_row, c["w1_col"], dx1)
+                del dy1_row
+                grads["dx1"] = dx1
+            if self.grad_probs:
+                grads["dprobs"] = dprobs
+        elif self.recompute and g2:
+            # nothing below FC2 needs a gradient: FC2's columnwise input is regenerated from the saved
+            # BF16 FC1 output by a forward launch that requests only that output (the same bits)
             a_col = N.QTensor(fmt, True, splits, f)
             self.trace["bwd_act_col"] += 1
-        N.grouped_scaled_act_bwd(self.act, fmt, splits, f_in, c["y1"], da, c["probs"],
-                                 dx_row=dy1_row, dx_col=dy1_col, dx_group_amax=self._amax_buf(e),
-                                 dprobs=dprobs, dx_col_sum=db1, act_col=a_col if self.recompute else None,
-                                 saved_group_amax=c["a_amax"],
-                                 workspace=self._workspace(N.act_bwd_workspace_bytes(self.act, splits, f_in)))
-        del da
-        dx1 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
-        N.grouped_gemm_mx("dgrad", fmt, splits, m, h, f_in, dy1_row, c["w1_col"], dx1)
-        del dy1_row
+            N.grouped_scaled_act_fwd(self.act, fmt, splits, f_in, c["y1"], c["probs"], None, a_col,
+                                     self._amax_buf(e))
         # what the weight gradients consume stays alive until backward_dw (possibly delayed)
-        self.pending_wgrad = dict(splits=splits, m=m, dy2_col=dy2_col, a_col=a_col,
-                                  dy1_col=dy1_col, x1_col=c["x1_col"], db1=db1, db2=db2)
+        self.pending_wgrad = dict(splits=splits, m=m, dy2_col=dy2_col, a_col=a_col if g2 else None,
+                                  dy1_col=dy1_col, x1_col=c["x1_col"] if g1 else None, db1=db1, db2=db2)
         self.ctx = None
-        grads = {"dx1": dx1, "dprobs": dprobs}
         if not self.delay_wgrad:
             grads.update(self.backward_dw())
         return grads
@@ -131,13 +160,17 @@ class ExpertMLP:
         assert p is not None, "backward_dw() without a pending backward"
         splits, m, fmt = p["splits"], p["m"], self.fmt
         e, h, f, f_in = self.e, self.h, self.f, self.f_in
-        if dw2 is None:
-            dw2 = torch.empty((e, h, f), dtype=torch.float32, device="cuda")
-        if dw1 is None:
-            dw1 = torch.empty((e, f_in, h), dtype=torch.float32, device="cuda")
-        N.grouped_gemm_mx("wgrad", fmt, splits, h, f, m, p["dy2_col"], p["a_col"], dw2, accumulate=accumulate)
-        N.grouped_gemm_mx("wgrad", fmt, splits, f_in, h, m, p["dy1_col"], p["x1_col"], dw1, accumulate=accumulate)
-        out = {"dw1": dw1, "dw2": dw2}
+        out = {}
+        if self.grad_fc2:
+            if dw2 is None:
+                dw2 = torch.empty((e, h, f), dtype=torch.float32, device="cuda")
+            N.grouped_gemm_mx("wgrad", fmt, splits, h, f, m, p["dy2_col"], p["a_col"], dw2, accumulate=accumulate)
+            out["dw2"] = dw2
+        if self.grad_fc1:
+            if dw1 is None:
+                dw1 = torch.empty((e, f_in, h), dtype=torch.float32, device="cuda")
+            N.grouped_gemm_mx("wgrad", fmt, splits, f_in, h, m, p["dy1_col"], p["x1_col"], dw1, accumulate=accumulate)
+            out["dw1"] = dw1
         # the bias gradients were taken in the backward's quantize / activation passes
         if p["db2"] is not None:
             out["db2"] = p["db2"]

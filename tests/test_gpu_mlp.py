@@ -126,3 +126,47 @@ def test_no_bias_variant(torch_mod):
     d = _inputs("srelu", e, splits, h, f, seed=8)
     a = _run_gpu("srelu", "mxfp8", d, recompute=False, delay=False, bias=False)
     assert "db1" not in a and np.isfinite(a["dw1"]).all()
+
+
+def _run_partial(fmt, d, recompute, flags):
+    """One step with only the gradients `flags` asks for; returns the host copies of what it produced."""
+    import torch
+    from moe_grouped_scaled_amd.expert_mlp import ExpertMLP
+    mlp = ExpertMLP("srelu", fmt, to_dev_bf16(d["w1"]), to_dev_bf16(d["w2"]), to_dev_bf16(d["b1"]),
+                    to_dev_bf16(d["b2"]), recompute=recompute, delay_wgrad=True, **flags)
+    y2 = mlp.forward(to_dev_bf16(d["x1"]), to_dev(d["p"]), list(d["splits"]))
+    g = mlp.backward(to_dev_bf16(d["dy2"]))
+    g.update(mlp.backward_dw())
+    torch.cuda.synchronize()
+    out = {k: (bf16_host(v) if v.dtype == torch.bfloat16 else f32(v)) for k, v in g.items()}
+    out["y2"] = bf16_host(y2)
+    return out
+
+
+# The review finding on the fused backward ("Activation + GroupedLinear Fusion for MOE", Greptile
+# review): FC1 frozen while the per-row scales and the module input still need gradients.  Every
+# request set must give bitwise the gradients of the full step, and nothing it did not ask for.
+PARTIAL = [
+    dict(grad_fc1=False),                                                   # the review's case
+    dict(grad_fc1=False, grad_x1=False, grad_fc2=False),                    # only the scales
+    dict(grad_x1=False, grad_probs=False, grad_fc1=False),                  # only FC2's parameters
+    dict(grad_probs=False),
+    dict(grad_x1=False, grad_fc2=False),
+]
+KEYS = {"dx1": "grad_x1", "dprobs": "grad_probs", "dw1": "grad_fc1", "db1": "grad_fc1",
+        "dw2": "grad_fc2", "db2": "grad_fc2"}
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("recompute", [True, False])
+def test_partial_gradients_match_full_step(torch_mod, fmt, recompute):
+    e, splits, h, f = 4, [64, 0, 96, 37], 128, 128
+    d = _inputs("srelu", e, splits, h, f, seed=11)
+    full = _run_partial(fmt, d, recompute, {})
+    assert set(full) == set(KEYS) | {"y2"}
+    for flags in PARTIAL:
+        got = _run_partial(fmt, d, recompute, flags)
+        want = {k for k, flag in KEYS.items() if flags.get(flag, True)} | {"y2"}
+        assert set(got) == want, (flags, sorted(got))
+        for k in want:
+            assert np.array_equal(got[k], full[k]), (flags, k)   # BF16 bits or FP32 values
