@@ -75,8 +75,8 @@ class Timer:
         self.records = []
         self.enabled = False
         self._orig = {}
-        for name in ("grouped_scaled_act_fwd", "grouped_scaled_act_bwd", "grouped_mx_quantize",
-                     "grouped_gemm_mx"):
+        for name in ("grouped_scaled_act_fwd", "grouped_scaled_act_fwd_f32", "grouped_scaled_act_bwd",
+                     "grouped_mx_quantize", "grouped_gemm_mx"):
             self._wrap(name)
 
     def _wrap(self, name):
@@ -128,12 +128,12 @@ def measured_traffic(fmt):
 
 def cpu_baseline(kind, fmt, seed=0):
     """The oracle's expert-MLP step on a bounded sample of the workload: one of the 16 experts with
-    512 tokens, full hidden 4096 / ffn 4096 weights.  Returns the oracle's GEMM TFLOP/s."""
+    1024 tokens, full hidden 4096 / ffn 4096 weights.  Returns the oracle's GEMM TFLOP/s."""
     from oracle import mlp as M
     import workloads
     from oracle.codecs import bf16_bits_to_f64
     rng = np.random.default_rng(seed)
-    e, tok, h, f = 1, 512, 4096, 4096
+    e, tok, h, f = 1, 1024, 4096, 4096
     splits = [tok] * e
     m = e * tok
     x1 = bf16_bits_to_f64(workloads.normal_bf16(rng, (m, h)))
@@ -153,8 +153,8 @@ def cpu_baseline(kind, fmt, seed=0):
     except Exception:  # threadpoolctl missing: report the visible cores
         threads = os.cpu_count()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "oracle expert-MLP step (numpy float64), 1 expert x 512 tokens, hidden 4096, "
-                      "ffn 4096, same recipe; %.1f s wall" % dt}
+            "sample": "oracle expert-MLP step (numpy float64), 1 expert x %d tokens, hidden 4096, "
+                      "ffn 4096, same recipe; %.1f s wall" % (tok, dt)}
 
 
 def main():
@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--fmt", default="mxfp8", choices=["mxfp8", "nvfp4"])
     ap.add_argument("--act", default="srelu", choices=["srelu", "tanh_srelu", "gelu", "sigmoid"])
+    ap.add_argument("--fc1-fp32-act", action="store_true",
+                    help="activate FC1's FP32 output in the forward (the recompute then regenerates FC2's "
+                         "input from its BF16 copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -202,7 +205,8 @@ def main():
     # recompute memory drop, measured between forward and backward
     held = {}
     for rc in (False, True):
-        mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=rc, delay_wgrad=True, s=2.0)
+        mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=rc, delay_wgrad=True, s=2.0,
+                        fc1_fp32_act=args.fc1_fp32_act)
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         y = mlp.forward(x1, p, splits)
@@ -214,7 +218,8 @@ def main():
     col_rows = m  # every expert's token count is a multiple of 32
     drop_closed = col_rows * f + col_rows * f // 32 if args.fmt == "mxfp8" else col_rows * f // 2 + col_rows * f // 16
 
-    mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=True, delay_wgrad=True, s=2.0)
+    mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=True, delay_wgrad=True, s=2.0,
+                    fc1_fp32_act=args.fc1_fp32_act)
 
     def step():
         mlp.forward(x1, p, splits)
@@ -246,11 +251,16 @@ def main():
     gemm_tflops = flops_launch / gemm_avg / 1e12
     peak = MFMA_PEAK_TFLOPS[args.fmt]
     fwd_b = act_fwd_bytes(m, f, f, args.fmt, row=True, col=False)
+    fwd_name = "grouped_scaled_act_fwd"
+    if args.fc1_fp32_act:
+        # FP32 input instead of BF16, plus the BF16 copy the backward keeps
+        fwd_b += 2 * m * f + 2 * m * f
+        fwd_name = "grouped_scaled_act_fwd_f32"
     # the step asks the backward for quantized dY1 (row + col), dprobs, the recomputed FC2 input and
     # FC1's bias gradient; the dense BF16 dY1 is not written
     bwd_b = act_bwd_bytes(m, f, f, args.fmt, dense=False, row=True, col=True, dprobs=True, recompute=True,
                           col_sum_groups=e)
-    t_fwd = float(np.mean(dur["grouped_scaled_act_fwd"]))
+    t_fwd = float(np.mean(dur[fwd_name]))
     t_bwd = float(np.mean(dur["grouped_scaled_act_bwd"]))
     kernels = {
         "act_fwd": {"GB/s": fwd_b / t_fwd / 1e9, "frac_hbm": fwd_b / t_fwd / 1e9 / HBM_PEAK_GBPS,
@@ -269,8 +279,10 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8" if args.fmt == "mxfp8" else "fp4", "data": "synthetic",
         "config": {"workload": "expert-MLP train step: 16 experts x 2048 tokens, hidden 4096, ffn 4096, "
-                               "%s, %s, bias, recompute on, delayed wgrad" % (args.act, args.fmt.upper()),
-                   "experts": e, "tokens": m, "hidden": h, "ffn": f, "recipe": args.fmt, "act": args.act},
+                               "%s, %s, bias, recompute on, delayed wgrad%s" % (
+                                   args.act, args.fmt.upper(), ", FP32 FC1 output activated" if args.fc1_fp32_act else ""),
+                   "experts": e, "tokens": m, "hidden": h, "ffn": f, "recipe": args.fmt, "act": args.act,
+                   "act_input": "fp32" if args.fc1_fp32_act else "bf16"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": gemm_tflops / peak, "traffic": measured_traffic(args.fmt)},
         "kernels": kernels,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MGS_ABI_VERSION 3
+#define MGS_ABI_VERSION 4
 #define MGS_MAX_GROUPS 256
 
 enum mgs_status {
@@ -151,6 +151,20 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
                                int64_t width_in, const void* x_bf16, const float* probs,
                                const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
                                void* stream);
+
+/* Fused forward from the FP32 FC1 output.  [P1] Description and review discussion: in the fused
+ * forward the activation is applied to the FP32 accumulator of the FC1 GEMM, while the backward and
+ * the recompute read the saved BF16 FC1 output; the regenerated FC2 input therefore differs slightly
+ * from the forward's (the deviation that page tabulates for the FC2 weight gradient).  Same outputs
+ * and rules as mgs_grouped_scaled_act_fwd, except:
+ *   x_f32      [M x width_in] FP32, row-major (required unless M == 0); width_in * 128 < 2^31
+ *   x_bf16_out [M x width_in] BF16 nullable: receives x rounded to nearest-even, the tensor the
+ *              backward and the recompute take as x_bf16 (written in the same pass)
+ * At least one of out_row, out_col, x_bf16_out must be requested. */
+int mgs_grouped_scaled_act_fwd_f32(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                                   int64_t width_in, const float* x_f32, const float* probs,
+                                   const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
+                                   void* x_bf16_out, void* stream);
 
 /* Fused backward.  [P2] sequence diagram, backward half: grouped_scaled_d{swiglu,srelu}(grad, input_,
  * scales, quantizer) -> (grouped_dy, dense_dy, grad_scales), where grad = dL/d(act_out * scales);

@@ -59,6 +59,7 @@ def _load():
         "mgs_last_error": (ctypes.c_char_p, []),
         "mgs_qtensor_nbytes": (i64, [i32, i32, pgr, i64, i32]),
         "mgs_grouped_scaled_act_fwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, pq, pq, vp, vp]),
+        "mgs_grouped_scaled_act_fwd_f32": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, pq, pq, vp, vp, vp]),
         "mgs_grouped_scaled_act_bwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, vp, vp, pq, pq, vp,
                                                       vp, vp, pq, vp, vp, i64, vp]),
         "mgs_act_bwd_workspace_bytes": (i64, [pact, pgr, i64]),
@@ -77,6 +78,7 @@ def _load():
 
 LIB = _load()
 EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
+            "mgs_grouped_scaled_act_fwd_f32",
             "mgs_grouped_scaled_act_bwd", "mgs_act_bwd_workspace_bytes", "mgs_grouped_mx_quantize",
             "mgs_grouped_mx_quantize_workspace_bytes", "mgs_grouped_gemm_mx", "mgs_grouped_col_sum")
 
@@ -170,6 +172,17 @@ def grouped_scaled_act_fwd(act, fmt, split_sizes, width_in, x, probs, out_row=No
     _c, cref = _qref(out_col)
     _check(LIB.mgs_grouped_scaled_act_fwd(ctypes.byref(act), FMT[fmt], g.ref, int(width_in), _ptr(x),
                                           _ptr(probs), rref, cref, _ptr(group_amax), _stream(stream)))
+
+
+def grouped_scaled_act_fwd_f32(act, fmt, split_sizes, width_in, x, probs, out_row=None, out_col=None,
+                               group_amax=None, x_bf16_out=None, stream=None):
+    """Forward from an FP32 input `x`; `x_bf16_out` (nullable) receives its BF16 rounding."""
+    g = _GroupsArg(split_sizes)
+    _r, rref = _qref(out_row)
+    _c, cref = _qref(out_col)
+    _check(LIB.mgs_grouped_scaled_act_fwd_f32(ctypes.byref(act), FMT[fmt], g.ref, int(width_in), _ptr(x),
+                                              _ptr(probs), rref, cref, _ptr(group_amax), _ptr(x_bf16_out),
+                                              _stream(stream)))
 
 
 def act_bwd_workspace_bytes(act, split_sizes, width_in):

@@ -87,9 +87,14 @@ __device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t vo, uint32_t so) {
   const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// A store of more than 8 bytes reads its data VGPRs after it issues: on gfx950 a VALU write to one
+// of them in the very next instruction changed what the last lanes of each 16-lane group stored
+// (measured: they stored the new value), and the compiler does not keep the two apart for this
+// target.  The empty asm keeps the data registers live until two wait states after the store.
 __device__ __forceinline__ void bst16(uint4 d, rsrc_t r, uint32_t vo, uint32_t so) {
   const v4u v = {d.x, d.y, d.z, d.w};
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)vo, (int)so, 0);
+  asm volatile("s_nop 1" :: "v"(v));
 }
 __device__ __forceinline__ void bst8(uint2 d, rsrc_t r, uint32_t vo, uint32_t so) {
   const v2u v = {d.x, d.y};
@@ -340,6 +345,81 @@ __device__ __forceinline__ void compute_y(const ActArgs& aa, const uint4 (&xg)[8
   }
 }
 
+// An FP32 row-major tensor seen from the panel's first row, in the same view type: element (lr, c)
+// at byte ((lr * ld + c) * 4); a lane's 8 consecutive values are two 16-byte loads.
+__device__ __forceinline__ Bf16View f32_view(const float* p, int64_t ld, int64_t row0, int64_t rows,
+                                             int lr0, int64_t col) {
+  Bf16View v;
+  v.r = view(p, row0 * ld * 4, rows * ld * 4);
+  v.ld2 = (uint32_t)(ld * 4);
+  v.vo = ((uint32_t)lr0 * (uint32_t)ld + (uint32_t)col) * 4u;
+  return v;
+}
+
+__device__ __forceinline__ void load_row8_f32(const Bf16View& xv, uint32_t vo, uint32_t so, float (&v)[8]) {
+  const uint4 a = bld16(xv.r, vo, so);
+  const uint4 b = bld16(xv.r, vo == MASKED ? MASKED : vo + 16u, so);
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
+// The lane's 8 x 8 FP32 input tile(s); `up_off` in bytes.
+template <bool GATED>
+__device__ __forceinline__ void load_x32(const Bf16View& xv, uint32_t up_off, int lr0, int nrows,
+                                         bool valid, float (&xg)[8][8], float (&xu)[GATED ? 8 : 1][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool rv = valid && (lr0 + i) < nrows;
+    load_row8_f32(xv, rv ? xv.vo : MASKED, i * xv.ld2, xg[i]);
+    if constexpr (GATED) load_row8_f32(xv, rv ? xv.vo + up_off : MASKED, i * xv.ld2, xu[i]);
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ void compute_y32(const ActArgs& aa, const float (&xg)[8][8],
+                                            const float (&xu)[is_gated<KIND>() ? 8 : 1][8],
+                                            const float (&p)[8], float (&y)[8][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (is_gated<KIND>()) y[i][j] = act_gated<KIND>(xg[i][j], xu[i][j], aa) * p[i];
+      else y[i][j] = act_unary<KIND>(xg[i][j], aa) * p[i];
+    }
+  }
+}
+
+// The input tile and y = a(x) * p of the forward kernels, from a BF16 or (XF32) an FP32 input.  With
+// an FP32 input and `x_copy`, the lane also writes the BF16 (round-to-nearest-even) copy of its tile
+// into x_copy (same shape as x): the copy the backward and the recompute read.
+template <int KIND, bool XF32>
+__device__ __forceinline__ void fwd_tile_y(const ActArgs& aa, const GroupTable& gt, const PanelInfo& pi,
+                                           const void* x, uint16_t* x_copy, int64_t width_in, int64_t wa,
+                                           int lr0, int64_t col, bool valid, const float (&p)[8],
+                                           float (&y)[8][8]) {
+  constexpr bool GATED = is_gated<KIND>();
+  if constexpr (XF32) {
+    const Bf16View xv = f32_view(static_cast<const float*>(x), width_in, pi.row0, gt.total_rows, lr0, col);
+    float xg[8][8], xu[GATED ? 8 : 1][8];
+    load_x32<GATED>(xv, (uint32_t)wa * 4u, lr0, pi.nrows, valid, xg, xu);
+    if (x_copy) {
+      const Bf16View cv = bf16_view(x_copy, width_in, pi.row0, gt.total_rows, lr0, col);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool rv = valid && (lr0 + i) < pi.nrows;
+        bst16(pack8_bf16(xg[i]), cv.r, rv ? cv.vo : MASKED, i * cv.ld2);
+        if constexpr (GATED) bst16(pack8_bf16(xu[i]), cv.r, rv ? cv.vo + (uint32_t)wa * 2u : MASKED, i * cv.ld2);
+      }
+    }
+    compute_y32<KIND>(aa, xg, xu, p, y);
+  } else {
+    const Bf16View xv = bf16_view(static_cast<const uint16_t*>(x), width_in, pi.row0, gt.total_rows, lr0, col);
+    uint4 xg[8], xu[GATED ? 8 : 1];
+    load_x<GATED>(xv, (uint32_t)wa * 2u, lr0, pi.nrows, valid, xg, xu);
+    compute_y<KIND>(aa, xg, xu, p, y);
+  }
+}
+
 // ---------------------------------------------------------------------------------- kernels
 
 __global__ void zero_f32_kernel(float* __restrict__ p, int n) {
@@ -517,13 +597,12 @@ __device__ __forceinline__ void cs_flush(const float* lds, float* __restrict__ p
   }
 }
 
-template <int KIND, int FMT>
+template <int KIND, int FMT, bool XF32>
 __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
-                                                      const uint16_t* __restrict__ x,
+                                                      const void* __restrict__ x,
                                                       const float* __restrict__ probs,
                                                       int64_t width_in, QOut out, float* __restrict__ cs_part,
-                                                      int n_ct) {
-  constexpr bool GATED = is_gated<KIND>();
+                                                      int n_ct, uint16_t* __restrict__ x_copy) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[Stage<FMT>::BYTES];
   __shared__ __attribute__((aligned(16))) float cs_lds[4 * BLOCK_COLS];
   const int64_t wa = out.width;
@@ -535,13 +614,10 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
     write_group_scales(gt, out);
     s_enc = nv_encode_scale(out.amax[pi.g]);
   }
-  const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, bp.lr0, bp.col);
-  uint4 xg[8], xu[GATED ? 8 : 1];
-  load_x<GATED>(xv, (uint32_t)wa * 2u, bp.lr0, pi.nrows, valid, xg, xu);
   float p[8];
   load_probs(probs, pi, gt.total_rows, bp.lr0, p);
   float y[8][8];
-  compute_y<KIND>(aa, xg, xu, p, y);
+  fwd_tile_y<KIND, XF32>(aa, gt, pi, x, x_copy, width_in, wa, bp.lr0, bp.col, valid, p, y);
   if (out.row_data)
     emit_row<FMT>(y, row_dst<FMT>(out, wa, gt.total_rows, pi.row0, bp.lr0, bp.col, bp.lane), bp.lr0, pi.nrows, valid, s_enc);
   if (cs_part) {
@@ -838,9 +914,9 @@ __global__ __launch_bounds__(256) void col_sum_kernel(GroupTable gt, int64_t wid
 // over the wave, LDS over the four waves) and adds one unsigned atomic max of the FP32 bits to its
 // group's entry: far fewer atomics on the per-group array (one cache line for all groups) than one
 // per wave.  BWD: the value is dx = (da/dg * dy) * p (both halves for gated kinds); else y = a * p.
-template <int KIND, bool BWD>
+template <int KIND, bool BWD, bool XF32>
 __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable gt,
-                                                         const uint16_t* __restrict__ x,
+                                                         const void* __restrict__ xp,
                                                          const uint16_t* __restrict__ dy,
                                                          const float* __restrict__ probs,
                                                          int64_t width_in, int64_t wa, int n_chunks,
@@ -857,10 +933,11 @@ __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable 
   for (int c = bp.ct * cpw; c < c_end; ++c) {
     const int64_t col = (int64_t)c * BLOCK_COLS + 8 * bp.cc;
     const bool valid = col < wa;
-    const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, lr0, col);
-    uint4 xg[8], xu[GATED ? 8 : 1];
-    load_x<GATED>(xv, (uint32_t)wa * 2u, lr0, pi.nrows, valid, xg, xu);
     if constexpr (BWD) {
+      const uint16_t* x = static_cast<const uint16_t*>(xp);
+      const Bf16View xv = bf16_view(x, width_in, pi.row0, gt.total_rows, lr0, col);
+      uint4 xg[8], xu[GATED ? 8 : 1];
+      load_x<GATED>(xv, (uint32_t)wa * 2u, lr0, pi.nrows, valid, xg, xu);
       const Bf16View dyv = bf16_view(dy, wa, pi.row0, gt.total_rows, lr0, col);
       uint4 dyt[8];
 #pragma unroll
@@ -886,7 +963,7 @@ __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable 
       }
     } else {
       float y[8][8];
-      compute_y<KIND>(aa, xg, xu, p, y);
+      fwd_tile_y<KIND, XF32>(aa, gt, pi, xp, nullptr, width_in, wa, lr0, col, valid, p, y);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -913,40 +990,52 @@ int amax_cpw(const GroupTable& gt, int n_chunks) {
 }
 
 template <int KIND, bool BWD>
-void launch_group_amax(hipStream_t st, const ActArgs& aa, const GroupTable& gt, const uint16_t* x,
+void launch_group_amax(hipStream_t st, const ActArgs& aa, const GroupTable& gt, const void* x, bool x_f32,
                        const uint16_t* dy, const float* probs, int64_t width_in, int64_t wa,
                        float* amax) {
   const int n_chunks = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
   const int cpw = amax_cpw(gt, n_chunks);
   const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * ((n_chunks + cpw - 1) / cpw)));
-  hipLaunchKernelGGL((group_amax_kernel<KIND, BWD>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa,
-                     n_chunks, cpw, amax);
+  if (!BWD && x_f32)
+    hipLaunchKernelGGL((group_amax_kernel<KIND, false, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
+                       width_in, wa, n_chunks, cpw, amax);
+  else
+    hipLaunchKernelGGL((group_amax_kernel<KIND, BWD, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
+                       width_in, wa, n_chunks, cpw, amax);
 }
 
 template <bool BWD>
 void group_amax_dispatch(int kind, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
-                         const uint16_t* x, const uint16_t* dy, const float* probs, int64_t width_in,
-                         int64_t wa, float* amax) {
+                         const void* x, bool x_f32, const uint16_t* dy, const float* probs,
+                         int64_t width_in, int64_t wa, float* amax) {
   switch (kind) {
-    case MGS_ACT_IDENTITY: launch_group_amax<MGS_ACT_IDENTITY, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_SRELU: launch_group_amax<MGS_ACT_SRELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_TANH_SRELU: launch_group_amax<MGS_ACT_TANH_SRELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_SWIGLU: launch_group_amax<MGS_ACT_SWIGLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_GELU: launch_group_amax<MGS_ACT_GELU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_SIGMOID: launch_group_amax<MGS_ACT_SIGMOID, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_GLU: launch_group_amax<MGS_ACT_GLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
-    default: launch_group_amax<MGS_ACT_CLAMPED_SWIGLU, BWD>(st, aa, gt, x, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_IDENTITY: launch_group_amax<MGS_ACT_IDENTITY, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_SRELU: launch_group_amax<MGS_ACT_SRELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_TANH_SRELU: launch_group_amax<MGS_ACT_TANH_SRELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_SWIGLU: launch_group_amax<MGS_ACT_SWIGLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_GELU: launch_group_amax<MGS_ACT_GELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_SIGMOID: launch_group_amax<MGS_ACT_SIGMOID, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_GLU: launch_group_amax<MGS_ACT_GLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    default: launch_group_amax<MGS_ACT_CLAMPED_SWIGLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
   }
 }
 
-template <int KIND>
+template <int KIND, bool XF32>
 void fwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
-                      const uint16_t* x, const float* probs, int64_t width_in, const QOut& out,
-                      float* cs_part, int n_ct) {
+                      const void* x, const float* probs, int64_t width_in, const QOut& out,
+                      float* cs_part, int n_ct, uint16_t* x_copy) {
   if (fmt == MGS_FMT_MXFP8)
-    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct);
+    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8, XF32>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
   else
-    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct);
+    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_NVFP4, XF32>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+}
+
+template <int KIND>
+void fwd_dispatch(int fmt, bool x_f32, dim3 grid, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
+                  const void* x, const float* probs, int64_t width_in, const QOut& out, float* cs_part,
+                  int n_ct, uint16_t* x_copy) {
+  if (x_f32) fwd_dispatch_fmt<KIND, true>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+  else fwd_dispatch_fmt<KIND, false>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, nullptr);
 }
 
 template <int KIND>
@@ -970,8 +1059,8 @@ ActArgs to_args(const ActHost& a) { return ActArgs{a.kind, a.s, a.inv_s, a.limit
 }  // namespace
 
 hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
-                          const uint16_t* x, const float* probs, QOut out, float* group_amax,
-                          float* col_sum, float* cs_part, hipStream_t st) {
+                          const void* x, bool x_f32, const float* probs, QOut out, float* group_amax,
+                          float* col_sum, float* cs_part, uint16_t* x_copy, hipStream_t st) {
   if (gt.num_panels == 0) {
     // every group is empty: its column sums are zeros
     if (col_sum) launch_col_sum_reduce(gt, out.width, cs_part, col_sum, st);
@@ -986,18 +1075,18 @@ hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int
   if (!out.row_data && !out.col_data) fmt = MGS_FMT_MXFP8;
   if (fmt == MGS_FMT_NVFP4) {
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, group_amax, gt.num_groups);
-    group_amax_dispatch<false>(act.kind, st, aa, gt, x, nullptr, probs, width_in, wa, group_amax);
+    group_amax_dispatch<false>(act.kind, st, aa, gt, x, x_f32, nullptr, probs, width_in, wa, group_amax);
     out.amax = group_amax;
   }
   switch (act.kind) {
-    case MGS_ACT_IDENTITY: fwd_dispatch_fmt<MGS_ACT_IDENTITY>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
-    case MGS_ACT_SRELU: fwd_dispatch_fmt<MGS_ACT_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
-    case MGS_ACT_TANH_SRELU: fwd_dispatch_fmt<MGS_ACT_TANH_SRELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
-    case MGS_ACT_SWIGLU: fwd_dispatch_fmt<MGS_ACT_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
-    case MGS_ACT_GELU: fwd_dispatch_fmt<MGS_ACT_GELU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
-    case MGS_ACT_SIGMOID: fwd_dispatch_fmt<MGS_ACT_SIGMOID>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
-    case MGS_ACT_GLU: fwd_dispatch_fmt<MGS_ACT_GLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
-    default: fwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct); break;
+    case MGS_ACT_IDENTITY: fwd_dispatch<MGS_ACT_IDENTITY>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
+    case MGS_ACT_SRELU: fwd_dispatch<MGS_ACT_SRELU>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
+    case MGS_ACT_TANH_SRELU: fwd_dispatch<MGS_ACT_TANH_SRELU>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
+    case MGS_ACT_SWIGLU: fwd_dispatch<MGS_ACT_SWIGLU>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
+    case MGS_ACT_GELU: fwd_dispatch<MGS_ACT_GELU>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
+    case MGS_ACT_SIGMOID: fwd_dispatch<MGS_ACT_SIGMOID>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
+    case MGS_ACT_GLU: fwd_dispatch<MGS_ACT_GLU>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
+    default: fwd_dispatch<MGS_ACT_CLAMPED_SWIGLU>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
   }
   if (col_sum) launch_col_sum_reduce(gt, wa, cs_part, col_sum, st);
   return hipGetLastError();
@@ -1020,7 +1109,7 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
   const bool quant_dx = dxq.row_data || dxq.col_data;
   if (fmt == MGS_FMT_NVFP4 && quant_dx) {
     hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, dx_amax, gt.num_groups);
-    group_amax_dispatch<true>(act.kind, st, aa, gt, x, dy, probs, width_in, wa, dx_amax);
+    group_amax_dispatch<true>(act.kind, st, aa, gt, x, false, dy, probs, width_in, wa, dx_amax);
     dxq.amax = dx_amax;
   }
   const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);

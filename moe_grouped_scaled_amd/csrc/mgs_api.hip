@@ -181,8 +181,38 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
   if (fmt == MGS_FMT_NVFP4 && !group_amax)
     return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
   const mgs::QOut q = make_qout(out_row, out_col, wa);
-  return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
-                                        probs, q, group_amax, nullptr, nullptr,
+  return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width_in, x_bf16, false, probs, q, group_amax,
+                                        nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int mgs_grouped_scaled_act_fwd_f32(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                                   int64_t width_in, const float* x_f32, const float* probs,
+                                   const mgs_qbuf* out_row, const mgs_qbuf* out_col, float* group_amax,
+                                   void* x_bf16_out, void* stream) {
+  mgs::ActHost ah;
+  int rc = check_act(act, &ah);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
+  const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
+  if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
+  if ((rc = check_extent(gt, wa, "width"))) return rc;
+  if ((int64_t)mgs::PANEL_ROWS * width_in * 4 >= ((int64_t)1 << 31))
+    return fail(MGS_ERR_SHAPE, "width_in %lld too large for the FP32 input", (long long)width_in);
+  if (!x_f32 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_f32 is NULL");
+  if (!qbuf_requested(out_row) && !qbuf_requested(out_col) && !x_bf16_out)
+    return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row, out_col and x_bf16_out are all empty)");
+  if ((rc = check_qbuf(out_row, fmt, "out_row"))) return rc;
+  if ((rc = check_qbuf(out_col, fmt, "out_col"))) return rc;
+  const bool quant = qbuf_requested(out_row) || qbuf_requested(out_col);
+  if (fmt == MGS_FMT_NVFP4 && quant && !group_amax)
+    return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
+  const mgs::QOut q = make_qout(out_row, out_col, wa);
+  return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width_in, x_f32, true, probs, q, group_amax,
+                                        nullptr, nullptr, static_cast<uint16_t*>(x_bf16_out),
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -277,8 +307,8 @@ int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width
   ah.s = ah.inv_s = ah.limit = ah.alpha = 1.0f;
   ah.beta = 0.0f;
   const mgs::QOut q = make_qout(out_row, out_col, width);
-  return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width, static_cast<const uint16_t*>(x_bf16),
-                                        nullptr, q, group_amax, col_sum, static_cast<float*>(workspace),
+  return hip_status(mgs::launch_act_fwd(ah, fmt, gt, width, x_bf16, false, nullptr, q, group_amax, col_sum,
+                                        static_cast<float*>(workspace), nullptr,
                                         static_cast<hipStream_t>(stream)));
 }
 

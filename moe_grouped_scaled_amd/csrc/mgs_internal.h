@@ -72,11 +72,12 @@ struct GemmArgs {
 
 // ---- launchers (return hipGetLastError() after the launches) ----
 
+// x: BF16, or FP32 when x_f32 (then x_copy, nullable, receives its BF16 rounding, same shape).
 // col_sum (nullable): per-group column sums of the output values [E x W_a]; cs_part: workspace of
 // col_sum_part_bytes(gt, W_a) bytes for the per-block partial sums (used when col_sum is requested).
 hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int64_t width_in,
-                          const uint16_t* x, const float* probs, QOut out, float* group_amax,
-                          float* col_sum, float* cs_part, hipStream_t stream);
+                          const void* x, bool x_f32, const float* probs, QOut out, float* group_amax,
+                          float* col_sum, float* cs_part, uint16_t* x_copy, hipStream_t stream);
 
 // workspace: act_bwd_workspace_bytes(gt, activation width, width_in) bytes, used when dprobs or
 // dx_col_sum is requested: per-row partial sums of dprobs per 128-column tile at offset 0, then (at

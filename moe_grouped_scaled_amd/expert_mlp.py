@@ -10,6 +10,12 @@ Sources:
     weight-gradient state.  Here every gradient is requested separately (`grad_x1`, `grad_probs`,
     `grad_fc1`, `grad_fc2`); an unrequested one is a NULL output of the fused launches, and the
     quantized copies only it would consume are neither made nor kept.
+  * same page ("[PyTorch] Enable fused activation recompute ...", Description and review discussion):
+    the fused forward activates FC1's FP32 accumulator, the backward and the recompute its saved BF16
+    rounding.  `fc1_fp32_act=True` does the same here: FC1 writes FP32, one fused launch activates and
+    quantizes it and writes the BF16 copy the backward keeps; the regenerated FC2 input then differs
+    from the forward's by the BF16 rounding, and so does FC2's weight gradient with recompute on.
+    With the default (False) both passes activate the BF16 FC1 output and the twins are bitwise equal.
   * page "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU", Description: with
     activation recompute the forward keeps only the BF16 FC1 output and the backward regenerates FC2's
     input from it; forward, dgrad, dprobs and FC1 wgrad are unchanged; memory drops between forward and
@@ -32,7 +38,7 @@ GATED = ("swiglu", "clamped_swiglu", "glu")
 class ExpertMLP:
     def __init__(self, kind, fmt, w1, w2, b1=None, b2=None, recompute=False, delay_wgrad=False,
                  s=2.0, limit=7.0, alpha=1.0, beta=0.0, grad_x1=True, grad_probs=True, grad_fc1=True,
-                 grad_fc2=True):
+                 grad_fc2=True, fc1_fp32_act=False):
         self.kind, self.fmt = kind, fmt
         self.w1, self.w2, self.b1, self.b2 = w1, w2, b1, b2
         self.e, self.f_in, self.h = w1.shape
@@ -40,6 +46,7 @@ class ExpertMLP:
         assert w2.shape == (self.e, self.h, self.f)
         assert self.f_in == (2 * self.f if kind in GATED else self.f)
         self.recompute, self.delay_wgrad = recompute, delay_wgrad
+        self.fc1_fp32_act = fc1_fp32_act
         # which gradients the backward produces (parameters of FC1 / FC2 = weight and bias)
         self.grad_x1, self.grad_probs = grad_x1, grad_probs
         self.grad_fc1, self.grad_fc2 = grad_fc1, grad_fc2
@@ -73,12 +80,20 @@ class ExpertMLP:
         w1_row, w1_col = self._quant(self.w1.view(e * f_in, h), wsplit1, h,  # fprop / dgrad copies
                                      col=self.grad_x1)
         y1 = torch.empty((m, f_in), dtype=torch.bfloat16, device="cuda")
-        N.grouped_gemm_mx("fprop", fmt, splits, m, f_in, h, x1_row, w1_row, y1, bias=self.b1)
-        del x1_row, w1_row
         a_row = N.QTensor(fmt, False, splits, f)
         a_col = None if (self.recompute or not self.grad_fc2) else N.QTensor(fmt, True, splits, f)
         a_amax = self._amax_buf(e)
-        N.grouped_scaled_act_fwd(self.act, fmt, splits, f_in, y1, probs, a_row, a_col, a_amax)
+        if self.fc1_fp32_act:
+            y1_f32 = torch.empty((m, f_in), dtype=torch.float32, device="cuda")
+            N.grouped_gemm_mx("fprop", fmt, splits, m, f_in, h, x1_row, w1_row, y1_f32, bias=self.b1)
+            del x1_row, w1_row
+            N.grouped_scaled_act_fwd_f32(self.act, fmt, splits, f_in, y1_f32, probs, a_row, a_col, a_amax,
+                                         x_bf16_out=y1)
+            del y1_f32
+        else:
+            N.grouped_gemm_mx("fprop", fmt, splits, m, f_in, h, x1_row, w1_row, y1, bias=self.b1)
+            del x1_row, w1_row
+            N.grouped_scaled_act_fwd(self.act, fmt, splits, f_in, y1, probs, a_row, a_col, a_amax)
         self.trace["fwd_act_col"] += a_col is not None
         w2_row, w2_col = self._quant(self.w2.view(e * h, f), wsplit2, f, col=self.grad_below_fc2)
         y2 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")

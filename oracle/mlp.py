@@ -16,9 +16,13 @@ Step, in order (each GEMM as in oracle.gemm, each quantization as in oracle.quan
             dY1 -> bf16 dense, q(row, col); dX1 = bf16(dY1 W1_g)
   wgrad   : dW2_g = dY2_g^T A_g ; dW1_g = dY1_g^T X1_g (both from the columnwise copies, FP32)
             db2_g = sum over the group's rows of dY2 ; db1_g = sum of the dense BF16 dY1.
-The recompute variant computes the same values (recompute only changes what is kept between forward
-and backward), so the oracle has one step function; the memory drop is a closed form, see
-``recompute_memory_drop``.
+With act_input="bf16" (default) the recompute variant computes the same values (recompute only
+changes what is kept between forward and backward); the memory drop is a closed form, see
+``recompute_memory_drop``.  With act_input="fp32" the forward activates the FP32 FC1 output
+f32(X1 W1_g^T + b1_g) instead of its BF16 rounding ([P1] Description and review discussion: the fused
+forward reads the FP32 accumulator, the backward the saved BF16 output); the backward still reads
+Y1 = bf16(...), and with recompute FC2's columnwise input is regenerated from Y1 (NVFP4: under the
+forward's group amax), so FC2's weight gradient alone differs between the recompute twins.
 
 Parity: composed from the pinned pieces; end-to-end values are compared with relative-RMS bounds.
 """
@@ -53,7 +57,8 @@ def _q(x, splits, fmt, width, row=True, col=True):
     return out
 
 
-def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None):
+def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None, act_input="bf16",
+             recompute=False):
     """All inputs are float64 arrays holding BF16 (x1, w1, b1, w2, b2, dy2) or FP32 (p) values.
 
     Shapes: x1 [M, H]; w1 [E, F_in, H]; b1 [E, F_in]; w2 [E, H, F]; b2 [E, H]; p [M]; dy2 [M, H].
@@ -71,10 +76,22 @@ def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None):
     qw1 = _q(w1.reshape(e * f_in, h), wsplit_1, fmt, h)
     w1_row = qw1["row"].reshape(e, f_in, h)
     w1_col = dgrad_weight(qw1["col"], f_in)  # per expert [H x F_in]
-    y1 = _bf16(gemm_grouped_m(qx1["row"], list(w1_row), splits, bias=b1))
+    y1_acc = gemm_grouped_m(qx1["row"], list(w1_row), splits, bias=b1)
+    y1 = _bf16(y1_acc)
 
-    a32 = act_mod.scaled_act_fwd(kind, y1, p, **act_params)
+    if act_input == "fp32":
+        a32 = act_mod.scaled_act_fwd(kind, f32(y1_acc), p, **act_params)
+    else:
+        assert act_input == "bf16", act_input
+        a32 = act_mod.scaled_act_fwd(kind, y1, p, **act_params)
     qa = _q(a32, splits, fmt, f)
+    if recompute and act_input == "fp32":
+        # FC2's columnwise input regenerated from the saved BF16 Y1 (the forward's only rowwise)
+        a_rec = act_mod.scaled_act_fwd(kind, y1, p, **act_params)
+        amax = qa["raw"].get("group_amax")
+        q_rec = quantize_grouped(a_rec, splits, fmt, rowwise=False, colwise=True, group_amax=amax)
+        qa["col"] = dequant_col_grouped(fmt, q_rec["col_data"], q_rec["col_scales"], splits, f,
+                                        q_rec.get("group_scale"))
     qw2 = _q(w2.reshape(e * h, f), wsplit_2, fmt, f)
     w2_row = qw2["row"].reshape(e, h, f)
     w2_col = dgrad_weight(qw2["col"], h)     # per expert [F x H]

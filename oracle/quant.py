@@ -163,11 +163,14 @@ def nvfp4_quantize_rows(y32, s_enc):
 
 # ----------------------------------------------------------------------------- grouped
 
-def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True):
+def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True, group_amax=None):
     """Grouped quantization of a [M, W] float32 tensor (float64 array of float32 values).
 
     Returns a dict with (as requested) 'row_data', 'row_scales', 'col_data', 'col_scales' (flat uint8
     buffers in the documented layouts), and for NVFP4 'group_amax' and 'group_scale' (float32 [E]).
+    NVFP4 with `group_amax` given takes the per-tensor scales from it instead of from y: the recompute
+    requantizes with the amax its forward saved ([P1] Description: recompute regenerates FC2's input
+    under the forward's quantization state).
     """
     y = np.asarray(y32, dtype=np.float64)
     m_total, w = y.shape
@@ -182,6 +185,8 @@ def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True):
         for g in range(e):
             sl = y[off[g]:off[g + 1]]
             amax[g] = np.max(np.abs(sl)) if sl.size else 0.0
+        if group_amax is not None:
+            amax = np.asarray(group_amax, dtype=np.float64)
         pairs = [nvfp4_global(a) for a in amax]
         s_enc = np.array([p[0] for p in pairs])
         out["group_amax"] = f32(amax)

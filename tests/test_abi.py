@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_symbols():
         assert hasattr(lib, name), name
     assert set(_native.EXPORTED) == set(_declared_symbols())
-    assert _native.abi_version() == 3
+    assert _native.abi_version() == 4
 
 
 def test_qtensor_nbytes_layouts():

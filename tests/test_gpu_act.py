@@ -162,6 +162,53 @@ def test_act_fwd_parity(N, kind, fmt, splits, width_in, std):
     check_fwd(fmt, kind, got, ref, splits, A.out_width(kind, width_in), kind in EXACT_KINDS)
 
 
+F32_CASES = [
+    # (kind, fmt, splits, width_in, x std): FP32 inputs that are not BF16 values
+    ("srelu", "mxfp8", [64, 128, 32, 32], 512, 1.0),
+    ("srelu", "mxfp8", [0, 1, 31, 33, 64], 96, 1.0),
+    ("tanh_srelu", "mxfp8", [40, 0, 300], 1024, 1.5),
+    ("tanh_srelu", "nvfp4", [512, 512, 512, 512], 1024, 1.5),
+    ("srelu", "nvfp4", [0, 1, 31, 33, 64], 64, 1.5),
+    ("swiglu", "mxfp8", [100, 0, 333, 591], 4096, 1.0),
+    ("clamped_swiglu", "nvfp4", [64, 100], 512, 3.0),
+    ("gelu", "mxfp8", [37, 0, 200, 91], 1024, 1.5),
+]
+
+
+@pytest.mark.parametrize("kind,fmt,splits,width_in,std", F32_CASES)
+def test_act_fwd_f32_input_parity(N, kind, fmt, splits, width_in, std):
+    """The forward from an FP32 FC1 output: quantized y against the oracle on the same FP32 values
+    (x*x is no longer exact in FP32, so even SReLU is held to the tolerance criterion), and the BF16
+    copy it writes bit-exact against round-to-nearest-even."""
+    import torch
+    from oracle.codecs import f32_to_bf16_bits
+    rng = np.random.default_rng(21)
+    m = int(np.sum(splits))
+    x = (rng.standard_normal((m, width_in)) * std).astype(np.float32)
+    p = workloads.uniform_f32(rng, m)
+    wa = A.out_width(kind, width_in)
+    qr, qc = N.QTensor(fmt, False, splits, wa), N.QTensor(fmt, True, splits, wa)
+    amax = torch.empty(len(splits), dtype=torch.float32, device="cuda") if fmt == "nvfp4" else None
+    xb = torch.full((m, width_in), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    N.grouped_scaled_act_fwd_f32(N.act_params(kind, **_params(kind)), fmt, splits, width_in, to_dev(x),
+                                 to_dev(p), qr, qc, amax, x_bf16_out=xb)
+    torch.cuda.synchronize()
+    got = {"row_data": u8(qr.data), "row_scales": u8(qr.scales), "col_data": u8(qc.data),
+           "col_scales": u8(qc.scales)}
+    if fmt == "nvfp4":
+        got.update(row_gs=f32(qr.group_scale), col_gs=f32(qc.group_scale), amax=f32(amax))
+    y = A.scaled_act_fwd(kind, x.astype(np.float64), p.astype(np.float64), **_params(kind))
+    ref = Q.quantize_grouped(y, splits, fmt)
+    check_fwd(fmt, kind, got, ref, splits, wa, False)
+    assert np.array_equal(bf16_host(xb), f32_to_bf16_bits(x)), "BF16 copy differs"
+    # the BF16 copy alone (no quantized output requested)
+    xb2 = torch.zeros_like(xb)
+    N.grouped_scaled_act_fwd_f32(N.act_params(kind, **_params(kind)), fmt, splits, width_in, to_dev(x),
+                                 to_dev(p), None, None, None, x_bf16_out=xb2)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(xb2), bf16_host(xb))
+
+
 def test_act_fwd_swiglu_zipf_full_size(N):
     """The Zipf-split SwiGLU workload at full size: 8 experts, 8192 tokens, FC1 out 2 x 2048."""
     d = workloads.make("swiglu_zipf")
