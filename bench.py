@@ -76,7 +76,7 @@ class Timer:
         self.enabled = False
         self._orig = {}
         for name in ("grouped_scaled_act_fwd", "grouped_scaled_act_fwd_f32", "grouped_scaled_act_bwd",
-                     "grouped_mx_quantize", "grouped_gemm_mx"):
+                     "grouped_mx_quantize", "grouped_gemm_mx", "grouped_gemm_mx_fprop_act"):
             self._wrap(name)
 
     def _wrap(self, name):
@@ -91,7 +91,7 @@ class Timer:
             s.record()
             r = orig(*a, **kw)
             e.record()
-            tag = name if name != "grouped_gemm_mx" else "gemm_" + a[0]
+            tag = "gemm_" + a[0] if name == "grouped_gemm_mx" else name
             self.records.append((tag, s, e))
             return r
 
@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--fc1-fp32-act", action="store_true",
                     help="activate FC1's FP32 output in the forward (the recompute then regenerates FC2's "
                          "input from its BF16 copy)")
+    ap.add_argument("--fc1-act", default="separate", choices=["epilogue", "separate"],
+                    help="run the forward activation + quantization in FC1's GEMM epilogue (MXFP8, unary "
+                         "activations) or as its own fused pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -206,7 +209,7 @@ def main():
     held = {}
     for rc in (False, True):
         mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=rc, delay_wgrad=True, s=2.0,
-                        fc1_fp32_act=args.fc1_fp32_act)
+                        fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue")
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         y = mlp.forward(x1, p, splits)
@@ -219,7 +222,7 @@ def main():
     drop_closed = col_rows * f + col_rows * f // 32 if args.fmt == "mxfp8" else col_rows * f // 2 + col_rows * f // 16
 
     mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=True, delay_wgrad=True, s=2.0,
-                    fc1_fp32_act=args.fc1_fp32_act)
+                    fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue")
 
     def step():
         mlp.forward(x1, p, splits)
@@ -237,6 +240,29 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timer.enabled = False
+    fused_fc1 = mlp.fused_fc1_calls > 0
+    if fused_fc1:
+        # the step ran the forward activation inside FC1's epilogue; time the separate fused pass on
+        # the same FC1 output on its own, for its GB/s (not part of the step time)
+        y1 = torch.empty((m, f), dtype=torch.bfloat16, device="cuda")
+        qx, qw = N.QTensor(args.fmt, False, splits, h), N.QTensor(args.fmt, False, [f] * e, h)
+        N.grouped_mx_quantize(args.fmt, splits, h, x1, qx)
+        N.grouped_mx_quantize(args.fmt, [f] * e, h, w1.view(e * f, h), qw)
+        ya = N.QTensor(args.fmt, False, splits, f)
+        if args.fc1_fp32_act:
+            y1f = torch.empty((m, f), dtype=torch.float32, device="cuda")
+            N.grouped_gemm_mx("fprop", args.fmt, splits, m, f, h, qx, qw, y1f, bias=b1)
+            run_fwd = lambda: N.grouped_scaled_act_fwd_f32(mlp.act, args.fmt, splits, f, y1f, p, ya, x_bf16_out=y1)
+        else:
+            N.grouped_gemm_mx("fprop", args.fmt, splits, m, f, h, qx, qw, y1, bias=b1)
+            run_fwd = lambda: N.grouped_scaled_act_fwd(mlp.act, args.fmt, splits, f, y1, p, ya)
+        run_fwd()
+        torch.cuda.synchronize()
+        timer.enabled = True
+        for _ in range(args.steps):
+            run_fwd()
+        torch.cuda.synchronize()
+        timer.enabled = False
     dur = timer.durations()
 
     ms_per_step = wall / args.steps * 1e3
@@ -264,7 +290,8 @@ def main():
     t_bwd = float(np.mean(dur["grouped_scaled_act_bwd"]))
     kernels = {
         "act_fwd": {"GB/s": fwd_b / t_fwd / 1e9, "frac_hbm": fwd_b / t_fwd / 1e9 / HBM_PEAK_GBPS,
-                    "us": t_fwd * 1e6, "bytes": fwd_b},
+                    "us": t_fwd * 1e6, "bytes": fwd_b,
+                    "in_step": "no: FC1's epilogue ran it; timed alone on the same data" if fused_fc1 else "yes"},
         "act_bwd": {"GB/s": bwd_b / t_bwd / 1e9, "frac_hbm": bwd_b / t_bwd / 1e9 / HBM_PEAK_GBPS,
                     "us": t_bwd * 1e6, "bytes": bwd_b},
         "gemm": {"TFLOP/s": gemm_tflops, "frac_mfma": gemm_tflops / peak, "us_avg": gemm_avg * 1e6,
@@ -274,15 +301,19 @@ def main():
         # gradient in the same pass)
         "mx_quantize_us": float(np.mean(dur["grouped_mx_quantize"])) * 1e6,
     }
+    if fused_fc1:
+        kernels["gemm_fprop_act_us"] = float(np.mean(dur["grouped_gemm_mx_fprop_act"])) * 1e6
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8" if args.fmt == "mxfp8" else "fp4", "data": "synthetic",
         "config": {"workload": "expert-MLP train step: 16 experts x 2048 tokens, hidden 4096, ffn 4096, "
-                               "%s, %s, bias, recompute on, delayed wgrad%s" % (
-                                   args.act, args.fmt.upper(), ", FP32 FC1 output activated" if args.fc1_fp32_act else ""),
+                               "%s, %s, bias, recompute on, delayed wgrad%s%s" % (
+                                   args.act, args.fmt.upper(), ", FP32 FC1 output activated" if args.fc1_fp32_act else "",
+                                   ", activation in FC1's epilogue" if fused_fc1 else ""),
                    "experts": e, "tokens": m, "hidden": h, "ffn": f, "recipe": args.fmt, "act": args.act,
-                   "act_input": "fp32" if args.fc1_fp32_act else "bf16"},
+                   "act_input": "fp32" if args.fc1_fp32_act else "bf16",
+                   "fc1_act": "epilogue" if fused_fc1 else "separate"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": gemm_tflops / peak, "traffic": measured_traffic(args.fmt)},
         "kernels": kernels,

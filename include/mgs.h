@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MGS_ABI_VERSION 4
+#define MGS_ABI_VERSION 5
 #define MGS_MAX_GROUPS 256
 
 enum mgs_status {
@@ -239,6 +239,25 @@ int64_t mgs_grouped_mx_quantize_workspace_bytes(const mgs_groups* groups, int64_
 int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int64_t m, int64_t n,
                         int64_t k, const mgs_qbuf* a, const mgs_qbuf* b, void* c, int32_t c_dtype,
                         const void* bias_bf16, int32_t accumulate, void* stream);
+
+/* FC1's forward GEMM with the scaled activation and MXFP8 rowwise quantization in its epilogue.
+ * [P1] Description and review discussion: the fused forward applies the activation to FC1's output
+ * inside the GEMM and hands FC2 its quantized input; [P2] Greptile summary (per-row scale, activation
+ * and grouped quantization in one pass).  An FPROP of mgs_grouped_gemm_mx (same A, B, groups, m, n, k,
+ * bias; MXFP8 only) that also writes
+ *   out_row    rowwise MXFP8 qtensor [M x n] of y = act(c) * probs[row], required: the bytes
+ *              mgs_grouped_scaled_act_fwd (act_input BF16) or mgs_grouped_scaled_act_fwd_f32
+ *              (act_input F32) writes for out_row from this C, bit for bit
+ *   c_bf16     [M x n] BF16 FC1 output, required (the tensor the backward and the recompute read)
+ *   act        unary kinds only (IDENTITY, SRELU, TANH_SRELU, GELU, SIGMOID); gated kinds return
+ *              MGS_ERR_UNSUPPORTED (their two halves lie in different output tiles)
+ *   probs      [M] FP32 per-row scale; NULL means 1
+ *   act_input  MGS_DTYPE_F32: activate the FP32 value c = A.B^T + bias; MGS_DTYPE_BF16: its BF16 rounding
+ * No columnwise copy: the recompute forward needs none; callers wanting one use the separate forward. */
+int mgs_grouped_gemm_mx_fprop_act(const mgs_groups* groups, int64_t m, int64_t n, int64_t k,
+                                  const mgs_qbuf* a, const mgs_qbuf* b, void* c_bf16,
+                                  const void* bias_bf16, const mgs_act_params* act, const float* probs,
+                                  int32_t act_input, const mgs_qbuf* out_row, void* stream);
 
 /* Per-group column sums (bias gradient): out[g, j] = sum over group g's rows of x[r, j], FP32,
  * fixed summation order.  [P1] Description, second paragraph: bias changes what wgrad consumes.

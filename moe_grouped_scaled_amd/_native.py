@@ -67,6 +67,8 @@ def _load():
         "mgs_grouped_mx_quantize_workspace_bytes": (i64, [pgr, i64]),
         "mgs_grouped_gemm_mx": (ctypes.c_int, [i32, i32, pgr, i64, i64, i64, pq, pq, vp, i32, vp, i32,
                                                vp]),
+        "mgs_grouped_gemm_mx_fprop_act": (ctypes.c_int, [pgr, i64, i64, i64, pq, pq, vp, vp, pact, vp, i32,
+                                                         pq, vp]),
         "mgs_grouped_col_sum": (ctypes.c_int, [pgr, i64, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -80,7 +82,8 @@ LIB = _load()
 EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
             "mgs_grouped_scaled_act_fwd_f32",
             "mgs_grouped_scaled_act_bwd", "mgs_act_bwd_workspace_bytes", "mgs_grouped_mx_quantize",
-            "mgs_grouped_mx_quantize_workspace_bytes", "mgs_grouped_gemm_mx", "mgs_grouped_col_sum")
+            "mgs_grouped_mx_quantize_workspace_bytes", "mgs_grouped_gemm_mx", "mgs_grouped_gemm_mx_fprop_act",
+            "mgs_grouped_col_sum")
 
 
 def _check(rc):
@@ -245,6 +248,18 @@ def grouped_gemm_mx(mode, fmt, split_sizes, m, n, k, a, b, c, bias=None, accumul
     _check(LIB.mgs_grouped_gemm_mx(GEMM_MODE[mode], FMT[fmt], g.ref, int(m), int(n), int(k), aref, bref,
                                    _ptr(c), DTYPE[c.dtype], _ptr(bias), int(bool(accumulate)),
                                    _stream(stream)))
+
+
+def grouped_gemm_mx_fprop_act(split_sizes, m, n, k, a, b, c, act, probs, out_row, bias=None,
+                              act_input="bf16", stream=None):
+    """MXFP8 FPROP whose epilogue also writes out_row = MXFP8(act(c) * probs); c is BF16."""
+    g = _GroupsArg(split_sizes)
+    _a, aref = _qref(a)
+    _b, bref = _qref(b)
+    _o, oref = _qref(out_row)
+    _check(LIB.mgs_grouped_gemm_mx_fprop_act(g.ref, int(m), int(n), int(k), aref, bref, _ptr(c), _ptr(bias),
+                                             ctypes.byref(act), _ptr(probs),
+                                             {"bf16": 0, "fp32": 1}[act_input], oref, _stream(stream)))
 
 
 def grouped_col_sum(split_sizes, width, x, out, stream=None):

@@ -287,6 +287,75 @@ __device__ __forceinline__ void mfma_drain() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
 }
 
+// FPROP epilogue with the scaled activation and MXFP8 rowwise quantization of its result (page
+// "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU", Description and review
+// discussion: the fused forward activates FC1's output in the GEMM epilogue and quantizes it for FC2).
+// Per fragment row the lane stores its BF16 values of C as the plain epilogue does, and evaluates
+// y = act(x) * p with x the FP32 value or its BF16 rounding; a 32-column block of a row is held by
+// the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (8 values each, fragment columns 2b and 2b + 1), so the block
+// maximum is two cross-lane steps.  The scale code, the reciprocal power of two and the saturating
+// E4M3 convert are the shared helpers the fused activation kernels use, so the codes equal theirs on
+// the same x bit for bit.  The four scales of the wave's 128 columns (one K step of FC2's operand)
+// go out as one dword per row.
+template <int KIND>
+__device__ __forceinline__ void epilogue_act(const TileJob& j, const GemmArgs& ga, v4f (&acc)[8][8],
+                                             const uint2 (&bw)[8], int wm, int wn, int q, int r16) {
+  const ActArgs aa{ga.act_kind, ga.act_s, ga.act_inv_s, ga.act_limit, ga.act_alpha, ga.act_beta};
+  const int cw = wn * 128;                          // the wave's first column within the tile
+  const int64_t col0 = j.ccol0 + cw;                // ... within C
+  const int64_t srows = j.a.srows;                  // all M rows: the scale matrix's row count
+  const bool wave_cols = cw < j.b.rows;             // the wave's columns reach into C
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm) {
+    const int row = wm * 128 + fm * 16 + r16;
+    const bool rok = row < j.a.rows;
+    const int64_t gr = j.crow0 + row;
+    const float p = !rok ? 0.0f : ga.probs ? ga.probs[gr] : 1.0f;
+    uint32_t sdw = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bool bok = cw + 32 * b < j.b.rows;      // n % 32 == 0: a block is all in or all out
+      float y[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int fn = 2 * b + h;
+        const int col = cw + fn * 16 + 4 * q;
+        float v[4];
+        frag_values(j, acc[fm][fn], bw[fn], v);
+        uint2 w;
+        w.x = bf16x2(v[0], v[1]);
+        w.y = bf16x2(v[2], v[3]);
+        if (rok && bok) *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + j.ccol0 + col) = w;
+        float x[4];
+        if (ga.act_on_bf16) {
+          x[0] = bf16lo(w.x); x[1] = bf16hi(w.x); x[2] = bf16lo(w.y); x[3] = bf16hi(w.y);
+        } else {
+          x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[4 * h + t] = bok ? act_unary<KIND>(x[t], aa) * p : 0.0f;
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(y[t]));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const uint32_t c = mx_scale_code(m);
+      const float inv = mx_inv_scale(c);
+      const uint32_t q0 = e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
+      const uint32_t q1 = e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
+      if (rok && bok) {
+        uint8_t* dst = ga.act_data + gr * ga.n + col0 + 32 * b + 4 * q;
+        *reinterpret_cast<uint32_t*>(dst) = q0;
+        *reinterpret_cast<uint32_t*>(dst + 16) = q1;
+      }
+      sdw |= (bok ? c : 0u) << (8 * b);
+    }
+    if (rok && wave_cols && q == 0)
+      *reinterpret_cast<uint32_t*>(ga.act_scales + ((col0 / 128) * srows + gr) * 4) = sdw;
+  }
+}
+
 // Epilogue of the 256 x 256 kernel: group factor, bias (from LDS), optional FP32 accumulation, store.
 __device__ __forceinline__ void epilogue_256(const TileJob& j, const GemmArgs& ga, v4f (&acc)[8][8],
                                              const uint2* bias_lds, int wm, int wn, int q, int r16) {
@@ -334,9 +403,21 @@ __device__ __forceinline__ void epilogue_256(const TileJob& j, const GemmArgs& g
       }
     }
   };
-  if (!j.c32) epilogue(std::false_type{}, std::false_type{});
-  else if (!ga.accumulate) epilogue(std::true_type{}, std::false_type{});
-  else epilogue(std::true_type{}, std::true_type{});
+  if (ga.act_enabled) {
+    switch (ga.act_kind) {
+      case MGS_ACT_SRELU: epilogue_act<MGS_ACT_SRELU>(j, ga, acc, bw, wm, wn, q, r16); break;
+      case MGS_ACT_TANH_SRELU: epilogue_act<MGS_ACT_TANH_SRELU>(j, ga, acc, bw, wm, wn, q, r16); break;
+      case MGS_ACT_GELU: epilogue_act<MGS_ACT_GELU>(j, ga, acc, bw, wm, wn, q, r16); break;
+      case MGS_ACT_SIGMOID: epilogue_act<MGS_ACT_SIGMOID>(j, ga, acc, bw, wm, wn, q, r16); break;
+      default: epilogue_act<MGS_ACT_IDENTITY>(j, ga, acc, bw, wm, wn, q, r16); break;
+    }
+  } else if (!j.c32) {
+    epilogue(std::false_type{}, std::false_type{});
+  } else if (!ga.accumulate) {
+    epilogue(std::true_type{}, std::false_type{});
+  } else {
+    epilogue(std::true_type{}, std::true_type{});
+  }
 }
 
 // Per-tile state of the direct-to-LDS loads: buffer descriptors of the operands, their scales and the

@@ -370,6 +370,57 @@ int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int
   return hip_status(mgs::launch_gemm(ga, gt, static_cast<hipStream_t>(stream)));
 }
 
+int mgs_grouped_gemm_mx_fprop_act(const mgs_groups* groups, int64_t m, int64_t n, int64_t k,
+                                  const mgs_qbuf* a, const mgs_qbuf* b, void* c_bf16,
+                                  const void* bias_bf16, const mgs_act_params* act, const float* probs,
+                                  int32_t act_input, const mgs_qbuf* out_row, void* stream) {
+  mgs::ActHost ah;
+  int rc = check_act(act, &ah);
+  if (rc) return rc;
+  if (is_gated(ah.kind))
+    return fail(MGS_ERR_UNSUPPORTED, "gated activations need both halves of a row: use the separate forward");
+  if (act_input != MGS_DTYPE_BF16 && act_input != MGS_DTYPE_F32)
+    return fail(MGS_ERR_INVALID_ARG, "unknown act_input %d", act_input);
+  if (!out_row || !out_row->data || !out_row->scales)
+    return fail(MGS_ERR_INVALID_ARG, "out_row (data, scales) is NULL");
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (!a || !a->data || !a->scales) return fail(MGS_ERR_INVALID_ARG, "operand A (data, scales) is NULL");
+  if (!b || !b->data || !b->scales) return fail(MGS_ERR_INVALID_ARG, "operand B (data, scales) is NULL");
+  if (!c_bf16) return fail(MGS_ERR_INVALID_ARG, "c_bf16 is NULL");
+  if ((rc = check_width(n, "n"))) return rc;
+  if ((rc = check_width(k, "k"))) return rc;
+  if (m != rows) return fail(MGS_ERR_SHAPE, "m = %lld must equal the split sum %lld", (long long)m, (long long)rows);
+  mgs::GemmArgs ga{};
+  ga.mode = MGS_GEMM_FPROP;
+  ga.fmt = MGS_FMT_MXFP8;
+  ga.m = m;
+  ga.n = n;
+  ga.k = k;
+  ga.a_data = static_cast<const uint8_t*>(a->data);
+  ga.a_scales = static_cast<const uint8_t*>(a->scales);
+  ga.b_data = static_cast<const uint8_t*>(b->data);
+  ga.b_scales = static_cast<const uint8_t*>(b->scales);
+  ga.c = c_bf16;
+  ga.c_f32 = 0;
+  ga.accumulate = 0;
+  ga.bias = static_cast<const uint16_t*>(bias_bf16);
+  ga.act_enabled = 1;
+  ga.act_kind = ah.kind;
+  ga.act_on_bf16 = act_input == MGS_DTYPE_BF16;
+  ga.act_s = ah.s;
+  ga.act_inv_s = ah.inv_s;
+  ga.act_limit = ah.limit;
+  ga.act_alpha = ah.alpha;
+  ga.act_beta = ah.beta;
+  ga.probs = probs;
+  ga.act_data = static_cast<uint8_t*>(out_row->data);
+  ga.act_scales = static_cast<uint8_t*>(out_row->scales);
+  if (mgs::gemm_tile_count(ga, gt) > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
+  return hip_status(mgs::launch_gemm(ga, gt, static_cast<hipStream_t>(stream)));
+}
+
 int mgs_grouped_col_sum(const mgs_groups* groups, int64_t width, const void* x_bf16, float* out,
                         void* stream) {
   mgs::GroupTable gt;

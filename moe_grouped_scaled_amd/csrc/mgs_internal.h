@@ -68,6 +68,17 @@ struct GemmArgs {
   int c_f32;
   int accumulate;
   const uint16_t* bias;
+  // FPROP epilogue activation (act_enabled == 0, the zero-initialised default: none).  With it the
+  // epilogue also quantizes y = act(c) * probs[row] to MXFP8 rowwise: codes [M x n] at act_data,
+  // scales K-step grouped over n at act_scales; c is the FP32 value (act_on_bf16 == 0) or its BF16
+  // rounding (1).  C is BF16.
+  int act_enabled;
+  int act_kind;
+  int act_on_bf16;
+  float act_s, act_inv_s, act_limit, act_alpha, act_beta;
+  const float* probs;
+  uint8_t* act_data;
+  uint8_t* act_scales;
 };
 
 // ---- launchers (return hipGetLastError() after the launches) ----

@@ -16,6 +16,11 @@ Sources:
     quantizes it and writes the BF16 copy the backward keeps; the regenerated FC2 input then differs
     from the forward's by the BF16 rounding, and so does FC2's weight gradient with recompute on.
     With the default (False) both passes activate the BF16 FC1 output and the twins are bitwise equal.
+  * same page, Description and review discussion: the fused forward runs the activation in FC1's
+    GEMM epilogue.  `fuse_fc1_act=True` does that here for MXFP8 and unary activations when the
+    forward writes no columnwise copy (recompute on, or no FC2 weight gradient): FC1's epilogue stores
+    the BF16 FC1 output and FC2's quantized input in one launch, bit for bit what the separate pass
+    writes from the same values (its FP32 value with `fc1_fp32_act`, else its BF16 rounding).
   * page "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU", Description: with
     activation recompute the forward keeps only the BF16 FC1 output and the backward regenerates FC2's
     input from it; forward, dgrad, dprobs and FC1 wgrad are unchanged; memory drops between forward and
@@ -38,7 +43,7 @@ GATED = ("swiglu", "clamped_swiglu", "glu")
 class ExpertMLP:
     def __init__(self, kind, fmt, w1, w2, b1=None, b2=None, recompute=False, delay_wgrad=False,
                  s=2.0, limit=7.0, alpha=1.0, beta=0.0, grad_x1=True, grad_probs=True, grad_fc1=True,
-                 grad_fc2=True, fc1_fp32_act=False):
+                 grad_fc2=True, fc1_fp32_act=False, fuse_fc1_act=False):
         self.kind, self.fmt = kind, fmt
         self.w1, self.w2, self.b1, self.b2 = w1, w2, b1, b2
         self.e, self.f_in, self.h = w1.shape
@@ -47,6 +52,8 @@ class ExpertMLP:
         assert self.f_in == (2 * self.f if kind in GATED else self.f)
         self.recompute, self.delay_wgrad = recompute, delay_wgrad
         self.fc1_fp32_act = fc1_fp32_act
+        self.fuse_fc1_act = fuse_fc1_act
+        self.fused_fc1_calls = 0  # forwards whose FC1 GEMM ran the activation in its epilogue
         # which gradients the backward produces (parameters of FC1 / FC2 = weight and bias)
         self.grad_x1, self.grad_probs = grad_x1, grad_probs
         self.grad_fc1, self.grad_fc2 = grad_fc1, grad_fc2
@@ -83,7 +90,12 @@ class ExpertMLP:
         a_row = N.QTensor(fmt, False, splits, f)
         a_col = None if (self.recompute or not self.grad_fc2) else N.QTensor(fmt, True, splits, f)
         a_amax = self._amax_buf(e)
-        if self.fc1_fp32_act:
+        if self.fuse_fc1_act and fmt == "mxfp8" and self.kind not in GATED and a_col is None:
+            N.grouped_gemm_mx_fprop_act(splits, m, f_in, h, x1_row, w1_row, y1, self.act, probs, a_row,
+                                        bias=self.b1, act_input="fp32" if self.fc1_fp32_act else "bf16")
+            del x1_row, w1_row
+            self.fused_fc1_calls += 1
+        elif self.fc1_fp32_act:
             y1_f32 = torch.empty((m, f_in), dtype=torch.float32, device="cuda")
             N.grouped_gemm_mx("fprop", fmt, splits, m, f_in, h, x1_row, w1_row, y1_f32, bias=self.b1)
             del x1_row, w1_row

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_symbols():
         assert hasattr(lib, name), name
     assert set(_native.EXPORTED) == set(_declared_symbols())
-    assert _native.abi_version() == 4
+    assert _native.abi_version() == 5
 
 
 def test_qtensor_nbytes_layouts():
@@ -158,6 +158,25 @@ def test_argument_validation_gemm():
     cb = torch.empty(1, dtype=torch.bfloat16)
     _expect(-3, g, "fprop", "mxfp8", [32], 32, 64, 64, q, q, cb, accumulate=True, stream=0)
     _expect(-1, g, "fprop", "nvfp4", [32], 32, 64, 64, _FakeQ(gs=False).q, q, c, stream=0)
+
+
+def test_argument_validation_fprop_act_and_f32_forward():
+    from moe_grouped_scaled_amd import _native as N
+    import torch
+    q = _FakeQ().q
+    cb = torch.empty(1, dtype=torch.bfloat16)
+    g = N.grouped_gemm_mx_fprop_act
+    srelu = N.act_params("srelu")
+    _expect(-3, g, [32], 32, 64, 64, q, q, cb, N.act_params("swiglu"), None, q, stream=0, match="gated")
+    _expect(-1, g, [32], 32, 64, 64, q, q, None, srelu, None, q, stream=0, match="c_bf16")
+    _expect(-1, g, [32], 32, 64, 64, q, q, cb, srelu, None, None, stream=0, match="out_row")
+    _expect(-2, g, [32, 32], 63, 64, 64, q, q, cb, srelu, None, q, stream=0, match="split sum")
+    _expect(-2, g, [32], 32, 48, 64, q, q, cb, srelu, None, q, stream=0, match="multiple of 32")
+    f = N.grouped_scaled_act_fwd_f32
+    x = torch.empty(1, dtype=torch.float32)
+    _expect(-1, f, srelu, "mxfp8", [32], 64, x, None, stream=0, match="no output")
+    _expect(-1, f, srelu, "nvfp4", [32], 64, x, None, q, stream=0, match="group_amax")
+    _expect(-2, f, srelu, "mxfp8", [32], 48, x, None, q, stream=0, match="multiple of 32")
 
 
 def test_last_error_is_cleared_on_success():

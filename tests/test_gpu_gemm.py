@@ -194,3 +194,50 @@ def test_fc2_clamped_workload_sampled(N):
         ref = a_deq @ w_deq.T
         ref_b = bf16_f64(codecs.f32_to_bf16_bits(codecs.f32(ref).astype(np.float32)))
         assert rel_rms(got_c[rows], ref_b) <= TOL, (g, rel_rms(got_c[rows], ref_b))
+
+
+FPROP_ACT_CASES = [(k, a) for k in ("srelu", "tanh_srelu", "gelu", "sigmoid", "identity") for a in ("bf16", "fp32")]
+
+
+@pytest.mark.parametrize("kind,act_input", FPROP_ACT_CASES)
+def test_fprop_act_epilogue_equals_separate_forward(N, kind, act_input):
+    """FC1 FPROP with the activation + MXFP8 rowwise quantization in its epilogue, against the two
+    launches it replaces on the same operands: the plain FPROP (BF16 output, or FP32 output for
+    act_input fp32) followed by the fused forward (BF16 input, or FP32 input writing the BF16 copy).
+    C and the quantized y must agree bit for bit.  Ragged groups (empty, 1, 31, 33 rows), n = 416
+    (the second tile column's second wave holds one 32-column block) and a partial K step."""
+    import torch
+    rng = np.random.default_rng(7)
+    splits = [0, 1, 31, 33, 300, 64]
+    e, m, n, k = len(splits), sum(splits), 416, 288
+    a = _f32_values(rng, (m, k))
+    w = _f32_values(rng, (e * n, k), 0.05)
+    qa = dev_q(N, "mxfp8", False, splits, k, Q.quantize_grouped(a, splits, "mxfp8", colwise=False))
+    qw = dev_q(N, "mxfp8", False, [n] * e, k, Q.quantize_grouped(w, [n] * e, "mxfp8", colwise=False))
+    bias = to_dev_bf16(workloads.normal_bf16(rng, (e, n), 0.5))
+    probs = to_dev(workloads.uniform_f32(rng, m)) if kind != "identity" else None
+    act = N.act_params(kind, s=2.0)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    qy = N.QTensor("mxfp8", False, splits, n)
+    N.grouped_gemm_mx_fprop_act(splits, m, n, k, qa, qw, c, act, probs, qy, bias=bias, act_input=act_input)
+    ref_row = N.QTensor("mxfp8", False, splits, n)
+    if act_input == "bf16":
+        c_ref = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        N.grouped_gemm_mx("fprop", "mxfp8", splits, m, n, k, qa, qw, c_ref, bias=bias)
+        N.grouped_scaled_act_fwd(act, "mxfp8", splits, n, c_ref, probs, ref_row)
+    else:
+        c32 = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        N.grouped_gemm_mx("fprop", "mxfp8", splits, m, n, k, qa, qw, c32, bias=bias)
+        c_ref = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        N.grouped_scaled_act_fwd_f32(act, "mxfp8", splits, n, c32, probs, ref_row, x_bf16_out=c_ref)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(c), bf16_host(c_ref)), "C differs"
+    assert np.array_equal(qy.scales.cpu().numpy(), ref_row.scales.cpu().numpy()), "scales differ"
+    assert np.array_equal(qy.data.cpu().numpy(), ref_row.data.cpu().numpy()), "codes differ"
+    if kind == "srelu" and act_input == "bf16":
+        # and against the oracle on the GPU's C (ScaledSReLU on BF16 input is exact in FP32)
+        from oracle import activations as A
+        y = A.scaled_act_fwd("srelu", bf16_f64(bf16_host(c)), f32(probs))
+        ref = Q.quantize_grouped(y, splits, "mxfp8", colwise=False)
+        assert np.array_equal(qy.data.cpu().numpy(), ref["row_data"])
+        assert np.array_equal(qy.scales.cpu().numpy(), ref["row_scales"])

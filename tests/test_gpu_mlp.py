@@ -32,7 +32,7 @@ def _inputs(kind, e, splits, h, f, seed):
                 dy2=workloads.normal_bf16(rng, (m, h)), splits=np.asarray(splits, np.int64))
 
 
-def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False):
+def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False, fuse_fc1_act=False):
     import torch
     from moe_grouped_scaled_amd.expert_mlp import ExpertMLP
     w1, w2 = to_dev_bf16(d["w1"]), to_dev_bf16(d["w2"])
@@ -40,7 +40,7 @@ def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False):
     b2 = to_dev_bf16(d["b2"]) if bias else None
     x1, p, dy2 = to_dev_bf16(d["x1"]), to_dev(d["p"]), to_dev_bf16(d["dy2"])
     mlp = ExpertMLP(kind, fmt, w1, w2, b1, b2, recompute=recompute, delay_wgrad=delay,
-                    fc1_fp32_act=fc1_fp32_act)
+                    fc1_fp32_act=fc1_fp32_act, fuse_fc1_act=fuse_fc1_act)
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated()
     y2 = mlp.forward(x1, p, list(d["splits"]))
@@ -52,7 +52,8 @@ def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False):
         g.update(mlp.backward_dw())
     torch.cuda.synchronize()
     out = {"y2": bf16_host(y2), "dx1": bf16_host(g["dx1"]), "dprobs": f32(g["dprobs"]),
-           "dw1": f32(g["dw1"]), "dw2": f32(g["dw2"]), "held": held, "trace": dict(mlp.trace)}
+           "dw1": f32(g["dw1"]), "dw2": f32(g["dw2"]), "held": held, "trace": dict(mlp.trace),
+           "fused": mlp.fused_fc1_calls}
     if bias:
         out["db1"], out["db2"] = f32(g["db1"]), f32(g["db2"])
     return out
@@ -186,3 +187,63 @@ def test_partial_gradients_match_full_step(torch_mod, fmt, recompute):
         assert set(got) == want, (flags, sorted(got))
         for k in want:
             assert np.array_equal(got[k], full[k]), (flags, k)   # BF16 bits or FP32 values
+
+
+@pytest.mark.parametrize("kind,fp32_act,size", [("srelu", False, "small"), ("srelu", True, "small"),
+                                               ("tanh_srelu", True, "small"), ("gelu", False, "small"),
+                                               ("srelu", True, "full")])
+def test_fc1_epilogue_act_step_equals_separate_forward(torch_mod, kind, fp32_act, size):
+    """The step with the activation in FC1's epilogue (recompute on) against the step with the
+    separate forward pass: every output bitwise equal; at full size too (16 x 2048 tokens, 4096)."""
+    if size == "full":
+        e, splits, h, f = 16, [2048] * 16, 4096, 4096
+    else:
+        e, splits, h, f = 4, [64, 0, 96, 37], 256, 384
+    d = _inputs(kind, e, splits, h, f, seed=9)
+    a = _run_gpu(kind, "mxfp8", d, recompute=True, delay=True, fc1_fp32_act=fp32_act, fuse_fc1_act=True)
+    b = _run_gpu(kind, "mxfp8", d, recompute=True, delay=True, fc1_fp32_act=fp32_act, fuse_fc1_act=False)
+    assert a["fused"] == 1 and b["fused"] == 0
+    for k in ("y2", "dx1", "dprobs", "dw1", "dw2", "db1", "db2"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["held"] == b["held"]
+
+
+def test_step_graph_replay_equals_eager(torch_mod):
+    """The whole step (forward, backward, delayed wgrad; FC1 activation in the GEMM epilogue) captured
+    in one HIP graph: every launch goes to the capturing stream and nothing in it allocates outside
+    torch's graph pool or writes with a memset.  Each of three replays, with eager steps and
+    synchronizations between them, gives bitwise the eager step's outputs."""
+    import torch
+    from moe_grouped_scaled_amd.expert_mlp import ExpertMLP
+    e, splits, h, f = 4, [64, 0, 96, 37], 256, 256
+    d = _inputs("srelu", e, splits, h, f, seed=12)
+    w1, w2, b1, b2 = (to_dev_bf16(d[k]) for k in ("w1", "w2", "b1", "b2"))
+    x1, p, dy2 = to_dev_bf16(d["x1"]), to_dev(d["p"]), to_dev_bf16(d["dy2"])
+    mlp = ExpertMLP("srelu", "mxfp8", w1, w2, b1, b2, recompute=True, delay_wgrad=True, fuse_fc1_act=True)
+
+    def step():
+        y = mlp.forward(x1, p, list(splits))
+        g = mlp.backward(dy2)
+        g.update(mlp.backward_dw())
+        g["y2"] = y
+        return g
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gout = step()
+    torch.cuda.synchronize()
+    keys = ("y2", "dx1", "dprobs", "dw1", "dw2", "db1", "db2")
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: gout[k].clone() for k in keys}
+        eager = step()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(got[k], eager[k]), k
