@@ -167,7 +167,7 @@ def main():
     ap.add_argument("--fc1-fp32-act", action="store_true",
                     help="activate FC1's FP32 output in the forward (the recompute then regenerates FC2's "
                          "input from its BF16 copy)")
-    ap.add_argument("--fc1-act", default="separate", choices=["epilogue", "separate"],
+    ap.add_argument("--fc1-act", default="epilogue", choices=["epilogue", "separate"],
                     help="run the forward activation + quantization in FC1's GEMM epilogue (MXFP8, unary "
                          "activations) or as its own fused pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -270,8 +270,8 @@ def main():
     value = flops_step / (wall / args.steps) / 1e12
 
     gemm_t = []
-    for tag in ("gemm_fprop", "gemm_dgrad", "gemm_wgrad"):
-        gemm_t += dur.get(tag, [])
+    for tag in ("gemm_fprop", "gemm_dgrad", "gemm_wgrad", "grouped_gemm_mx_fprop_act"):
+        gemm_t += dur.get(tag, [])    # the six GEMM launches of each step (FC1's may carry the activation)
     flops_launch = 2 * m * h * f          # every one of the six GEMMs has this size here
     gemm_avg = float(np.mean(gemm_t))
     gemm_tflops = flops_launch / gemm_avg / 1e12

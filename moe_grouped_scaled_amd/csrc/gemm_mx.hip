@@ -180,6 +180,36 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
   return j;
 }
 
+// Lane exchanges of gfx950 (VALU, no LDS).  swap16(a, b): lanes of even 16-lane rows get
+// (a[l], a[l + 16]), lanes of odd rows (b[l - 16], b[l]); swap32(a, b): lanes 0..31 get (a[l], a[l + 32]),
+// lanes 32..63 (b[l - 32], b[l]) (measured on the device).
+struct U2 { uint32_t x, y; };
+__device__ __forceinline__ U2 swap16(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return U2{r[0], r[1]};
+}
+__device__ __forceinline__ U2 swap32(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return U2{r[0], r[1]};
+}
+// max over the lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float max_over_rows(float m) {
+  U2 r = swap16(__float_as_uint(m), __float_as_uint(m));
+  m = fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+  r = swap32(__float_as_uint(m), __float_as_uint(m));
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+// 16-byte global store that keeps its data registers live through two wait states: a store wider
+// than 8 bytes reads its data after it issues, and a VALU write to them in the next instruction
+// changed what part of the wave stored (observed on gfx950).
+__device__ __forceinline__ void st16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const v4u v = {a, b, c, d};
+  *reinterpret_cast<v4u*>(p) = v;
+  asm volatile("s_nop 1" :: "v"(v));
+}
+
 // Epilogue value of one 16 x 16 fragment held as C[row][col0 .. col0 + 3] in each lane: the group
 // factor, then the bias (four BF16 values, already fetched).
 __device__ __forceinline__ void frag_values(const TileJob& j, v4f acc, uint2 bw, float (&v)[4]) {
@@ -193,7 +223,8 @@ __device__ __forceinline__ void store_values(const TileJob& j, int row, int col,
   if (row >= j.a.rows || col >= j.b.rows) return;  // b.rows is a multiple of 4 (N % 32 == 0)
   const int64_t gr = j.crow0 + row, gc = j.ccol0 + col;
   if (j.c32) {
-    *reinterpret_cast<float4*>(j.c32 + gr * j.ldc + gc) = make_float4(v[0], v[1], v[2], v[3]);
+    st16(j.c32 + gr * j.ldc + gc, __float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+         __float_as_uint(v[3]));
   } else {
     uint2 w;
     w.x = bf16x2(v[0], v[1]);
@@ -290,13 +321,17 @@ __device__ __forceinline__ void mfma_drain() {
 // FPROP epilogue with the scaled activation and MXFP8 rowwise quantization of its result (page
 // "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU", Description and review
 // discussion: the fused forward activates FC1's output in the GEMM epilogue and quantizes it for FC2).
-// Per fragment row the lane stores its BF16 values of C as the plain epilogue does, and evaluates
-// y = act(x) * p with x the FP32 value or its BF16 rounding; a 32-column block of a row is held by
-// the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (8 values each, fragment columns 2b and 2b + 1), so the block
-// maximum is two cross-lane steps.  The scale code, the reciprocal power of two and the saturating
-// E4M3 convert are the shared helpers the fused activation kernels use, so the codes equal theirs on
-// the same x bit for bit.  The four scales of the wave's 128 columns (one K step of FC2's operand)
-// go out as one dword per row.
+// Lane l = 16 q + r16 holds, for fragment row fm and fragment column fn, C[row][16 fn + 4 q .. + 3]
+// (row = 16 fm + r16 within the wave's 128 rows).  Per row the lane evaluates y = act(x) * p with x the
+// FP32 value or its BF16 rounding; a 32-column block b (fragment columns 2b, 2b + 1) of a row lies in
+// the 4 lanes l, l ^ 16, l ^ 32, l ^ 48, 8 values each, so its maximum is two lane swaps.  The scale
+// code, its reciprocal power of two and the saturating E4M3 convert are the helpers the fused
+// activation kernels use, so the codes equal theirs on the same x bit for bit.  Stores are regrouped
+// by lane swaps so every lane writes 16 contiguous bytes: for a block b the lane holds code dwords
+// 4q and 16 + 4q (bytes of the block); a 16-swap leaves lane q the 8 bytes at {16, 0, 24, 8}[q], a
+// 32-swap with block b + 1 then 16 bytes of block b + q / 2 at 16 (1 - q % 2).  The BF16 values of C
+// are regrouped the same way by one 16-swap per block (16 bytes at 64 b + {32, 0, 48, 16}[q]).  The
+// four scales of the wave's 128 columns (one K step of FC2's operand) go out as one dword per row.
 template <int KIND>
 __device__ __forceinline__ void epilogue_act(const TileJob& j, const GemmArgs& ga, v4f (&acc)[8][8],
                                              const uint2 (&bw)[8], int wm, int wn, int q, int r16) {
@@ -305,54 +340,91 @@ __device__ __forceinline__ void epilogue_act(const TileJob& j, const GemmArgs& g
   const int64_t col0 = j.ccol0 + cw;                // ... within C
   const int64_t srows = j.a.srows;                  // all M rows: the scale matrix's row count
   const bool wave_cols = cw < j.b.rows;             // the wave's columns reach into C
+  const bool odd = q & 1;
+  const int c16_off = 16 * (odd ? (q >> 1) : 2 + (q >> 1));   // BF16 bytes within a 64-byte block
 #pragma unroll
   for (int fm = 0; fm < 8; ++fm) {
     const int row = wm * 128 + fm * 16 + r16;
     const bool rok = row < j.a.rows;
     const int64_t gr = j.crow0 + row;
     const float p = !rok ? 0.0f : ga.probs ? ga.probs[gr] : 1.0f;
+    uint16_t* crow = j.c16 + gr * j.ldc + col0;
+    uint8_t* arow = ga.act_data + gr * ga.n + col0;
     uint32_t sdw = 0;
+    U2 pr[4];                                       // per block: the lane's 8 code bytes after the 16-swap
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const bool bok = cw + 32 * b < j.b.rows;      // n % 32 == 0: a block is all in or all out
       float y[8];
+      uint2 w[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int fn = 2 * b + h;
-        const int col = cw + fn * 16 + 4 * q;
         float v[4];
         frag_values(j, acc[fm][fn], bw[fn], v);
-        uint2 w;
-        w.x = bf16x2(v[0], v[1]);
-        w.y = bf16x2(v[2], v[3]);
-        if (rok && bok) *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + j.ccol0 + col) = w;
+        w[h].x = bf16x2(v[0], v[1]);
+        w[h].y = bf16x2(v[2], v[3]);
         float x[4];
         if (ga.act_on_bf16) {
-          x[0] = bf16lo(w.x); x[1] = bf16hi(w.x); x[2] = bf16lo(w.y); x[3] = bf16hi(w.y);
+          x[0] = bf16lo(w[h].x); x[1] = bf16hi(w[h].x); x[2] = bf16lo(w[h].y); x[3] = bf16hi(w[h].y);
         } else {
           x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) y[4 * h + t] = bok ? act_unary<KIND>(x[t], aa) * p : 0.0f;
       }
+      // C: 16 contiguous bytes of the block's 64 per lane
+      const U2 cx = swap16(w[1].x, w[0].x), cy = swap16(w[1].y, w[0].y);
+      if (rok && bok) st16(reinterpret_cast<uint8_t*>(crow) + 64 * b + c16_off, cx.x, cy.x, cx.y, cy.y);
       float m = 0.0f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(y[t]));
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
+      m = max_over_rows(m);
       const uint32_t c = mx_scale_code(m);
       const float inv = mx_inv_scale(c);
       const uint32_t q0 = e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
       const uint32_t q1 = e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
-      if (rok && bok) {
-        uint8_t* dst = ga.act_data + gr * ga.n + col0 + 32 * b + 4 * q;
-        *reinterpret_cast<uint32_t*>(dst) = q0;
-        *reinterpret_cast<uint32_t*>(dst + 16) = q1;
-      }
+      pr[b] = swap16(q1, q0);
       sdw |= (bok ? c : 0u) << (8 * b);
+    }
+    // codes: blocks (0, 1) and (2, 3); lane q writes 16 bytes of block b + q / 2
+#pragma unroll
+    for (int b = 0; b < 4; b += 2) {
+      const U2 lo = swap32(pr[b].x, pr[b + 1].x), hi = swap32(pr[b].y, pr[b + 1].y);
+      const int blk = b + (q >> 1);
+      if (rok && cw + 32 * blk < j.b.rows)
+        st16(arow + 32 * blk + (odd ? 0 : 16), lo.x, hi.x, lo.y, hi.y);
     }
     if (rok && wave_cols && q == 0)
       *reinterpret_cast<uint32_t*>(ga.act_scales + ((col0 / 128) * srows + gr) * 4) = sdw;
+  }
+}
+
+// BF16 epilogue: per fragment row, one 16-swap per 32-column block regroups the lane's two 8-byte
+// pieces (fragment columns 2b, 2b + 1) so it writes 16 contiguous bytes at 64 b + {32, 0, 48, 16}[q]:
+// four 16-byte stores per row of fragments instead of eight 8-byte ones.
+__device__ __forceinline__ void epilogue_bf16(const TileJob& j, v4f (&acc)[8][8], const uint2 (&bw)[8],
+                                              int wm, int wn, int q, int r16) {
+  const int cw = wn * 128;
+  const int c16_off = 16 * ((q & 1) ? (q >> 1) : 2 + (q >> 1));
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm) {
+    const int row = wm * 128 + fm * 16 + r16;
+    const bool rok = row < j.a.rows;
+    uint8_t* crow = reinterpret_cast<uint8_t*>(j.c16 + (j.crow0 + row) * j.ldc + j.ccol0 + cw);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint2 w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float v[4];
+        frag_values(j, acc[fm][2 * b + h], bw[2 * b + h], v);
+        w[h].x = bf16x2(v[0], v[1]);
+        w[h].y = bf16x2(v[2], v[3]);
+      }
+      const U2 cx = swap16(w[1].x, w[0].x), cy = swap16(w[1].y, w[0].y);
+      if (rok && cw + 32 * b < j.b.rows) st16(crow + 64 * b + c16_off, cx.x, cy.x, cx.y, cy.y);
+    }
   }
 }
 
@@ -360,14 +432,15 @@ __device__ __forceinline__ void epilogue_act(const TileJob& j, const GemmArgs& g
 __device__ __forceinline__ void epilogue_256(const TileJob& j, const GemmArgs& ga, v4f (&acc)[8][8],
                                              const uint2* bias_lds, int wm, int wn, int q, int r16) {
   // epilogue: bias from LDS; one straight-line variant per output kind, so that stores never wait
-  // for each other (with accumulation, the eight C fragments of a fragment row are loaded together
-  // before any of them is stored: one memory round trip per fragment row)
+  // for each other
   uint2 bw[8];
 #pragma unroll
   for (int fn = 0; fn < 8; ++fn)
     bw[fn] = j.bias ? bias_lds[(wn * 128 + fn * 16 + 4 * q) >> 2] : make_uint2(0, 0);
-  auto epilogue = [&](auto c32_tag, auto acc_tag) {
-    constexpr bool C32 = decltype(c32_tag)::value, ACC = decltype(acc_tag)::value;
+  // FP32 output (optionally accumulating): the eight C fragments of a fragment row are loaded together
+  // before any of them is stored, one memory round trip per fragment row
+  auto epilogue_f32 = [&](auto acc_tag) {
+    constexpr bool ACC = decltype(acc_tag)::value;
 #pragma unroll
     for (int fm = 0; fm < 8; ++fm) {
       const int row = wm * 128 + fm * 16 + r16;
@@ -390,16 +463,9 @@ __device__ __forceinline__ void epilogue_256(const TileJob& j, const GemmArgs& g
         if constexpr (ACC) {
           v[0] += old[fn].x; v[1] += old[fn].y; v[2] += old[fn].z; v[3] += old[fn].w;
         }
-        if (rok && col < j.b.rows) {
-          if constexpr (C32) {
-            *reinterpret_cast<float4*>(j.c32 + gr * j.ldc + j.ccol0 + col) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            uint2 w;
-            w.x = bf16x2(v[0], v[1]);
-            w.y = bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + j.ccol0 + col) = w;
-          }
-        }
+        if (rok && col < j.b.rows)
+          st16(j.c32 + gr * j.ldc + j.ccol0 + col, __float_as_uint(v[0]), __float_as_uint(v[1]),
+               __float_as_uint(v[2]), __float_as_uint(v[3]));
       }
     }
   };
@@ -412,11 +478,11 @@ __device__ __forceinline__ void epilogue_256(const TileJob& j, const GemmArgs& g
       default: epilogue_act<MGS_ACT_IDENTITY>(j, ga, acc, bw, wm, wn, q, r16); break;
     }
   } else if (!j.c32) {
-    epilogue(std::false_type{}, std::false_type{});
+    epilogue_bf16(j, acc, bw, wm, wn, q, r16);
   } else if (!ga.accumulate) {
-    epilogue(std::true_type{}, std::false_type{});
+    epilogue_f32(std::false_type{});
   } else {
-    epilogue(std::true_type{}, std::true_type{});
+    epilogue_f32(std::true_type{});
   }
 }
 
