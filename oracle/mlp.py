@@ -46,22 +46,25 @@ def _bf16(x64):
     return bf16_bits_to_f64(f32_to_bf16_bits(f32(x64).astype(np.float32)))
 
 
-def _q(x, splits, fmt, width, row=True, col=True):
-    q = quantize_grouped(x, splits, fmt, rowwise=row, colwise=col)
+def _q(x, splits, fmt, width, row=True, col=True, rht=None):
+    q = quantize_grouped(x, splits, fmt, rowwise=row, colwise=col, rht=rht)
     gs = q.get("group_scale")
     out = {"raw": q}
     if row:
         out["row"] = dequant_row_grouped(fmt, q["row_data"], q["row_scales"], splits, width, gs)
     if col:
-        out["col"] = dequant_col_grouped(fmt, q["col_data"], q["col_scales"], splits, width, gs)
+        out["col"] = dequant_col_grouped(fmt, q["col_data"], q["col_scales"], splits, width,
+                                         q.get("col_group_scale", gs))
     return out
 
 
 def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None, act_input="bf16",
-             recompute=False):
+             recompute=False, rht=None):
     """All inputs are float64 arrays holding BF16 (x1, w1, b1, w2, b2, dy2) or FP32 (p) values.
 
     Shapes: x1 [M, H]; w1 [E, F_in, H]; b1 [E, F_in]; w2 [E, H, F]; b2 [E, H]; p [M]; dy2 [M, H].
+    `rht` (NVFP4 only, a 16-bit sign mask): Hadamard-transform the columnwise copies of the four
+    weight-gradient operands (X1, A, dY2, dY1) with the same signs.
     Returns a dict of float64 results.
     """
     act_params = act_params or {}
@@ -72,7 +75,7 @@ def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None, act
     wsplit_1 = [f_in] * e
     wsplit_2 = [h] * e
 
-    qx1 = _q(x1, splits, fmt, h)
+    qx1 = _q(x1, splits, fmt, h, rht=rht)
     qw1 = _q(w1.reshape(e * f_in, h), wsplit_1, fmt, h)
     w1_row = qw1["row"].reshape(e, f_in, h)
     w1_col = dgrad_weight(qw1["col"], f_in)  # per expert [H x F_in]
@@ -84,24 +87,24 @@ def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None, act
     else:
         assert act_input == "bf16", act_input
         a32 = act_mod.scaled_act_fwd(kind, y1, p, **act_params)
-    qa = _q(a32, splits, fmt, f)
+    qa = _q(a32, splits, fmt, f, rht=rht)
     if recompute and act_input == "fp32":
         # FC2's columnwise input regenerated from the saved BF16 Y1 (the forward's only rowwise)
         a_rec = act_mod.scaled_act_fwd(kind, y1, p, **act_params)
         amax = qa["raw"].get("group_amax")
-        q_rec = quantize_grouped(a_rec, splits, fmt, rowwise=False, colwise=True, group_amax=amax)
+        q_rec = quantize_grouped(a_rec, splits, fmt, rowwise=False, colwise=True, group_amax=amax, rht=rht)
         qa["col"] = dequant_col_grouped(fmt, q_rec["col_data"], q_rec["col_scales"], splits, f,
-                                        q_rec.get("group_scale"))
+                                        q_rec.get("col_group_scale", q_rec.get("group_scale")))
     qw2 = _q(w2.reshape(e * h, f), wsplit_2, fmt, f)
     w2_row = qw2["row"].reshape(e, h, f)
     w2_col = dgrad_weight(qw2["col"], h)     # per expert [F x H]
     y2 = _bf16(gemm_grouped_m(qa["row"], list(w2_row), splits, bias=b2))
 
-    qdy2 = _q(dy2, splits, fmt, h)
+    qdy2 = _q(dy2, splits, fmt, h, rht=rht)
     da = _bf16(gemm_grouped_m(qdy2["row"], w2_col, splits))
     dy1_32, dp = act_mod.scaled_act_bwd(kind, y1, da, p, **act_params)
     dy1_bf16 = _bf16(dy1_32)
-    qdy1 = _q(dy1_32, splits, fmt, f_in)
+    qdy1 = _q(dy1_32, splits, fmt, f_in, rht=rht)
     dx1 = _bf16(gemm_grouped_m(qdy1["row"], w1_col, splits))
 
     dw2 = gemm_grouped_k(qdy2["col"], qa["col"])    # [E, H, F]

@@ -40,6 +40,15 @@ Buffer layouts produced here are the library's documented qtensor layouts:
   ((kb // 4) * R + r) * 4 + kb % 4, 4 * R * ceil(K / 128) bytes in all, unused bytes of a partial
   last step zero.
 
+Random Hadamard transform (the recipe [P1]'s deviation table names "NVFP4_RHT" without defining
+it; the reading follows the published NVFP4 training recipe): before NVFP4 columnwise quantization,
+every 16-token block v of a column becomes H16 diag(s) v / 4, H16 the Sylvester Hadamard matrix
+(H[k, n] = (-1)^popcount(k & n)) and s a fixed sign vector given as a 16-bit mask (bit i set: s_i = -1).
+The map is orthogonal, so applied to both operands of a weight-gradient GEMM along their common
+(token) axis it leaves the product unchanged while spreading outliers over the block.  The
+transformed copy takes its per-group encode scale from its own amax (over the transformed values,
+padding positions of a partial block included: they carry transformed values the product needs).
+
 Parity: MXFP8 pinned (closed-form scale codes, exhaustive codec tests, M6 statistics).  The NVFP4
 FP32 sequence is a reading; it is pinned only by invariants (the block holding the group maximum gets
 s_b = 448, codes within +-6, dequantization error bound), so its exact bits are "parity unpinned".
@@ -161,16 +170,40 @@ def nvfp4_quantize_rows(y32, s_enc):
     return pack_e2m1(codes.reshape(rows, w)), s_code
 
 
+# ----------------------------------------------------------------------------- Hadamard
+
+def hadamard16():
+    """Sylvester Hadamard matrix of order 16 from its closed form H[k, n] = (-1)^popcount(k & n)."""
+    k = np.arange(16)
+    parity = np.array([[bin(a & b).count("1") & 1 for b in k] for a in k])
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+def rht_signs(mask):
+    """The sign vector s (length 16) of a 16-bit mask: bit i set means s_i = -1."""
+    return np.array([-1.0 if (int(mask) >> i) & 1 else 1.0 for i in range(16)])
+
+
+def rht16(x, mask):
+    """H16 diag(s) v / 4 on every block of 16 consecutive values along the last axis (float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] % 16 == 0
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // 16, 16)) * rht_signs(mask)
+    return (blocks @ hadamard16().T / 4.0).reshape(x.shape)
+
+
 # ----------------------------------------------------------------------------- grouped
 
-def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True, group_amax=None):
+def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True, group_amax=None, rht=None):
     """Grouped quantization of a [M, W] float32 tensor (float64 array of float32 values).
 
     Returns a dict with (as requested) 'row_data', 'row_scales', 'col_data', 'col_scales' (flat uint8
     buffers in the documented layouts), and for NVFP4 'group_amax' and 'group_scale' (float32 [E]).
     NVFP4 with `group_amax` given takes the per-tensor scales from it instead of from y: the recompute
     requantizes with the amax its forward saved ([P1] Description: recompute regenerates FC2's input
-    under the forward's quantization state).
+    under the forward's quantization state).  NVFP4 with `rht` (a 16-bit sign mask) transforms the
+    columnwise copy (see the module notes) and returns its own 'col_group_amax' / 'col_group_scale'
+    (`group_amax` then applies to the rowwise copy only).
     """
     y = np.asarray(y32, dtype=np.float64)
     m_total, w = y.shape
@@ -208,19 +241,31 @@ def quantize_grouped(y32, split_sizes, fmt, rowwise=True, colwise=True, group_am
         out["row_data"] = d.reshape(-1)
         out["row_scales"] = mx_scales_to_kstep(s) if fmt == MXFP8 else s.reshape(-1)
     if colwise:
-        parts_d, parts_s = [], []
+        assert rht is None or fmt == NVFP4, "the Hadamard transform applies to NVFP4 columnwise copies"
+        col_t, col_enc = [], s_enc
         for g in range(e):
             m_g = off[g + 1] - off[g]
             mp = coff[g + 1] - coff[g]
-            if mp == 0:
-                continue
             yt = np.zeros((w, mp))
             yt[:, :m_g] = y[off[g]:off[g + 1]].T
+            col_t.append(f32(rht16(yt, rht)) if rht is not None and mp else yt)
+        if rht is not None:
+            camax = np.array([np.max(np.abs(t)) if t.size else 0.0 for t in col_t])
+            pairs = [nvfp4_global(a) for a in camax]
+            col_enc = np.array([p[0] for p in pairs])
+            out["col_group_amax"] = f32(camax)
+            out["col_group_scale"] = np.array([p[1] for p in pairs])
+        parts_d, parts_s = [], []
+        for g in range(e):
+            mp = coff[g + 1] - coff[g]
+            if mp == 0:
+                continue
+            yt = col_t[g]
             if fmt == MXFP8:
                 d_g, s_g = mxfp8_quantize_rows(yt)
                 s_g = mx_scales_to_kstep(s_g)
             else:
-                d_g, s_g = nvfp4_quantize_rows(yt, s_enc[g])
+                d_g, s_g = nvfp4_quantize_rows(yt, col_enc[g])
             parts_d.append(d_g.reshape(-1))
             parts_s.append(s_g.reshape(-1))
         out["col_data"] = np.concatenate(parts_d) if parts_d else np.zeros(0, np.uint8)

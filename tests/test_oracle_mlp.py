@@ -10,8 +10,9 @@ The oracle's step with act_input="fp32" is that reading; its FC2-wgrad deviation
 at hidden 256 and 4 groups, must land on the table's MXFP8 RMS values (within 25%: the pages give
 neither token counts nor value distributions, so the N(0, 0.02) weights, N(0, 1) inputs and 256
 tokens per group used here are this suite's choice).  The NVFP4 rows were measured with the
-Hadamard-transformed recipe the page names NVFP4_RHT, which this library does not implement, so they
-are upper bounds only.  The table's max-abs column is an extreme statistic that grows with the tensor
+Hadamard-transformed recipe the page names NVFP4_RHT; the oracle runs NVFP4 with and without its
+reading of that transform (oracle.quant), and both stay under the printed values, which serve as upper
+bounds only.  The table's max-abs column is an extreme statistic that grows with the tensor
 size the page does not give; it is printed, not asserted.
 """
 
@@ -28,7 +29,7 @@ from tests.helpers import bf16_f64
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _step_pair(kind, fmt, act_input, h=256, f=256, splits=(256, 256, 256, 256), seed=0):
+def _step_pair(kind, fmt, act_input, h=256, f=256, splits=(256, 256, 256, 256), seed=0, rht=None):
     rng = np.random.default_rng(seed)
     e, m = len(splits), int(sum(splits))
     x1 = workloads.normal_bf16(rng, (m, h))
@@ -41,8 +42,8 @@ def _step_pair(kind, fmt, act_input, h=256, f=256, splits=(256, 256, 256, 256), 
     args = (kind, fmt, list(splits), bf16_f64(x1), bf16_f64(w1), bf16_f64(b1), bf16_f64(w2),
             bf16_f64(b2), p.astype(np.float64), bf16_f64(dy2))
     ap = {"s": 2.0} if kind == "tanh_srelu" else None
-    off = M.mlp_step(*args, act_params=ap, act_input=act_input, recompute=False)
-    on = M.mlp_step(*args, act_params=ap, act_input=act_input, recompute=True)
+    off = M.mlp_step(*args, act_params=ap, act_input=act_input, recompute=False, rht=rht)
+    on = M.mlp_step(*args, act_params=ap, act_input=act_input, recompute=True, rht=rht)
     return off, on
 
 
@@ -52,16 +53,19 @@ def _bound(kind, fmt):
     return [r for r in rows if r["recipe"] == fmt and r["act"] == kind][0]
 
 
-@pytest.mark.parametrize("kind,fmt", [("srelu", "mxfp8"), ("tanh_srelu", "mxfp8"), ("srelu", "nvfp4"),
-                                      ("tanh_srelu", "nvfp4")])
-def test_recompute_deviation_matches_pages_table(kind, fmt):
-    off, on = _step_pair(kind, fmt, "fp32")
+@pytest.mark.parametrize("kind,fmt,rht", [("srelu", "mxfp8", None), ("tanh_srelu", "mxfp8", None),
+                                          ("srelu", "nvfp4", None), ("tanh_srelu", "nvfp4", None),
+                                          ("srelu", "nvfp4", 0x6B35), ("tanh_srelu", "nvfp4", 0x6B35)])
+def test_recompute_deviation_matches_pages_table(kind, fmt, rht):
+    """With the Hadamard transform (the page's NVFP4_RHT recipe) the NVFP4 deviation rises (2.7 -> 3.9 %
+    for SReLU, 2.5 -> 3.4 % for TanhSReLU here) toward the page's 8.8 % / 4.1 %, still below them."""
+    off, on = _step_pair(kind, fmt, "fp32", rht=rht)
     for k in ("y2", "dx1", "dp", "dw1", "db1", "db2"):
         assert np.array_equal(on[k], off[k]), k
     diff = on["dw2"] - off["dw2"]
     rms = np.sqrt(np.mean(off["dw2"] ** 2))
     dev_pct = 100 * np.sqrt(np.mean(diff ** 2)) / rms
-    print(kind, fmt, "rms %.2f%%, max-abs %.1f%%, mean/rms %+.4f" % (
+    print(kind, fmt, rht, "rms %.2f%%, max-abs %.1f%%, mean/rms %+.4f" % (
         dev_pct, 100 * np.max(np.abs(diff)) / rms, np.mean(diff) / rms))
     b = _bound(kind, fmt)
     assert abs(np.mean(diff)) / rms <= 0.01          # the table's mean column: 0.00
