@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MGS_ABI_VERSION 5
+#define MGS_ABI_VERSION 6
 #define MGS_MAX_GROUPS 256
 
 enum mgs_status {
@@ -123,6 +123,14 @@ typedef struct {
   void* data;
   void* scales;
   float* group_scale; /* NVFP4 only: S_dec per group [E]; ignored for MXFP8 */
+  /* NVFP4 columnwise copies only (0 elsewhere): random Hadamard transform of every 16-token block
+   * of a column before quantization, v -> H16 diag(s) v / 4 (H16[k][n] = (-1)^popcount(k & n)).
+   * 0 = off; otherwise bit 16 must be set and bits 0..15 give the signs (bit n set: s_n = -1).
+   * [P1] names this recipe NVFP4_RHT for its NVFP4 measurements without defining it; it is for the
+   * two operands of a weight-gradient GEMM, made with the same signs, whose product the orthogonal
+   * transform leaves unchanged.  The transformed copy's per-group encode scale comes from its own
+   * amax (see group_amax below); the GEMM reads such a copy like any other. */
+  uint32_t rht;
 } mgs_qbuf;
 
 /* Library ABI version (MGS_ABI_VERSION). */
@@ -146,6 +154,8 @@ int64_t mgs_qtensor_nbytes(int32_t fmt, int32_t colwise, const mgs_groups* group
  *   out_col    columnwise qtensor of y; nullable (NULL in the recompute forward, [P1] Description)
  *   group_amax [E] FP32: NVFP4 only, required there; receives max|y| per group (the per-tensor
  *              amax of each expert slice) and must be kept for a later recompute.  Ignored for MXFP8.
+ *              [2E] when out_col has the Hadamard transform (mgs_qbuf.rht): entries E..2E-1 receive
+ *              the transformed values' amax, which scales the columnwise copy.
  * NVFP4 runs two passes over x (group amax, then quantize). */
 int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
                                int64_t width_in, const void* x_bf16, const float* probs,
@@ -174,16 +184,21 @@ int mgs_grouped_scaled_act_fwd_f32(const mgs_act_params* act, int32_t fmt, const
  *   probs         [M] FP32; NULL means 1
  *   dx_bf16       [M x width_in] BF16 dense dL/dx = dy * p * a'(x); nullable
  *   dx_row/dx_col quantized dL/dx (rowwise / columnwise); nullable
- *   dx_group_amax [E] FP32: required when dx is quantized to NVFP4 (receives max|dL/dx| per group)
+ *   dx_group_amax [E] FP32: required when dx is quantized to NVFP4 (receives max|dL/dx| per group);
+ *                 [2E] when dx_col has the Hadamard transform (transformed amax at E..2E-1)
  *   dprobs        [M] FP32 dL/dp = sum_j dy * a(x); nullable
  *   dx_col_sum    [E x width_in] FP32 per-group column sums of the dense BF16 dL/dx (the values dx_bf16
  *                 holds, whether or not it is requested): the FC1 bias gradient.  [P1] Description,
  *                 second paragraph (bias in the fused step).  Nullable; empty groups give zeros.
  *   act_col       columnwise qtensor of y = a(x) * p regenerated from x (recompute); nullable.  Its bytes
  *                 equal those the forward's out_col would have held.
- *   saved_group_amax [E] FP32 group amax written by the forward; required for an NVFP4 act_col.
+ *   saved_group_amax [E] FP32 group amax written by the forward; required for an NVFP4 act_col
+ *                 without the Hadamard transform.  With it (act_col.rht) the transformed values'
+ *                 amax is taken again from x in this call (the same bits the forward's copy used)
+ *                 and the workspace is required.
  *   workspace     DEVICE scratch of at least mgs_act_bwd_workspace_bytes() bytes, required when dprobs
- *                 or dx_col_sum is requested (else ignored; may be NULL); owned by the caller,
+ *                 or dx_col_sum is requested, or act_col has the Hadamard transform (else ignored;
+ *                 may be NULL); owned by the caller,
  *                 contents undefined before and after the call.  The kernel writes partial sums there
  *                 (dprobs: one per row and 128-column tile; column sums: one per 128-token block and
  *                 column) and second kernels add them in a fixed order, so both are deterministic.
@@ -197,8 +212,9 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
                                const float* saved_group_amax, void* workspace,
                                int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes mgs_grouped_scaled_act_bwd needs for dprobs and dx_col_sum:
- * roundup(4 * M * ceil(W_a / 128), 256) + 4 * (P / 128) * width_in, P = sum_g roundup(m_g, 128).
+/* Workspace bytes mgs_grouped_scaled_act_bwd needs for dprobs, dx_col_sum and a transformed act_col:
+ * roundup(roundup(4 * M * ceil(W_a / 128), 256) + 4 * (P / 128) * width_in, 256) + 8 * E,
+ * P = sum_g roundup(m_g, 128).
  * Negative MGS_ERR_* on invalid arguments. */
 int64_t mgs_act_bwd_workspace_bytes(const mgs_act_params* act, const mgs_groups* groups,
                                     int64_t width_in);

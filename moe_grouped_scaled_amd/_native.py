@@ -44,7 +44,10 @@ class Groups(ctypes.Structure):
 
 class QBuf(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("group_scale", ctypes.c_void_p)]
+                ("group_scale", ctypes.c_void_p), ("rht", ctypes.c_uint32)]
+
+
+RHT_ON = 1 << 16  # mgs_qbuf.rht: bit 16 enables the Hadamard transform, bits 0..15 are its signs
 
 
 def _load():
@@ -136,8 +139,10 @@ def act_params(kind, s=2.0, limit=7.0, alpha=1.0, beta=0.0):
 class QTensor:
     """One orientation (rowwise or columnwise) of a grouped quantized tensor: three torch buffers."""
 
-    def __init__(self, fmt, colwise, split_sizes, width, device="cuda"):
+    def __init__(self, fmt, colwise, split_sizes, width, device="cuda", rht=None):
+        """`rht` (NVFP4 columnwise only): 16-bit sign mask of the Hadamard transform of the copy."""
         self.fmt, self.colwise, self.width = fmt, bool(colwise), int(width)
+        self.rht = 0 if rht is None else RHT_ON | (int(rht) & 0xFFFF)
         self.split_sizes = np.asarray(split_sizes, dtype=np.int64)
         nd = qtensor_nbytes(fmt, colwise, split_sizes, width, "data")
         ns = qtensor_nbytes(fmt, colwise, split_sizes, width, "scales")
@@ -147,7 +152,7 @@ class QTensor:
         self.group_scale = torch.empty(ng // 4, dtype=torch.float32, device=device) if ng else None
 
     def qbuf(self):
-        return QBuf(self.data.data_ptr(), self.scales.data_ptr(), _ptr(self.group_scale))
+        return QBuf(self.data.data_ptr(), self.scales.data_ptr(), _ptr(self.group_scale), self.rht)
 
     def nbytes(self):
         return self.data.numel() + self.scales.numel() + (self.group_scale.numel() * 4 if self.group_scale is not None else 0)

@@ -430,9 +430,8 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int n) {
 __device__ __forceinline__ void write_group_scales(const GroupTable& gt, const QOut& q) {
   if (blockIdx.x != 0 || q.amax == nullptr) return;
   for (int g = threadIdx.x; g < gt.num_groups; g += blockDim.x) {
-    const float s_dec = 1.0f / nv_encode_scale(q.amax[g]);
-    if (q.row_gscale) q.row_gscale[g] = s_dec;
-    if (q.col_gscale) q.col_gscale[g] = s_dec;
+    if (q.row_gscale) q.row_gscale[g] = 1.0f / nv_encode_scale(q.amax[g]);
+    if (q.col_gscale) q.col_gscale[g] = 1.0f / nv_encode_scale(q.col_amax[g]);
   }
 }
 
@@ -515,14 +514,44 @@ __device__ __forceinline__ void stage_col(const float (&v)[8], uint8_t* st, cons
   }
 }
 
+// Random Hadamard transform of a 16-token block of one column (the weight-gradient operands of the
+// NVFP4 recipe the recompute page names NVFP4_RHT): v -> H16 diag(s) v / 4, H16[k][n] =
+// (-1)^popcount(k & n), s_n = -1 where bit n of `rht` is set.  The block is the lane pair (rc, rc ^ 1)
+// of a quad: the lane holds tokens 8 (rc & 1) + i.  Three butterfly stages run in the lane (token bits
+// 0..2), the fourth across the pair (DPP quad_perm [1,0,3,2]); the scaling by 1/4 is exact.
+__device__ __forceinline__ void rht16_col(float (&v)[8], uint32_t rht, int rc) {
+  const int base = 8 * (rc & 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if ((rht >> (base + i)) & 1u) v[i] = -v[i];
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float o = dpp_f<DPP_QUAD_XOR1>(v[i]);
+    v[i] = ((rc & 1) ? o - v[i] : v[i] + o) * 0.25f;
+  }
+}
+
+// Columnwise staging of a whole tile; `rht` (NVFP4 only, wave-uniform): bit 16 enables the Hadamard
+// transform of each column's 16-token blocks before quantization, bits 0..15 are its signs.
 template <int FMT>
 __device__ __forceinline__ void stage_tile(const float (&y)[8][8], uint8_t* st, const BlockPos& bp,
-                                           float s_enc) {
+                                           float s_enc, uint32_t rht = 0) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = y[i][j];
+    if (FMT == MGS_FMT_NVFP4 && rht) rht16_col(v, rht, bp.lane & 3);
     stage_col<FMT>(v, st, bp, j, s_enc);
   }
 }
@@ -609,10 +638,11 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
   const BlockPos bp = block_pos(gt, n_ct);
   const PanelInfo& pi = bp.pi;
   const bool valid = bp.col < wa;
-  float s_enc = 1.0f;
+  float s_enc = 1.0f, s_enc_col = 1.0f;
   if constexpr (FMT == MGS_FMT_NVFP4) {
     write_group_scales(gt, out);
     s_enc = nv_encode_scale(out.amax[pi.g]);
+    s_enc_col = nv_encode_scale(out.col_amax[pi.g]);
   }
   float p[8];
   load_probs(probs, pi, gt.total_rows, bp.lr0, p);
@@ -630,7 +660,7 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
     }
     cs_stage(cs, cs_lds, bp);
   }
-  if (out.col_data) stage_tile<FMT>(y, stage, bp, s_enc);
+  if (out.col_data) stage_tile<FMT>(y, stage, bp, s_enc_col, out.col_rht);
   if (out.col_data || cs_part) {
     __syncthreads();
     if (out.col_data) flush_col<FMT>(stage, out, wa, (int64_t)PANEL_ROWS * gt.num_panels, bp);
@@ -691,12 +721,13 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
   const int64_t col = bp.col;
   const bool valid = col < wa;
   const int64_t total_padded = (int64_t)PANEL_ROWS * gt.num_panels;
-  float s_dx = 1.0f, s_act = 1.0f;
+  float s_dx = 1.0f, s_dx_col = 1.0f, s_act = 1.0f;
   if constexpr (FMT == MGS_FMT_NVFP4) {
     write_group_scales(gt, dxq);
     write_group_scales(gt, actq);
     if (dxq.amax) s_dx = nv_encode_scale(dxq.amax[pi.g]);
-    if (actq.amax) s_act = nv_encode_scale(actq.amax[pi.g]);
+    if (dxq.amax) s_dx_col = nv_encode_scale(dxq.col_amax[pi.g]);
+    if (actq.col_data && actq.col_amax) s_act = nv_encode_scale(actq.col_amax[pi.g]);
   }
   const uint32_t up2 = (uint32_t)wa * 2u;  // byte offset of the up half in a BF16 row
 
@@ -747,7 +778,7 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
     if (dxq.row_data) quant_row<FMT>(d[i], rd, i, rv, s_dx);
   }
   if (cs_part) col_sums(cs_lds);
-  if (dxq.col_data) stage_tile<FMT>(d, st_dx, bp, s_dx);
+  if (dxq.col_data) stage_tile<FMT>(d, st_dx, bp, s_dx_col, dxq.col_rht);
   // gated: the up half in the same registers
   if constexpr (GATED) {
     const RowDst ru = row_dst<FMT>(dxq, width_in, gt.total_rows, pi.row0, lr0, wa + col, bp.lane);
@@ -767,7 +798,7 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
       if (dxq.row_data) quant_row<FMT>(d[i], ru, i, rv, s_dx);
     }
     if (cs_part) col_sums(cs_lds + 4 * BLOCK_COLS);
-    if (dxq.col_data) stage_tile<FMT>(d, st_up, bp, s_dx);
+    if (dxq.col_data) stage_tile<FMT>(d, st_up, bp, s_dx_col, dxq.col_rht);
   }
   // recompute: y = a * p -> columnwise codes of the activation
   if (actq.col_data) {
@@ -784,6 +815,7 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
         if constexpr (GATED) v[i] = act_gated<KIND>(bf16_at(xg[i], j), bf16_at(xu[GATED ? i : 0], j), aa) * p[i];
         else v[i] = act_unary<KIND>(bf16_at(xg[i], j), aa) * p[i];
       }
+      if (FMT == MGS_FMT_NVFP4 && actq.col_rht) rht16_col(v, actq.col_rht, bp.lane & 3);
       stage_col<FMT>(v, st_act, bp, j, s_act);
     }
   }
@@ -914,21 +946,41 @@ __global__ __launch_bounds__(256) void col_sum_kernel(GroupTable gt, int64_t wid
 // over the wave, LDS over the four waves) and adds one unsigned atomic max of the FP32 bits to its
 // group's entry: far fewer atomics on the per-group array (one cache line for all groups) than one
 // per wave.  BWD: the value is dx = (da/dg * dy) * p (both halves for gated kinds); else y = a * p.
+// With `rht` (bit 16 set) the pass also takes the maximum of the Hadamard-transformed columns (the
+// columnwise copy's values) into amax[E + g].
 template <int KIND, bool BWD, bool XF32>
 __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable gt,
                                                          const void* __restrict__ xp,
                                                          const uint16_t* __restrict__ dy,
                                                          const float* __restrict__ probs,
                                                          int64_t width_in, int64_t wa, int n_chunks,
-                                                         int cpw, float* __restrict__ amax) {
+                                                         int cpw, float* __restrict__ amax, uint32_t rht) {
   constexpr bool GATED = is_gated<KIND>();
-  __shared__ float wmax[4];
+  __shared__ float wmax[2][4];
   const BlockPos bp = block_pos(gt, (n_chunks + cpw - 1) / cpw);
   const PanelInfo& pi = bp.pi;
   const int lr0 = bp.lr0;
   float p[8];
   load_probs(probs, pi, gt.total_rows, lr0, p);
-  float m = 0.0f;
+  float m = 0.0f, mt = 0.0f;
+  // max |.| of a tile, and of its transformed columns
+  auto take = [&](const float (&t)[8][8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t[i][j]));
+    if (rht) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = t[i][j];
+        rht16_col(v, rht, bp.lane & 3);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mt = fmaxf(mt, fabsf(v[i]));
+      }
+    }
+  };
   const int c_end = min(n_chunks, (bp.ct + 1) * cpw);
   for (int c = bp.ct * cpw; c < c_end; ++c) {
     const int64_t col = (int64_t)c * BLOCK_COLS + 8 * bp.cc;
@@ -945,6 +997,7 @@ __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable 
         const bool rv = valid && (lr0 + i) < pi.nrows;
         dyt[i] = bld16(dyv.r, rv ? dyv.vo : MASKED, i * dyv.ld2);
       }
+      float dg[8][8], du[GATED ? 8 : 1][8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -952,33 +1005,43 @@ __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable 
           const float dd = bf16_at(dyt[i], j), g = bf16_at(xg[i], j);
           if constexpr (GATED) {
             const float u = bf16_at(xu[GATED ? i : 0], j);
-            float a, dg, du;
-            dact_gated<KIND>(g, u, aa, a, dg, du);
-            m = fmaxf(m, fabsf((dg * dd) * p[i]));
-            m = fmaxf(m, fabsf((du * dd) * p[i]));
+            float a, dgv, duv;
+            dact_gated<KIND>(g, u, aa, a, dgv, duv);
+            dg[i][j] = (dgv * dd) * p[i];
+            du[GATED ? i : 0][j] = (duv * dd) * p[i];
           } else {
-            m = fmaxf(m, fabsf((dact_unary<KIND>(g, aa) * dd) * p[i]));
+            dg[i][j] = (dact_unary<KIND>(g, aa) * dd) * p[i];
           }
         }
       }
+      take(dg);
+      if constexpr (GATED) take(du);
     } else {
       float y[8][8];
       fwd_tile_y<KIND, XF32>(aa, gt, pi, xp, nullptr, width_in, wa, lr0, col, valid, p, y);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[i][j]));
+      take(y);
     }
   }
-  m = quad_max(m);
-  m = row4_max(m);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  if (bp.lane == 0) wmax[bp.wave] = m;
+  auto reduce = [&](float v) {
+    v = quad_max(v);
+    v = row4_max(v);
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+  };
+  m = reduce(m);
+  if (rht) mt = reduce(mt);
+  if (bp.lane == 0) {
+    wmax[0][bp.wave] = m;
+    wmax[1][bp.wave] = mt;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float b = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float b = fmaxf(fmaxf(wmax[0][0], wmax[0][1]), fmaxf(wmax[0][2], wmax[0][3]));
     atomicMax(reinterpret_cast<unsigned int*>(amax + pi.g), __float_as_uint(b));
+    if (rht) {
+      const float bt = fmaxf(fmaxf(wmax[1][0], wmax[1][1]), fmaxf(wmax[1][2], wmax[1][3]));
+      atomicMax(reinterpret_cast<unsigned int*>(amax + gt.num_groups + pi.g), __float_as_uint(bt));
+    }
   }
 }
 
@@ -992,31 +1055,33 @@ int amax_cpw(const GroupTable& gt, int n_chunks) {
 template <int KIND, bool BWD>
 void launch_group_amax(hipStream_t st, const ActArgs& aa, const GroupTable& gt, const void* x, bool x_f32,
                        const uint16_t* dy, const float* probs, int64_t width_in, int64_t wa,
-                       float* amax) {
+                       float* amax, uint32_t rht) {
   const int n_chunks = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
   const int cpw = amax_cpw(gt, n_chunks);
   const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * ((n_chunks + cpw - 1) / cpw)));
   if (!BWD && x_f32)
     hipLaunchKernelGGL((group_amax_kernel<KIND, false, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
-                       width_in, wa, n_chunks, cpw, amax);
+                       width_in, wa, n_chunks, cpw, amax, rht);
   else
     hipLaunchKernelGGL((group_amax_kernel<KIND, BWD, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
-                       width_in, wa, n_chunks, cpw, amax);
+                       width_in, wa, n_chunks, cpw, amax, rht);
 }
 
+// Zeroes `amax` (E entries, 2E with rht) and takes the group maxima into it.
 template <bool BWD>
 void group_amax_dispatch(int kind, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
                          const void* x, bool x_f32, const uint16_t* dy, const float* probs,
-                         int64_t width_in, int64_t wa, float* amax) {
+                         int64_t width_in, int64_t wa, float* amax, uint32_t rht) {
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, amax, (rht ? 2 : 1) * gt.num_groups);
   switch (kind) {
-    case MGS_ACT_IDENTITY: launch_group_amax<MGS_ACT_IDENTITY, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_SRELU: launch_group_amax<MGS_ACT_SRELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_TANH_SRELU: launch_group_amax<MGS_ACT_TANH_SRELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_SWIGLU: launch_group_amax<MGS_ACT_SWIGLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_GELU: launch_group_amax<MGS_ACT_GELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_SIGMOID: launch_group_amax<MGS_ACT_SIGMOID, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
-    case MGS_ACT_GLU: launch_group_amax<MGS_ACT_GLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
-    default: launch_group_amax<MGS_ACT_CLAMPED_SWIGLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax); break;
+    case MGS_ACT_IDENTITY: launch_group_amax<MGS_ACT_IDENTITY, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
+    case MGS_ACT_SRELU: launch_group_amax<MGS_ACT_SRELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
+    case MGS_ACT_TANH_SRELU: launch_group_amax<MGS_ACT_TANH_SRELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
+    case MGS_ACT_SWIGLU: launch_group_amax<MGS_ACT_SWIGLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
+    case MGS_ACT_GELU: launch_group_amax<MGS_ACT_GELU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
+    case MGS_ACT_SIGMOID: launch_group_amax<MGS_ACT_SIGMOID, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
+    case MGS_ACT_GLU: launch_group_amax<MGS_ACT_GLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
+    default: launch_group_amax<MGS_ACT_CLAMPED_SWIGLU, BWD>(st, aa, gt, x, x_f32, dy, probs, width_in, wa, amax, rht); break;
   }
 }
 
@@ -1074,9 +1139,10 @@ hipError_t launch_act_fwd(const ActHost& act, int fmt, const GroupTable& gt, int
   // column sums alone: no quantized output, so no group amax pass and no format-specific work
   if (!out.row_data && !out.col_data) fmt = MGS_FMT_MXFP8;
   if (fmt == MGS_FMT_NVFP4) {
-    hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, group_amax, gt.num_groups);
-    group_amax_dispatch<false>(act.kind, st, aa, gt, x, x_f32, nullptr, probs, width_in, wa, group_amax);
+    const uint32_t rht = out.col_data ? out.col_rht : 0u;
+    group_amax_dispatch<false>(act.kind, st, aa, gt, x, x_f32, nullptr, probs, width_in, wa, group_amax, rht);
     out.amax = group_amax;
+    out.col_amax = rht ? group_amax + gt.num_groups : group_amax;
   }
   switch (act.kind) {
     case MGS_ACT_IDENTITY: fwd_dispatch<MGS_ACT_IDENTITY>(fmt, x_f32, grid, st, aa, gt, x, probs, width_in, out, cs, n_ct, x_copy); break;
@@ -1108,9 +1174,21 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
   const ActArgs aa = to_args(act);
   const bool quant_dx = dxq.row_data || dxq.col_data;
   if (fmt == MGS_FMT_NVFP4 && quant_dx) {
-    hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, st, dx_amax, gt.num_groups);
-    group_amax_dispatch<true>(act.kind, st, aa, gt, x, false, dy, probs, width_in, wa, dx_amax);
+    const uint32_t rht = dxq.col_data ? dxq.col_rht : 0u;
+    group_amax_dispatch<true>(act.kind, st, aa, gt, x, false, dy, probs, width_in, wa, dx_amax, rht);
     dxq.amax = dx_amax;
+    dxq.col_amax = rht ? dx_amax + gt.num_groups : dx_amax;
+  }
+  actq.col_amax = actq.amax;
+  if (fmt == MGS_FMT_NVFP4 && actq.col_data) {
+    if (actq.col_rht) {
+      // the transformed copy's amax is not the forward's saved one: take it again from x into the
+      // workspace (the same inputs as the forward's, so the same bits)
+      float* ra = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + act_bwd_rht_offset(gt, wa, width_in));
+      group_amax_dispatch<false>(act.kind, st, aa, gt, x, false, nullptr, probs, width_in, wa, ra, actq.col_rht);
+      actq.amax = ra;
+      actq.col_amax = ra + gt.num_groups;
+    }
   }
   const int n_ct = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
   const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * n_ct));
@@ -1141,8 +1219,13 @@ int64_t col_sum_part_bytes(const GroupTable& gt, int64_t width) {
   return 4 * (int64_t)(gt.num_panels / 4) * width;
 }
 
+int64_t act_bwd_rht_offset(const GroupTable& gt, int64_t wa, int64_t width_in) {
+  const int64_t o = act_bwd_cs_offset(gt.total_rows, wa) + col_sum_part_bytes(gt, width_in);
+  return (o + 255) & ~(int64_t)255;
+}
+
 int64_t act_bwd_workspace_bytes(const GroupTable& gt, int64_t wa, int64_t width_in) {
-  return act_bwd_cs_offset(gt.total_rows, wa) + col_sum_part_bytes(gt, width_in);
+  return act_bwd_rht_offset(gt, wa, width_in) + 8 * (int64_t)gt.num_groups;
 }
 
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,

@@ -82,13 +82,22 @@ int check_extent(const mgs::GroupTable& gt, int64_t width, const char* what) {
 
 bool qbuf_requested(const mgs_qbuf* q) { return q && q->data; }
 
-int check_qbuf(const mgs_qbuf* q, int32_t fmt, const char* what) {
+int check_qbuf(const mgs_qbuf* q, int32_t fmt, const char* what, bool colwise) {
   if (!qbuf_requested(q)) return MGS_OK;
   if (!q->scales) return fail(MGS_ERR_INVALID_ARG, "%s.scales is NULL", what);
   if (fmt == MGS_FMT_NVFP4 && !q->group_scale)
     return fail(MGS_ERR_INVALID_ARG, "%s.group_scale is NULL (required for NVFP4)", what);
+  if (q->rht) {
+    if (!colwise || fmt != MGS_FMT_NVFP4)
+      return fail(MGS_ERR_UNSUPPORTED, "%s.rht: the Hadamard transform applies to NVFP4 columnwise copies only", what);
+    if ((q->rht >> 16) != 1u)
+      return fail(MGS_ERR_INVALID_ARG, "%s.rht = 0x%x: bit 16 enables the transform, bits 0..15 are the signs",
+                  what, q->rht);
+  }
   return MGS_OK;
 }
+
+uint32_t qbuf_rht(const mgs_qbuf* q) { return qbuf_requested(q) ? q->rht : 0u; }
 
 int check_act(const mgs_act_params* act, mgs::ActHost* out) {
   if (!act) return fail(MGS_ERR_INVALID_ARG, "act is NULL");
@@ -119,6 +128,7 @@ mgs::QOut make_qout(const mgs_qbuf* row, const mgs_qbuf* col, int64_t width) {
     q.col_data = static_cast<uint8_t*>(col->data);
     q.col_scales = static_cast<uint8_t*>(col->scales);
     q.col_gscale = col->group_scale;
+    q.col_rht = col->rht;
   }
   q.width = width;
   return q;
@@ -176,8 +186,8 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
   if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
   if (!qbuf_requested(out_row) && !qbuf_requested(out_col))
     return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row and out_col are both empty)");
-  if ((rc = check_qbuf(out_row, fmt, "out_row"))) return rc;
-  if ((rc = check_qbuf(out_col, fmt, "out_col"))) return rc;
+  if ((rc = check_qbuf(out_row, fmt, "out_row", false))) return rc;
+  if ((rc = check_qbuf(out_col, fmt, "out_col", true))) return rc;
   if (fmt == MGS_FMT_NVFP4 && !group_amax)
     return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
   const mgs::QOut q = make_qout(out_row, out_col, wa);
@@ -205,8 +215,8 @@ int mgs_grouped_scaled_act_fwd_f32(const mgs_act_params* act, int32_t fmt, const
   if (!x_f32 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_f32 is NULL");
   if (!qbuf_requested(out_row) && !qbuf_requested(out_col) && !x_bf16_out)
     return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row, out_col and x_bf16_out are all empty)");
-  if ((rc = check_qbuf(out_row, fmt, "out_row"))) return rc;
-  if ((rc = check_qbuf(out_col, fmt, "out_col"))) return rc;
+  if ((rc = check_qbuf(out_row, fmt, "out_row", false))) return rc;
+  if ((rc = check_qbuf(out_col, fmt, "out_col", true))) return rc;
   const bool quant = qbuf_requested(out_row) || qbuf_requested(out_col);
   if (fmt == MGS_FMT_NVFP4 && quant && !group_amax)
     return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
@@ -239,20 +249,21 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
   const bool want_dxq = qbuf_requested(dx_row) || qbuf_requested(dx_col);
   if (!dx_bf16 && !want_dxq && !dprobs && !dx_col_sum && !qbuf_requested(act_col))
     return fail(MGS_ERR_INVALID_ARG, "no output requested");
-  if ((rc = check_qbuf(dx_row, fmt, "dx_row"))) return rc;
-  if ((rc = check_qbuf(dx_col, fmt, "dx_col"))) return rc;
-  if ((rc = check_qbuf(act_col, fmt, "act_col"))) return rc;
+  if ((rc = check_qbuf(dx_row, fmt, "dx_row", false))) return rc;
+  if ((rc = check_qbuf(dx_col, fmt, "dx_col", true))) return rc;
+  if ((rc = check_qbuf(act_col, fmt, "act_col", true))) return rc;
   if (fmt == MGS_FMT_NVFP4 && want_dxq && !dx_group_amax)
     return fail(MGS_ERR_INVALID_ARG, "dx_group_amax is required to quantize dx to NVFP4");
-  if (fmt == MGS_FMT_NVFP4 && qbuf_requested(act_col) && !saved_group_amax)
+  const bool act_rht = qbuf_rht(act_col) != 0;
+  if (fmt == MGS_FMT_NVFP4 && qbuf_requested(act_col) && !act_rht && !saved_group_amax)
     return fail(MGS_ERR_UNSUPPORTED,
                 "NVFP4 recompute (act_col) needs saved_group_amax, the group amax of the forward");
-  if (dprobs || dx_col_sum) {
+  if (dprobs || dx_col_sum || act_rht) {
     const int64_t need = mgs::act_bwd_workspace_bytes(gt, wa, width_in);
     if (need > 0 && (!workspace || workspace_bytes < need))
       return fail(MGS_ERR_INVALID_ARG, "%s needs a workspace of %lld bytes (got %lld%s)",
-                  dprobs ? "dprobs" : "dx_col_sum", (long long)need, (long long)workspace_bytes,
-                  workspace ? "" : ", NULL");
+                  dprobs ? "dprobs" : dx_col_sum ? "dx_col_sum" : "a transformed act_col", (long long)need,
+                  (long long)workspace_bytes, workspace ? "" : ", NULL");
   }
   mgs::QOut dxq = make_qout(dx_row, dx_col, width_in);
   mgs::QOut aq = make_qout(nullptr, act_col, wa);
@@ -291,8 +302,8 @@ int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width
   if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
   if (!qbuf_requested(out_row) && !qbuf_requested(out_col) && !col_sum)
     return fail(MGS_ERR_INVALID_ARG, "no output requested (out_row, out_col and col_sum are all empty)");
-  if ((rc = check_qbuf(out_row, fmt, "out_row"))) return rc;
-  if ((rc = check_qbuf(out_col, fmt, "out_col"))) return rc;
+  if ((rc = check_qbuf(out_row, fmt, "out_row", false))) return rc;
+  if ((rc = check_qbuf(out_col, fmt, "out_col", true))) return rc;
   const bool quant = qbuf_requested(out_row) || qbuf_requested(out_col);
   if (fmt == MGS_FMT_NVFP4 && quant && !group_amax)
     return fail(MGS_ERR_INVALID_ARG, "group_amax is required for NVFP4 (per-group amax pass)");
@@ -383,6 +394,7 @@ int mgs_grouped_gemm_mx_fprop_act(const mgs_groups* groups, int64_t m, int64_t n
     return fail(MGS_ERR_INVALID_ARG, "unknown act_input %d", act_input);
   if (!out_row || !out_row->data || !out_row->scales)
     return fail(MGS_ERR_INVALID_ARG, "out_row (data, scales) is NULL");
+  if (out_row->rht) return fail(MGS_ERR_UNSUPPORTED, "out_row.rht: the Hadamard transform applies to columnwise copies");
   mgs::GroupTable gt;
   int64_t rows = 0;
   if ((rc = build_groups(groups, &gt, &rows))) return rc;

@@ -39,6 +39,10 @@ struct QOut {
   float* col_gscale;
   const float* amax;  // NVFP4: per-group amax the encode scale derives from
   int64_t width;
+  // NVFP4 columnwise copy: its per-group amax (the transformed values' with col_rht, else amax) and
+  // the Hadamard transform (bit 16: on; bits 0..15: signs)
+  const float* col_amax;
+  uint32_t col_rht;
 };
 
 struct ActHost {
@@ -99,6 +103,7 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
                           QOut dxq, float* dx_amax, float* dprobs, float* dx_col_sum, void* workspace,
                           QOut actq, hipStream_t stream);
 int64_t act_bwd_cs_offset(int64_t rows, int64_t wa);
+int64_t act_bwd_rht_offset(const GroupTable& gt, int64_t wa, int64_t width_in);
 int64_t col_sum_part_bytes(const GroupTable& gt, int64_t width);
 int64_t act_bwd_workspace_bytes(const GroupTable& gt, int64_t wa, int64_t width_in);
 

@@ -21,6 +21,10 @@ Sources:
     forward writes no columnwise copy (recompute on, or no FC2 weight gradient): FC1's epilogue stores
     the BF16 FC1 output and FC2's quantized input in one launch, bit for bit what the separate pass
     writes from the same values (its FP32 value with `fc1_fp32_act`, else its BF16 rounding).
+  * same page, deviation table: its NVFP4 rows were measured with a recipe it names NVFP4_RHT.
+    `rht_signs` (NVFP4; a 16-bit sign mask) applies the random Hadamard transform to the columnwise
+    copies of the four weight-gradient operands (X1, A, dY2, dY1), all with the same signs, so both
+    weight-gradient GEMMs multiply transformed operands whose product is unchanged.
   * page "[PyTorch] Enable fused activation recompute for ScaledTanhSReLU", Description: with
     activation recompute the forward keeps only the BF16 FC1 output and the backward regenerates FC2's
     input from it; forward, dgrad, dprobs and FC1 wgrad are unchanged; memory drops between forward and
@@ -43,7 +47,7 @@ GATED = ("swiglu", "clamped_swiglu", "glu")
 class ExpertMLP:
     def __init__(self, kind, fmt, w1, w2, b1=None, b2=None, recompute=False, delay_wgrad=False,
                  s=2.0, limit=7.0, alpha=1.0, beta=0.0, grad_x1=True, grad_probs=True, grad_fc1=True,
-                 grad_fc2=True, fc1_fp32_act=False, fuse_fc1_act=False):
+                 grad_fc2=True, fc1_fp32_act=False, fuse_fc1_act=False, rht_signs=None):
         self.kind, self.fmt = kind, fmt
         self.w1, self.w2, self.b1, self.b2 = w1, w2, b1, b2
         self.e, self.f_in, self.h = w1.shape
@@ -53,6 +57,8 @@ class ExpertMLP:
         self.recompute, self.delay_wgrad = recompute, delay_wgrad
         self.fc1_fp32_act = fc1_fp32_act
         self.fuse_fc1_act = fuse_fc1_act
+        assert rht_signs is None or fmt == "nvfp4", "the Hadamard transform is an NVFP4 recipe"
+        self.rht = rht_signs
         self.fused_fc1_calls = 0  # forwards whose FC1 GEMM ran the activation in its epilogue
         # which gradients the backward produces (parameters of FC1 / FC2 = weight and bias)
         self.grad_x1, self.grad_probs = grad_x1, grad_probs
@@ -67,15 +73,15 @@ class ExpertMLP:
         self.trace = {"fwd_act_col": 0, "bwd_act_col": 0}
 
     # ------------------------------------------------------------------ helpers
-    def _quant(self, x, splits, width, row=True, col=True):
+    def _quant(self, x, splits, width, row=True, col=True, rht=None):
         qr = N.QTensor(self.fmt, False, splits, width) if row else None
-        qc = N.QTensor(self.fmt, True, splits, width) if col else None
-        amax = torch.empty(len(splits), dtype=torch.float32, device="cuda") if self.fmt == "nvfp4" else None
-        N.grouped_mx_quantize(self.fmt, splits, width, x, qr, qc, amax)
+        qc = N.QTensor(self.fmt, True, splits, width, rht=rht) if col else None
+        N.grouped_mx_quantize(self.fmt, splits, width, x, qr, qc, self._amax_buf(len(splits), col and rht is not None))
         return qr, qc
 
-    def _amax_buf(self, n):
-        return torch.empty(n, dtype=torch.float32, device="cuda") if self.fmt == "nvfp4" else None
+    def _amax_buf(self, n, rht=False):
+        """NVFP4 per-group amax: E entries, 2E when a columnwise copy is Hadamard-transformed."""
+        return torch.empty(2 * n if rht else n, dtype=torch.float32, device="cuda") if self.fmt == "nvfp4" else None
 
     # ------------------------------------------------------------------ forward
     def forward(self, x1, probs, splits):
@@ -83,13 +89,13 @@ class ExpertMLP:
         m = x1.shape[0]
         fmt = self.fmt
         wsplit1, wsplit2 = [f_in] * e, [h] * e
-        x1_row, x1_col = self._quant(x1, splits, h, col=self.grad_fc1)       # FC1 fprop / FC1 wgrad
+        x1_row, x1_col = self._quant(x1, splits, h, col=self.grad_fc1, rht=self.rht)  # FC1 fprop / wgrad
         w1_row, w1_col = self._quant(self.w1.view(e * f_in, h), wsplit1, h,  # fprop / dgrad copies
                                      col=self.grad_x1)
         y1 = torch.empty((m, f_in), dtype=torch.bfloat16, device="cuda")
         a_row = N.QTensor(fmt, False, splits, f)
-        a_col = None if (self.recompute or not self.grad_fc2) else N.QTensor(fmt, True, splits, f)
-        a_amax = self._amax_buf(e)
+        a_col = None if (self.recompute or not self.grad_fc2) else N.QTensor(fmt, True, splits, f, rht=self.rht)
+        a_amax = self._amax_buf(e, a_col is not None and self.rht is not None)
         if self.fuse_fc1_act and fmt == "mxfp8" and self.kind not in GATED and a_col is None:
             N.grouped_gemm_mx_fprop_act(splits, m, f_in, h, x1_row, w1_row, y1, self.act, probs, a_row,
                                         bias=self.b1, act_input="fp32" if self.fc1_fp32_act else "bf16")
@@ -131,10 +137,11 @@ class ExpertMLP:
         g1, g2, below = self.grad_fc1, self.grad_fc2, self.grad_below_fc2
         # dY2 quantized for FC2's dgrad and wgrad; FC2's bias gradient (its column sums) in the same pass
         dy2_row = N.QTensor(fmt, False, splits, h) if below else None
-        dy2_col = N.QTensor(fmt, True, splits, h) if g2 else None
+        dy2_col = N.QTensor(fmt, True, splits, h, rht=self.rht) if g2 else None
         db2 = torch.empty((e, h), dtype=torch.float32, device="cuda") if (g2 and self.b2 is not None) else None
         if below or g2:
-            N.grouped_mx_quantize(fmt, splits, h, dy2, dy2_row, dy2_col, self._amax_buf(e), col_sum=db2,
+            N.grouped_mx_quantize(fmt, splits, h, dy2, dy2_row, dy2_col,
+                                  self._amax_buf(e, g2 and self.rht is not None), col_sum=db2,
                                   workspace=self._workspace(N.quantize_workspace_bytes(splits, h)))
         a_col = c["a_col"]
         grads = {}
@@ -146,14 +153,15 @@ class ExpertMLP:
             # FC1's bias gradient: column sums of the dense BF16 dY1, taken inside the activation backward
             db1 = torch.empty((e, f_in), dtype=torch.float32, device="cuda") if (g1 and self.b1 is not None) else None
             dy1_row = N.QTensor(fmt, False, splits, f_in) if self.grad_x1 else None
-            dy1_col = N.QTensor(fmt, True, splits, f_in) if g1 else None
+            dy1_col = N.QTensor(fmt, True, splits, f_in, rht=self.rht) if g1 else None
             dprobs = torch.empty(m, dtype=torch.float32, device="cuda") if self.grad_probs else None
             if self.recompute and g2:
-                a_col = N.QTensor(fmt, True, splits, f)
+                a_col = N.QTensor(fmt, True, splits, f, rht=self.rht)
                 self.trace["bwd_act_col"] += 1
             N.grouped_scaled_act_bwd(self.act, fmt, splits, f_in, c["y1"], da, c["probs"],
                                      dx_row=dy1_row, dx_col=dy1_col,
-                                     dx_group_amax=self._amax_buf(e) if (dy1_row is not None or dy1_col is not None) else None,
+                                     dx_group_amax=self._amax_buf(e, g1 and self.rht is not None)
+                                     if (dy1_row is not None or dy1_col is not None) else None,
                                      dprobs=dprobs, dx_col_sum=db1,
                                      act_col=a_col if (self.recompute and g2) else None,
                                      saved_group_amax=c["a_amax"],
@@ -169,10 +177,10 @@ class ExpertMLP:
         elif self.recompute and g2:
             # nothing below FC2 needs a gradient: FC2's columnwise input is regenerated from the saved
             # BF16 FC1 output by a forward launch that requests only that output (the same bits)
-            a_col = N.QTensor(fmt, True, splits, f)
+            a_col = N.QTensor(fmt, True, splits, f, rht=self.rht)
             self.trace["bwd_act_col"] += 1
             N.grouped_scaled_act_fwd(self.act, fmt, splits, f_in, c["y1"], c["probs"], None, a_col,
-                                     self._amax_buf(e))
+                                     self._amax_buf(e, self.rht is not None))
         # what the weight gradients consume stays alive until backward_dw (possibly delayed)
         self.pending_wgrad = dict(splits=splits, m=m, dy2_col=dy2_col, a_col=a_col if g2 else None,
                                   dy1_col=dy1_col, x1_col=c["x1_col"] if g1 else None, db1=db1, db2=db2)

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_symbols():
         assert hasattr(lib, name), name
     assert set(_native.EXPORTED) == set(_declared_symbols())
-    assert _native.abi_version() == 5
+    assert _native.abi_version() == 6
 
 
 def test_qtensor_nbytes_layouts():
@@ -121,14 +121,16 @@ def _padded_rows(splits):
 
 def test_workspace_bytes():
     """Closed forms: dprobs partials (one FP32 per row and 128-column tile, rounded up to 256 bytes)
-    followed by one FP32 column partial per 128-token block of the columnwise-padded rows."""
+    followed by one FP32 column partial per 128-token block of the columnwise-padded rows, then (at
+    the next 256-byte boundary) 2 E FP32 group maxima for a Hadamard-transformed recompute."""
     from moe_grouped_scaled_amd import _native as N
     for kind, w_in, wa in (("srelu", 4096, 4096), ("swiglu", 4096, 2048), ("identity", 96, 96)):
         for splits in ([64, 128, 32, 32], [0, 1, 31, 33, 64], [2048] * 16, [0, 0]):
             m = sum(splits)
             dp = -(-(4 * m * -(-wa // 128)) // 256) * 256
             cs = 4 * (_padded_rows(splits) // 128) * w_in
-            assert N.act_bwd_workspace_bytes(N.act_params(kind), splits, w_in) == dp + cs
+            rht = -(-(dp + cs) // 256) * 256 + 8 * len(splits)
+            assert N.act_bwd_workspace_bytes(N.act_params(kind), splits, w_in) == rht
             assert N.quantize_workspace_bytes(splits, wa) == 4 * (_padded_rows(splits) // 128) * wa
     _expect(-2, N.act_bwd_workspace_bytes, N.act_params("swiglu"), [32], 96)
     _expect(-2, N.quantize_workspace_bytes, [32], 40)
@@ -177,6 +179,26 @@ def test_argument_validation_fprop_act_and_f32_forward():
     _expect(-1, f, srelu, "mxfp8", [32], 64, x, None, stream=0, match="no output")
     _expect(-1, f, srelu, "nvfp4", [32], 64, x, None, q, stream=0, match="group_amax")
     _expect(-2, f, srelu, "mxfp8", [32], 48, x, None, q, stream=0, match="multiple of 32")
+
+
+def test_argument_validation_rht():
+    """The Hadamard transform is for NVFP4 columnwise copies; bit 16 enables it."""
+    from moe_grouped_scaled_amd import _native as N
+    import torch
+    act = N.act_params("srelu")
+    x = torch.empty(1, dtype=torch.bfloat16)
+    amax = torch.empty(2, dtype=torch.float32)
+    col = N.QBuf(FAKE, FAKE, FAKE, N.RHT_ON | 0x1234)
+    row = N.QBuf(FAKE, FAKE, FAKE, N.RHT_ON | 0x1234)
+    bad = N.QBuf(FAKE, FAKE, FAKE, 0x1234)
+    f = N.grouped_scaled_act_fwd
+    _expect(-3, f, act, "nvfp4", [32], 64, x, None, out_row=row, group_amax=amax, stream=0, match="columnwise")
+    _expect(-3, f, act, "mxfp8", [32], 64, x, None, out_col=col, stream=0, match="NVFP4")
+    _expect(-1, f, act, "nvfp4", [32], 64, x, None, out_col=bad, group_amax=amax, stream=0, match="bit 16")
+    q = N.grouped_mx_quantize
+    _expect(-3, q, "nvfp4", [32], 64, x, out_row=row, group_amax=amax, stream=0, match="columnwise")
+    b = N.grouped_scaled_act_bwd
+    _expect(-1, b, act, "nvfp4", [32], 64, x, x, None, act_col=col, workspace=None, stream=0, match="workspace")
 
 
 def test_last_error_is_cleared_on_success():

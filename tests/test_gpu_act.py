@@ -471,3 +471,80 @@ def test_col_sum(N):
         ref = xv[off[g]:off[g + 1]].sum(axis=0)
         bound = (splits[g] + 1) * 2.0 ** -24 * np.abs(xv[off[g]:off[g + 1]]).sum(axis=0) + 1e-30
         assert np.all(np.abs(got[g] - ref) <= bound)
+
+
+RHT_MASK = 0x6B35
+RHT_CASES = [
+    # (kind, splits, width_in, x std): identity is the plain grouped quantize
+    ("identity", [0, 1, 31, 33, 64], 64, 1.0),
+    ("srelu", [128, 0, 37], 512, 1.5),
+    ("tanh_srelu", [512, 512, 512, 512], 1024, 1.5),
+    ("swiglu", [100, 70], 1024, 1.0),
+]
+
+
+def _rht_col_check(fmt, got_data, got_scales, got_gs, got_amax, ref, splits, width):
+    """Columnwise transformed copy against the oracle's: group amax and S_dec to FP32 rounding of the
+    transform (the GPU sums in FP32, the oracle in FP64), codes by the quantized-tolerance criterion."""
+    assert np.allclose(got_amax, ref["col_group_amax"], rtol=1e-5, atol=0)
+    assert np.allclose(got_gs, ref["col_group_scale"], rtol=1e-5, atol=0)
+    compare_quantized(fmt, _col_view(fmt, got_data, got_scales, splits, width, ref["col_group_scale"]),
+                      _col_view(fmt, ref["col_data"], ref["col_scales"], splits, width, ref["col_group_scale"]))
+
+
+@pytest.mark.parametrize("kind,splits,width_in,std", RHT_CASES)
+def test_act_fwd_rht_columnwise_parity(N, kind, splits, width_in, std):
+    """NVFP4 forward with the Hadamard-transformed columnwise copy (the NVFP4_RHT recipe): the
+    rowwise copy and its amax are untouched (bit-exact for identity / SReLU), the columnwise copy
+    matches the oracle's transform + quantization, its amax at entries E..2E-1."""
+    import torch
+    d = workloads.act_case(kind, splits, width_in, seed=17, std=std, with_dy=False)
+    wa = A.out_width(kind, width_in)
+    e = len(splits)
+    qr, qc = N.QTensor("nvfp4", False, splits, wa), N.QTensor("nvfp4", True, splits, wa, rht=RHT_MASK)
+    amax = torch.empty(2 * e, dtype=torch.float32, device="cuda")
+    if kind == "identity":
+        N.grouped_mx_quantize("nvfp4", splits, width_in, to_dev_bf16(d["x"]), qr, qc, amax)
+    else:
+        N.grouped_scaled_act_fwd(N.act_params(kind, **_params(kind)), "nvfp4", splits, width_in,
+                                 to_dev_bf16(d["x"]), to_dev(d["p"]), qr, qc, amax)
+    torch.cuda.synchronize()
+    p = np.ones(int(np.sum(splits))) if kind == "identity" else d["p"].astype(np.float64)
+    y = A.scaled_act_fwd(kind, bf16_f64(d["x"]), p, **_params(kind))
+    ref = Q.quantize_grouped(y, splits, "nvfp4", rht=RHT_MASK)
+    am = f32(amax)
+    exact = kind in EXACT_KINDS
+    check_fwd("nvfp4", kind, {"row_data": u8(qr.data), "row_scales": u8(qr.scales), "row_gs": f32(qr.group_scale),
+                              "amax": am[:e]}, ref, splits, wa, exact)
+    _rht_col_check("nvfp4", u8(qc.data), u8(qc.scales), f32(qc.group_scale), am[e:], ref, splits, wa)
+
+
+@pytest.mark.parametrize("kind", ["srelu", "swiglu"])
+def test_act_bwd_rht_columnwise_and_recompute(N, kind):
+    """NVFP4 backward with transformed copies: dL/dx columnwise against the oracle, and the recomputed
+    FC2 input (its amax taken again from x in the backward) byte-identical to the forward's
+    transformed columnwise copy."""
+    import torch
+    splits = [37, 0, 256, 95]
+    width_in = 1024 if kind in A.GATED else 512
+    wa = A.out_width(kind, width_in)
+    e = len(splits)
+    d = workloads.act_case(kind, splits, width_in, seed=33)
+    act = N.act_params(kind, **_params(kind))
+    x, p, dy = to_dev_bf16(d["x"]), to_dev(d["p"]), to_dev_bf16(d["dy"])
+    fr, fc = N.QTensor("nvfp4", False, splits, wa), N.QTensor("nvfp4", True, splits, wa, rht=RHT_MASK)
+    famax = torch.empty(2 * e, dtype=torch.float32, device="cuda")
+    N.grouped_scaled_act_fwd(act, "nvfp4", splits, width_in, x, p, fr, fc, famax)
+    dxc = N.QTensor("nvfp4", True, splits, width_in, rht=RHT_MASK)
+    ac = N.QTensor("nvfp4", True, splits, wa, rht=RHT_MASK)
+    dxa = torch.empty(2 * e, dtype=torch.float32, device="cuda")
+    ws = torch.empty(N.act_bwd_workspace_bytes(act, splits, width_in), dtype=torch.uint8, device="cuda")
+    N.grouped_scaled_act_bwd(act, "nvfp4", splits, width_in, x, dy, p, dx_col=dxc, dx_group_amax=dxa,
+                             act_col=ac, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(ac.data), u8(fc.data))
+    assert np.array_equal(u8(ac.scales), u8(fc.scales))
+    assert np.array_equal(f32(ac.group_scale), f32(fc.group_scale))
+    dx32, _ = A.scaled_act_bwd(kind, bf16_f64(d["x"]), bf16_f64(d["dy"]), d["p"].astype(np.float64), **_params(kind))
+    ref = Q.quantize_grouped(dx32, splits, "nvfp4", rowwise=False, rht=RHT_MASK)
+    _rht_col_check("nvfp4", u8(dxc.data), u8(dxc.scales), f32(dxc.group_scale), f32(dxa)[e:], ref, splits, width_in)

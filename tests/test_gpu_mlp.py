@@ -32,7 +32,7 @@ def _inputs(kind, e, splits, h, f, seed):
                 dy2=workloads.normal_bf16(rng, (m, h)), splits=np.asarray(splits, np.int64))
 
 
-def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False, fuse_fc1_act=False):
+def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False, fuse_fc1_act=False, rht=None):
     import torch
     from moe_grouped_scaled_amd.expert_mlp import ExpertMLP
     w1, w2 = to_dev_bf16(d["w1"]), to_dev_bf16(d["w2"])
@@ -40,7 +40,7 @@ def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False, fuse
     b2 = to_dev_bf16(d["b2"]) if bias else None
     x1, p, dy2 = to_dev_bf16(d["x1"]), to_dev(d["p"]), to_dev_bf16(d["dy2"])
     mlp = ExpertMLP(kind, fmt, w1, w2, b1, b2, recompute=recompute, delay_wgrad=delay,
-                    fc1_fp32_act=fc1_fp32_act, fuse_fc1_act=fuse_fc1_act)
+                    fc1_fp32_act=fc1_fp32_act, fuse_fc1_act=fuse_fc1_act, rht_signs=rht)
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated()
     y2 = mlp.forward(x1, p, list(d["splits"]))
@@ -63,15 +63,18 @@ def _run_gpu(kind, fmt, d, recompute, delay, bias=True, fc1_fp32_act=False, fuse
                                               ("srelu", "nvfp4", False), ("tanh_srelu", "nvfp4", False),
                                               ("swiglu", "mxfp8", False), ("gelu", "mxfp8", False),
                                               ("glu", "nvfp4", False), ("srelu", "mxfp8", True),
-                                              ("tanh_srelu", "nvfp4", True), ("swiglu", "mxfp8", True)])
+                                              ("tanh_srelu", "nvfp4", True), ("swiglu", "mxfp8", True),
+                                              ("srelu", "nvfp4-rht", True), ("swiglu", "nvfp4-rht", False)])
 def test_mlp_step_matches_oracle(torch_mod, kind, fmt, fp32_act):
     e, splits, h, f = 4, [64, 0, 96, 37], 128, 128
+    rht = 0x6B35 if fmt.endswith("-rht") else None
+    fmt = fmt.replace("-rht", "")
     d = _inputs(kind, e, splits, h, f, seed=3)
-    got = _run_gpu(kind, fmt, d, recompute=True, delay=True, fc1_fp32_act=fp32_act)
+    got = _run_gpu(kind, fmt, d, recompute=True, delay=True, fc1_fp32_act=fp32_act, rht=rht)
     ref = M.mlp_step(kind, fmt, list(splits), bf16_f64(d["x1"]), bf16_f64(d["w1"]), bf16_f64(d["b1"]),
                      bf16_f64(d["w2"]), bf16_f64(d["b2"]), d["p"].astype(np.float64), bf16_f64(d["dy2"]),
                      act_params={"s": 2.0} if kind == "tanh_srelu" else None,
-                     act_input="fp32" if fp32_act else "bf16", recompute=True)
+                     act_input="fp32" if fp32_act else "bf16", recompute=True, rht=rht)
     # chained quantities: the oracle's own BF16 / quantization roundings feed its later steps, so rare
     # bin flips propagate; relative RMS stays far below the quantization error itself
     tol = {"y2": 5e-3, "dx1": 1e-2, "dprobs": 1e-2, "dw1": 1e-2, "dw2": 5e-3, "db1": 1e-2, "db2": 1e-5}
@@ -88,6 +91,7 @@ def test_mlp_step_matches_oracle(torch_mod, kind, fmt, fp32_act):
 
 TWINS = [(k, f, a) for a in (False, True) for k, f in (("srelu", "mxfp8"), ("tanh_srelu", "mxfp8"),
                                                           ("srelu", "nvfp4"), ("tanh_srelu", "nvfp4"))]
+TWINS += [("srelu", "nvfp4-rht", True), ("tanh_srelu", "nvfp4-rht", True)]
 
 
 @pytest.mark.parametrize("kind,fmt,fp32_act", TWINS)
@@ -103,9 +107,11 @@ def test_recompute_twin_full_size(torch_mod, kind, fmt, fp32_act):
     Hadamard-transformed recipe); max-abs grows with the tensor size and is printed only."""
     e, h, f = 16, 4096, 4096
     splits = [2048] * e
+    rht = 0x6B35 if fmt.endswith("-rht") else None   # the page's NVFP4 rows are its NVFP4_RHT recipe
+    fmt = fmt.replace("-rht", "")
     d = _inputs(kind, e, splits, h, f, seed=5)
-    off = _run_gpu(kind, fmt, d, recompute=False, delay=True, fc1_fp32_act=fp32_act)
-    on = _run_gpu(kind, fmt, d, recompute=True, delay=True, fc1_fp32_act=fp32_act)
+    off = _run_gpu(kind, fmt, d, recompute=False, delay=True, fc1_fp32_act=fp32_act, rht=rht)
+    on = _run_gpu(kind, fmt, d, recompute=True, delay=True, fc1_fp32_act=fp32_act, rht=rht)
     for k in ("y2", "dx1", "dprobs", "dw1", "db1", "db2"):
         assert np.array_equal(on[k], off[k]), k
     with open(os.path.join(GOLDEN, "recompute_deviation_gb300.json")) as fh:
@@ -114,7 +120,7 @@ def test_recompute_twin_full_size(torch_mod, kind, fmt, fp32_act):
     dev = rel_rms(on["dw2"], off["dw2"])
     diff = on["dw2"] - off["dw2"]
     rms = np.sqrt(np.mean(off["dw2"] ** 2))
-    print(kind, fmt, "fp32 act" if fp32_act else "bf16 act", "FC2 wgrad deviation: rms %.3f%%, max-abs %.1f%%"
+    print(kind, fmt, "rht" if rht else "", "fp32 act" if fp32_act else "bf16 act", "FC2 wgrad deviation: rms %.3f%%, max-abs %.1f%%"
           % (100 * dev, 100 * np.max(np.abs(diff)) / rms))
     if fp32_act:
         assert dev > 0
