@@ -170,6 +170,8 @@ def main():
     ap.add_argument("--fc1-act", default="epilogue", choices=["epilogue", "separate"],
                     help="run the forward activation + quantization in FC1's GEMM epilogue (MXFP8, unary "
                          "activations) or as its own fused pass")
+    ap.add_argument("--rht", type=lambda v: int(v, 0), default=None,
+                    help="NVFP4: Hadamard-transform the weight-gradient operands with this 16-bit sign mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -209,7 +211,8 @@ def main():
     held = {}
     for rc in (False, True):
         mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=rc, delay_wgrad=True, s=2.0,
-                        fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue")
+                        fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue",
+                        rht_signs=args.rht)
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         y = mlp.forward(x1, p, splits)
@@ -222,7 +225,8 @@ def main():
     drop_closed = col_rows * f + col_rows * f // 32 if args.fmt == "mxfp8" else col_rows * f // 2 + col_rows * f // 16
 
     mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=True, delay_wgrad=True, s=2.0,
-                    fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue")
+                    fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue",
+                    rht_signs=args.rht)
 
     def step():
         mlp.forward(x1, p, splits)
@@ -313,6 +317,7 @@ def main():
                                    ", activation in FC1's epilogue" if fused_fc1 else ""),
                    "experts": e, "tokens": m, "hidden": h, "ffn": f, "recipe": args.fmt, "act": args.act,
                    "act_input": "fp32" if args.fc1_fp32_act else "bf16",
+                   "rht": None if args.rht is None else hex(args.rht),
                    "fc1_act": "epilogue" if fused_fc1 else "separate"},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": gemm_tflops / peak, "traffic": measured_traffic(args.fmt)},
