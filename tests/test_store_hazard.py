@@ -63,3 +63,24 @@ def test_no_wide_store_data_overwritten_next(src, tmp_path):
                    check=True, stdout=subprocess.PIPE, stderr=subprocess.PIPE)
     bad = _violations(out.read_text())
     assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", ["act_quant.hip", "gemm_mx.hip"])
+def test_no_kernel_uses_scratch(src, tmp_path):
+    """Every kernel keeps its values in registers: no spills to scratch.  In the GEMM a spill is not
+    only slow: the accumulators live in AGPRs written by MFMAs issued as inline assembly, whose
+    completion the compiler does not track, so a spill copy taken before the explicit drain reads
+    unfinished results (seen once: a change that let the compiler copy the accumulator array out
+    gave 1472 bytes of scratch per lane and wrong GEMM results)."""
+    from moe_grouped_scaled_amd.build import FLAGS, HIPCC
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    flags = [f for f in FLAGS if not f.startswith("-W")]
+    res = subprocess.run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", str(tmp_path / "k.o"),
+                          "-Rpass-analysis=kernel-resource-usage"], check=True, stdout=subprocess.PIPE,
+                         stderr=subprocess.STDOUT, text=True)
+    names = re.findall(r"Function Name: (\S+)", res.stdout)
+    scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", res.stdout)]
+    assert names and len(names) == len(scratch)
+    bad = [(n, s) for n, s in zip(names, scratch) if s]
+    assert not bad, bad[:5]
