@@ -177,7 +177,7 @@ def main():
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (expert-parallel "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (expert-parallel "
               "sharding is a design note); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
