@@ -128,12 +128,13 @@ def measured_traffic(fmt):
 
 def cpu_baseline(kind, fmt, seed=0):
     """The oracle's expert-MLP step on a bounded sample of the workload: one of the 16 experts with
-    1024 tokens, full hidden 4096 / ffn 4096 weights.  Returns the oracle's GEMM TFLOP/s."""
+    1536 tokens, full hidden 4096 / ffn 4096 weights (about 10 s on the host).  Returns the oracle's GEMM
+    TFLOP/s."""
     from oracle import mlp as M
     import workloads
     from oracle.codecs import bf16_bits_to_f64
     rng = np.random.default_rng(seed)
-    e, tok, h, f = 1, 1024, 4096, 4096
+    e, tok, h, f = 1, 1536, 4096, 4096
     splits = [tok] * e
     m = e * tok
     x1 = bf16_bits_to_f64(workloads.normal_bf16(rng, (m, h)))
