@@ -579,12 +579,13 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
 
   // One K step from stage buffer `stg` while the next step's loads go into the other buffer: four of
   // its load instructions before the fragment reads, the scales after the first MFMA and the other
-  // twelve after every second MFMA (a pace the load pipeline absorbs without stalling the wave).
+  // twelve after every third MFMA, spread over the first 36 of the step's 64 (a pace the load pipeline
+  // absorbs without stalling the wave; every second MFMA measured ~1% slower).
   // A fragment row 0 and the eight B fragments are read up front (the first MFMA waits only for the
   // first of them); A fragments then stream: the reads of fragment row fm + 1 are issued between the
   // first MFMAs of row fm, so most LDS reads overlap the matrix cores and 80 fragment registers are
   // live.  With `tail`, K chunks at or past `rem` are zeroed.
-  constexpr int PRE_LOADS = 4, LOAD_PACE = 2;
+  constexpr int PRE_LOADS = 4, LOAD_PACE = 3;
   auto step = [&](const uint8_t* stg, bool tail, int64_t rem, int next_st, uint8_t* next_stg) {
     if (next_st >= 0)
       for (int n = 0; n < PRE_LOADS; ++n) issue_one(next_st, next_stg, n);
