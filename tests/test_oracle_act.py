@@ -106,11 +106,10 @@ def test_sigmoid_and_glu_values():
     assert abs(dg[0, 0] - 2.0 * 0.25) < 1e-15 and abs(dg[0, 1] + 4.0 * 0.75 * 0.25) < 1e-14
 
 
-@pytest.mark.parametrize("kind", KINDS)
-@pytest.mark.parametrize("params", [{}, {"alpha": 1.702, "beta": 1.0}])
+# alpha / beta exist for clamped SwiGLU only
+@pytest.mark.parametrize("kind,params", [(k, {}) for k in KINDS]
+                         + [(A.CLAMPED_SWIGLU, {"alpha": 1.702, "beta": 1.0})])
 def test_gradients_match_central_differences(kind, params):
-    if params and kind != A.CLAMPED_SWIGLU:
-        pytest.skip("alpha/beta only apply to clamped SwiGLU")
     rng = np.random.default_rng(1)
     x = rng.standard_normal((4, 16)) * 3.0
     # keep away from kinks (0 for relu, +-L for the clamp)
