@@ -860,9 +860,9 @@ void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
     const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(o + 2), 0, 0);
     return lo | (hi << 16);
   };
-  // next step's loads: 2 before the fragment reads, then one after every fourth MFMA (issuing them
-  // early measured best: one per 16 MFMAs was 4% slower, one per 8 about 1%)
-  constexpr int PRE = 2, PACE = 4;
+  // next step's loads: 2 before the fragment reads, then one after every third MFMA (issuing them
+  // early measured best: one per 16 MFMAs was 5% slower, one per 8 about 2%, one per 4 0.7%, one per 2 1%)
+  constexpr int PRE = 2, PACE = 3;
   auto step = [&](const uint8_t* stg, bool tail, int64_t rem, int next_st, uint8_t* next_stg, int st) {
     if (next_st >= 0)
       for (int n = 0; n < PRE; ++n) issue_one(next_st, next_stg, n);
