@@ -1045,11 +1045,13 @@ __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable 
   }
 }
 
-// chunks per workgroup of the amax pass: about 1024 workgroups in all (at most 32 chunks each)
+// chunks per workgroup of the amax pass: about 1024 workgroups for small inputs, at most 8 chunks each
+// for large ones (measured on 32k x 4096 and 64k x 4096 inputs: 4 or 16 chunks per workgroup are both
+// slower than 8)
 int amax_cpw(const GroupTable& gt, int n_chunks) {
   const int64_t units = (int64_t)(gt.num_panels / 4) * n_chunks;
   int64_t c = units / 1024;
-  return (int)(c < 1 ? 1 : (c > 32 ? 32 : c));
+  return (int)(c < 1 ? 1 : (c > 8 ? 8 : c));
 }
 
 template <int KIND, bool BWD>
