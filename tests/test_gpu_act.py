@@ -443,6 +443,36 @@ def test_quantize_col_sum(N, fmt):
     assert np.all(a["cs"][1] == 0.0)
 
 
+@pytest.mark.parametrize("splits", [[3000, 5000, 8384], [5000, 0, 7777, 12000, 7991]])
+def test_nvfp4_group_amax_partial_chunk_runs(N, splits):
+    """The NVFP4 amax pass gives each workgroup a run of up to 8 column chunks of 128; at width 4480
+    (35 chunks) and 16k / 32k tokens the runs are 4 or 8 long and each row block's last run holds 3.
+    Every group's maximum is planted in a different place, half of them inside that short last run,
+    and the exact per-group max |x| (and the S_dec derived from it) must come back."""
+    import torch
+    width = 35 * 128
+    rng = np.random.default_rng(5)
+    m = int(sum(splits))
+    x = workloads.normal_bf16(rng, (m, width), 1.0)
+    off = Q.group_offsets(splits)
+    for g in range(len(splits)):
+        if splits[g] == 0:
+            continue
+        r = int(off[g]) + int(rng.integers(0, splits[g]))
+        c = int(rng.integers(32 * 128, width)) if g % 2 == 0 else int(rng.integers(0, 32 * 128))
+        x[r, c] = 0x4100 + (g << 4) + (0x8000 if g % 3 == 1 else 0)  # +-(8 + g), above any N(0, 1) sample here
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    ref = np.array([np.max(np.abs(xf[off[g]:off[g + 1]])) if splits[g] else 0.0 for g in range(len(splits))],
+                   dtype=np.float32)
+    assert [float(ref[g]) for g in range(len(splits)) if splits[g]] == [8.0 + g for g in range(len(splits)) if splits[g]]
+    qr = N.QTensor("nvfp4", False, splits, width)
+    amax = torch.empty(len(splits), dtype=torch.float32, device="cuda")
+    N.grouped_mx_quantize("nvfp4", splits, width, to_dev_bf16(x), qr, None, amax)
+    torch.cuda.synchronize()
+    assert np.array_equal(f32(amax), ref), (f32(amax), ref)
+    assert np.array_equal(f32(qr.group_scale), np.array([Q.nvfp4_global(a)[1] for a in ref], dtype=np.float32))
+
+
 def test_col_sums_of_all_empty_groups_are_zero(N):
     import torch
     splits, w = [0, 0, 0], 64
