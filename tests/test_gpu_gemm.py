@@ -152,6 +152,32 @@ def test_wgrad_and_accumulate(N, fmt):
     assert np.array_equal(f32(c2)[1], init[1].astype(np.float64))   # empty group left unchanged
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_wgrad_bf16_output(N, fmt):
+    """WGRAD into a BF16 weight gradient: the oracle's product rounded to BF16, per group, and zeros
+    for an empty group; a K length per group that is not a multiple of the 128-token K step."""
+    import torch
+    rng = np.random.default_rng(4)
+    splits = [0, 300, 17, 129]
+    e, m_tok, h, f = len(splits), sum(splits), 128, 224
+    dy = _f32_values(rng, (m_tok, h))
+    a = _f32_values(rng, (m_tok, f))
+    qdy = Q.quantize_grouped(dy, splits, fmt, rowwise=False)
+    qa = Q.quantize_grouped(a, splits, fmt, rowwise=False)
+    A = dev_q(N, fmt, True, splits, h, qdy)
+    B = dev_q(N, fmt, True, splits, f, qa)
+    ref = G.gemm_grouped_k(G.dequant_col_grouped(fmt, qdy["col_data"], qdy["col_scales"], splits, h, qdy.get("group_scale")),
+                           G.dequant_col_grouped(fmt, qa["col_data"], qa["col_scales"], splits, f, qa.get("group_scale")))
+    c = torch.full((e, h, f), 7.0, dtype=torch.bfloat16, device="cuda")
+    N.grouped_gemm_mx("wgrad", fmt, splits, h, f, m_tok, A, B, c)
+    torch.cuda.synchronize()
+    got = bf16_f64(bf16_host(c))
+    ref_b = bf16_f64(codecs.f32_to_bf16_bits(codecs.f32(ref).astype(np.float32)))
+    assert np.all(got[0] == 0.0)                       # empty group -> zero weight gradient
+    for g in range(1, e):
+        assert rel_rms(got[g], ref_b[g]) <= TOL, g
+
+
 def test_fc2_clamped_workload_sampled(N):
     """FC2 at the clamped-SwiGLU workload's full shape (32 experts, 65536 tokens Zipf split, ffn 2048,
     hidden 7168) on the GPU, checked on sampled output rows that the oracle computes one by one."""
