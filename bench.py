@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "fused act+MX-quant GB/s (% of HBM peak) fwd/bwd; grouped MX GEMM TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"mxfp8": 5000.0, "nvfp4": 2500.0}   # FP8 dense; NVFP4 runs on the FP16 MFMA
+FC1_ACT = {"auto": "auto", "epilogue": True, "separate": False}   # --fc1-act -> ExpertMLP(fuse_fc1_act=)
 
 
 def act_fwd_bytes(m, w_in, w_a, fmt, row=True, col=False, col_rows=None):
@@ -168,9 +169,10 @@ def main():
     ap.add_argument("--fc1-fp32-act", action="store_true",
                     help="activate FC1's FP32 output in the forward (the recompute then regenerates FC2's "
                          "input from its BF16 copy)")
-    ap.add_argument("--fc1-act", default="epilogue", choices=["epilogue", "separate"],
+    ap.add_argument("--fc1-act", default="auto", choices=["auto", "epilogue", "separate"],
                     help="run the forward activation + quantization in FC1's GEMM epilogue (MXFP8, unary "
-                         "activations) or as its own fused pass")
+                         "activations) or as its own fused pass; auto: the epilogue where it is faster "
+                         "(SReLU, sigmoid)")
     ap.add_argument("--rht", type=lambda v: int(v, 0), default=None,
                     help="NVFP4: Hadamard-transform the weight-gradient operands with this 16-bit sign mask")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -212,7 +214,7 @@ def main():
     held = {}
     for rc in (False, True):
         mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=rc, delay_wgrad=True, s=2.0,
-                        fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue",
+                        fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=FC1_ACT[args.fc1_act],
                         rht_signs=args.rht)
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
@@ -226,7 +228,7 @@ def main():
     drop_closed = col_rows * f + col_rows * f // 32 if args.fmt == "mxfp8" else col_rows * f // 2 + col_rows * f // 16
 
     mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=True, delay_wgrad=True, s=2.0,
-                    fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=args.fc1_act == "epilogue",
+                    fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=FC1_ACT[args.fc1_act],
                     rht_signs=args.rht)
 
     def step():
