@@ -455,17 +455,44 @@ __device__ __forceinline__ void epilogue_256(const TileJob& j, const GemmArgs& g
                                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
       }
+      if constexpr (ACC) {
 #pragma unroll
-      for (int fn = 0; fn < 8; ++fn) {
-        const int col = wn * 128 + fn * 16 + 4 * q;
-        float v[4];
-        frag_values(j, acc[fm][fn], bw[fn], v);
-        if constexpr (ACC) {
+        for (int fn = 0; fn < 8; ++fn) {
+          const int col = wn * 128 + fn * 16 + 4 * q;
+          float v[4];
+          frag_values(j, acc[fm][fn], bw[fn], v);
           v[0] += old[fn].x; v[1] += old[fn].y; v[2] += old[fn].z; v[3] += old[fn].w;
+          if (rok && col < j.b.rows)
+            st16(j.c32 + gr * j.ldc + j.ccol0 + col, __float_as_uint(v[0]), __float_as_uint(v[1]),
+                 __float_as_uint(v[2]), __float_as_uint(v[3]));
         }
-        if (rok && col < j.b.rows)
-          st16(j.c32 + gr * j.ldc + j.ccol0 + col, __float_as_uint(v[0]), __float_as_uint(v[1]),
-               __float_as_uint(v[2]), __float_as_uint(v[3]));
+      } else {
+        // fragment pair (2b, 2b + 1) = 32 columns = one 128-byte line per row: lanes r16 and r16 ^ 8
+        // trade values so that the first store writes rows 0..7 of the 16-row block as whole lines
+        // (lane r16 < 8: its own fragment-2b chunk; r16 >= 8: the chunk of fragment 2b + 1 of row
+        // r16 - 8) and the second store rows 8..15
+        const bool hi = r16 >= 8;
+        const int rlo = wm * 128 + fm * 16 + (r16 & 7);
+        const bool ok_a = rlo < j.a.rows, ok_b = rlo + 8 < j.a.rows;
+        const int64_t ga_ = j.crow0 + rlo;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float v0[4], v1[4], rv[4];
+          frag_values(j, acc[fm][2 * b], bw[2 * b], v0);
+          frag_values(j, acc[fm][2 * b + 1], bw[2 * b + 1], v1);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) rv[t] = dpp_f<DPP_ROW_ROR8>(hi ? v0[t] : v1[t]);
+          const int col = wn * 128 + 32 * b + (hi ? 16 : 0) + 4 * q;
+          if (col < j.b.rows) {
+            float* pa_ = j.c32 + ga_ * j.ldc + j.ccol0 + col;
+            if (ok_a)
+              st16(pa_, __float_as_uint(hi ? rv[0] : v0[0]), __float_as_uint(hi ? rv[1] : v0[1]),
+                   __float_as_uint(hi ? rv[2] : v0[2]), __float_as_uint(hi ? rv[3] : v0[3]));
+            if (ok_b)
+              st16(pa_ + 8 * j.ldc, __float_as_uint(hi ? v1[0] : rv[0]), __float_as_uint(hi ? v1[1] : rv[1]),
+                   __float_as_uint(hi ? v1[2] : rv[2]), __float_as_uint(hi ? v1[3] : rv[3]));
+          }
+        }
       }
     }
   };
