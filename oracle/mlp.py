@@ -7,7 +7,8 @@ Sources:
     saving (input_, scales) for backward; backward = FC2 backward giving dL/d(act_out * scales), then
     the activation backward giving (grouped_dy, dense_dy, grad_scales), then FC1's backward.
   * [P1] Description: the step runs with bias, with all experts' weights in one tensor and with
-    delayed weight-gradient computation; activation recompute changes only what is stashed.
+    delayed weight-gradient computation; turning recompute on alters only the tensors kept between
+    forward and backward.
 
 Step, in order (each GEMM as in oracle.gemm, each quantization as in oracle.quant):
   forward : X1 -> q(row, col); W1 -> q(row) and q(col); Y1 = bf16(X1 W1_g^T + b1_g)

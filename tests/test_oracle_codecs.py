@@ -20,27 +20,34 @@ def _all_finite_bf16_values():
 def _brute_nearest(values, mags):
     """Nearest magnitude by exhaustive distance search; ties -> even index; sign re-applied.
 
-    Independent of the oracle's search: computes every distance explicitly.
+    Independent of the oracle's search: computes every distance explicitly, in chunks.  Among the
+    magnitudes at the minimal distance the even index wins when there is one (the even code of a
+    tie), else the single nearest index.  Magnitudes above 2^20 are searched as 2^20: every value at or
+    above the largest magnitude has that magnitude as its unique nearest one, and below 2^20 all the
+    float64 differences are exact (beyond it, |a - m| rounds to the same double for neighbouring m
+    and would fake ties).
     """
-    a = np.abs(values)[:, None]
-    d = np.abs(a - mags[None, :])
-    best = d.min(axis=1, keepdims=True)
-    cand = d == best
-    idx = np.empty(len(values), dtype=np.int64)
-    for i in range(len(values)):
-        c = np.flatnonzero(cand[i])
-        ev = c[c % 2 == 0]
-        idx[i] = ev[0] if len(ev) else c[0]
+    a_all = np.minimum(np.abs(np.asarray(values, np.float64)), 2.0 ** 20)
+    assert mags[-1] < 2.0 ** 20
+    idx = np.empty(len(a_all), dtype=np.int64)
+    even = (np.arange(len(mags)) % 2 == 0)[None, :]
+    for c0 in range(0, len(a_all), 8192):
+        a = a_all[c0:c0 + 8192, None]
+        d = np.abs(a - mags[None, :])
+        cand = d == d.min(axis=1, keepdims=True)
+        ce = cand & even
+        has_even = ce.any(axis=1)
+        idx[c0:c0 + 8192] = np.where(has_even, np.argmax(ce, axis=1), np.argmax(cand, axis=1))
     return idx
 
 
 @pytest.mark.parametrize("log2_scale", [-12, -6, -3, 0, 3, 6, 9])
 def test_e4m3_encode_matches_brute_force(log2_scale):
+    """Every finite BF16 pattern (65,280 of the 65,536; the other 256 are infinities and NaNs), scaled
+    by 2^log2_scale: the encoder equals the nearest-magnitude search, saturation included (beyond 448
+    the nearest magnitude is 448), sign of zero kept."""
     v = _all_finite_bf16_values() * 2.0 ** log2_scale
-    # keep magnitudes where the search is meaningful but include saturation well above 448
-    v = v[np.abs(v) < 1e6]
-    rng = np.random.default_rng(1)
-    v = rng.choice(v, size=min(len(v), 20000), replace=False)
+    assert len(v) == 65536 - 256
     mags = codecs.E4M3_MAGS
     idx = _brute_nearest(v, mags)
     want = idx | (np.signbit(v).astype(np.int64) << 7)
