@@ -11,7 +11,8 @@
  *   - Every pointer argument named *_bf16, probs, dprobs, group_amax, data, scales, group_scale, c and
  *     bias is a DEVICE pointer; mgs_groups.split_sizes and the mgs_* structs themselves are HOST memory.
  *   - The caller owns every buffer, workspaces included.  The library allocates no memory and keeps no
- *     state between calls.
+ *     state between calls, apart from the static device scratch of mgs_grouped_scaled_act_bwd_noalloc
+ *     (and the per-device address of that scratch).
  *   - Every call validates its arguments on the host, then enqueues its kernels on `stream` (a
  *     hipStream_t; NULL = the null stream) and returns without synchronizing.
  *   - A NULL output pointer (or an mgs_qbuf with data == NULL) means "not requested": it is not computed.
@@ -55,8 +56,10 @@
 extern "C" {
 #endif
 
-#define MGS_ABI_VERSION 6
+#define MGS_ABI_VERSION 7
 #define MGS_MAX_GROUPS 256
+/* Size of the static per-device scratch of mgs_grouped_scaled_act_bwd_noalloc (16 MiB). */
+#define MGS_NOALLOC_SCRATCH_BYTES ((int64_t)16 << 20)
 
 enum mgs_status {
   MGS_OK = 0,
@@ -211,6 +214,26 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
                                float* dx_col_sum, const mgs_qbuf* act_col,
                                const float* saved_group_amax, void* workspace,
                                int64_t workspace_bytes, void* stream);
+
+/* The fused backward above without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs and results (bit for bit, the same kernels) as mgs_grouped_scaled_act_bwd;
+ * the partial sums go to a static scratch array of MGS_NOALLOC_SCRATCH_BYTES (16 MiB) in device
+ * memory that each device holds from the first call on it until the process ends.  The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ *   - MGS_ERR_SHAPE when the workspace the request needs (mgs_act_bwd_workspace_bytes, counted only
+ *     when dprobs, dx_col_sum or a transformed act_col is requested) exceeds the scratch; nothing is
+ *     enqueued then.
+ *   - Every call on one device shares that device's scratch, and the scratch keeps the last call's
+ *     contents (each call writes every partial it reads and zeroes its group maxima itself): calls
+ *     that overlap on one device (other streams, other threads) race and must be serialized by the
+ *     caller. */
+int mgs_grouped_scaled_act_bwd_noalloc(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                                       int64_t width_in, const void* x_bf16, const void* dy_bf16,
+                                       const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
+                                       const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
+                                       float* dx_col_sum, const mgs_qbuf* act_col,
+                                       const float* saved_group_amax, void* stream);
 
 /* Workspace bytes mgs_grouped_scaled_act_bwd needs for dprobs, dx_col_sum and a transformed act_col:
  * roundup(roundup(4 * M * ceil(W_a / 128), 256) + 4 * (P / 128) * width_in, 256) + 8 * E,

@@ -65,6 +65,8 @@ def _load():
         "mgs_grouped_scaled_act_fwd_f32": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, pq, pq, vp, vp, vp]),
         "mgs_grouped_scaled_act_bwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, vp, vp, pq, pq, vp,
                                                       vp, vp, pq, vp, vp, i64, vp]),
+        "mgs_grouped_scaled_act_bwd_noalloc": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, vp, vp, pq, pq,
+                                                              vp, vp, vp, pq, vp, vp]),
         "mgs_act_bwd_workspace_bytes": (i64, [pact, pgr, i64]),
         "mgs_grouped_mx_quantize": (ctypes.c_int, [i32, pgr, i64, vp, pq, pq, vp, vp, vp, i64, vp]),
         "mgs_grouped_mx_quantize_workspace_bytes": (i64, [pgr, i64]),
@@ -84,7 +86,7 @@ def _load():
 LIB = _load()
 EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
             "mgs_grouped_scaled_act_fwd_f32",
-            "mgs_grouped_scaled_act_bwd", "mgs_act_bwd_workspace_bytes", "mgs_grouped_mx_quantize",
+            "mgs_grouped_scaled_act_bwd", "mgs_grouped_scaled_act_bwd_noalloc", "mgs_act_bwd_workspace_bytes", "mgs_grouped_mx_quantize",
             "mgs_grouped_mx_quantize_workspace_bytes", "mgs_grouped_gemm_mx", "mgs_grouped_gemm_mx_fprop_act",
             "mgs_grouped_col_sum")
 
@@ -219,6 +221,24 @@ def grouped_scaled_act_bwd(act, fmt, split_sizes, width_in, x, dy, probs, dx=Non
                                           _ptr(dx_group_amax), _ptr(dprobs), _ptr(dx_col_sum), aref,
                                           _ptr(saved_group_amax), _ptr(workspace), int(ws_bytes),
                                           _stream(stream)))
+
+
+def grouped_scaled_act_bwd_noalloc(act, fmt, split_sizes, width_in, x, dy, probs, dx=None, dx_row=None,
+                                   dx_col=None, dx_group_amax=None, dprobs=None, dx_col_sum=None,
+                                   act_col=None, saved_group_amax=None, stream=None):
+    """The backward with the library's static per-device scratch in place of a workspace: nothing is
+    allocated here or in the library.  Calls that overlap on one device race on that scratch."""
+    g = _GroupsArg(split_sizes)
+    _r, rref = _qref(dx_row)
+    _c, cref = _qref(dx_col)
+    _a, aref = _qref(act_col)
+    _check(LIB.mgs_grouped_scaled_act_bwd_noalloc(ctypes.byref(act), FMT[fmt], g.ref, int(width_in), _ptr(x),
+                                                  _ptr(dy), _ptr(probs), _ptr(dx), rref, cref,
+                                                  _ptr(dx_group_amax), _ptr(dprobs), _ptr(dx_col_sum), aref,
+                                                  _ptr(saved_group_amax), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MGS_NOALLOC_SCRATCH_BYTES
 
 
 def quantize_workspace_bytes(split_sizes, width):

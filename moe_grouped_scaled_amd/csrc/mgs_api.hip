@@ -8,8 +8,16 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "mgs_internal.h"
+
+// Scratch of the allocation-free backward (mgs_grouped_scaled_act_bwd_noalloc): the dprobs and
+// bias-gradient partial sums and the group maxima of a transformed recompute.  Every device the
+// library runs on holds its own copy until the process ends.  Host code never uses this name as an
+// address (on the host it is only a stand-in for the symbol): scratch_address() looks up each
+// device's copy once and every later use goes through that pointer.
+static __device__ __align__(256) uint8_t scratch[MGS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -139,6 +147,89 @@ int hip_status(hipError_t e) {
   return ok();
 }
 
+// Device address of `scratch` on the current device, taken with that device current on the first
+// call that needs it and kept per device (each device's copy has its own address).
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MGS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MGS_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch covers", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MGS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MGS_OK;
+}
+
+// The backward's validation and launch, shared by the entry point with a caller workspace and the
+// allocation-free one (whose workspace is the static scratch).
+int act_bwd_impl(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups, int64_t width_in,
+                 const void* x_bf16, const void* dy_bf16, const float* probs, void* dx_bf16,
+                 const mgs_qbuf* dx_row, const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
+                 float* dx_col_sum, const mgs_qbuf* act_col, const float* saved_group_amax,
+                 void* workspace, int64_t workspace_bytes, bool static_scratch, void* stream) {
+  mgs::ActHost ah;
+  int rc = check_act(act, &ah);
+  if (rc) return rc;
+  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
+  const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
+  if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
+  if ((rc = check_extent(gt, width_in, "width_in"))) return rc;
+  if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
+  if (!dy_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "dy_bf16 is NULL");
+  const bool want_dxq = qbuf_requested(dx_row) || qbuf_requested(dx_col);
+  if (!dx_bf16 && !want_dxq && !dprobs && !dx_col_sum && !qbuf_requested(act_col))
+    return fail(MGS_ERR_INVALID_ARG, "no output requested");
+  if ((rc = check_qbuf(dx_row, fmt, "dx_row", false))) return rc;
+  if ((rc = check_qbuf(dx_col, fmt, "dx_col", true))) return rc;
+  if ((rc = check_qbuf(act_col, fmt, "act_col", true))) return rc;
+  if (fmt == MGS_FMT_NVFP4 && want_dxq && !dx_group_amax)
+    return fail(MGS_ERR_INVALID_ARG, "dx_group_amax is required to quantize dx to NVFP4");
+  const bool act_rht = qbuf_rht(act_col) != 0;
+  if (fmt == MGS_FMT_NVFP4 && qbuf_requested(act_col) && !act_rht && !saved_group_amax)
+    return fail(MGS_ERR_UNSUPPORTED,
+                "NVFP4 recompute (act_col) needs saved_group_amax, the group amax of the forward");
+  if (dprobs || dx_col_sum || act_rht) {
+    const int64_t need = mgs::act_bwd_workspace_bytes(gt, wa, width_in);
+    if (static_scratch) {
+      if (need > MGS_NOALLOC_SCRATCH_BYTES)
+        return fail(MGS_ERR_SHAPE,
+                    "%s needs %lld bytes of scratch, more than the %lld bytes of the allocation-free "
+                    "entry point's static scratch (use mgs_grouped_scaled_act_bwd with a workspace)",
+                    dprobs ? "dprobs" : dx_col_sum ? "dx_col_sum" : "a transformed act_col", (long long)need,
+                    (long long)MGS_NOALLOC_SCRATCH_BYTES);
+      if ((rc = scratch_address(&workspace))) return rc;
+      workspace_bytes = MGS_NOALLOC_SCRATCH_BYTES;
+    }
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(MGS_ERR_INVALID_ARG, "%s needs a workspace of %lld bytes (got %lld%s)",
+                  dprobs ? "dprobs" : dx_col_sum ? "dx_col_sum" : "a transformed act_col", (long long)need,
+                  (long long)workspace_bytes, workspace ? "" : ", NULL");
+  }
+  mgs::QOut dxq = make_qout(dx_row, dx_col, width_in);
+  mgs::QOut aq = make_qout(nullptr, act_col, wa);
+  aq.amax = saved_group_amax;
+  return hip_status(mgs::launch_act_bwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
+                                        static_cast<const uint16_t*>(dy_bf16), probs,
+                                        static_cast<uint16_t*>(dx_bf16), dxq, dx_group_amax, dprobs,
+                                        dx_col_sum, workspace, aq, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,45 +324,20 @@ int mgs_grouped_scaled_act_bwd(const mgs_act_params* act, int32_t fmt, const mgs
                                float* dx_col_sum, const mgs_qbuf* act_col,
                                const float* saved_group_amax, void* workspace,
                                int64_t workspace_bytes, void* stream) {
-  mgs::ActHost ah;
-  int rc = check_act(act, &ah);
-  if (rc) return rc;
-  if (!valid_fmt(fmt)) return fail(MGS_ERR_INVALID_ARG, "unknown format %d", fmt);
-  mgs::GroupTable gt;
-  int64_t rows = 0;
-  if ((rc = build_groups(groups, &gt, &rows))) return rc;
-  if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
-  const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
-  if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
-  if ((rc = check_extent(gt, width_in, "width_in"))) return rc;
-  if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
-  if (!dy_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "dy_bf16 is NULL");
-  const bool want_dxq = qbuf_requested(dx_row) || qbuf_requested(dx_col);
-  if (!dx_bf16 && !want_dxq && !dprobs && !dx_col_sum && !qbuf_requested(act_col))
-    return fail(MGS_ERR_INVALID_ARG, "no output requested");
-  if ((rc = check_qbuf(dx_row, fmt, "dx_row", false))) return rc;
-  if ((rc = check_qbuf(dx_col, fmt, "dx_col", true))) return rc;
-  if ((rc = check_qbuf(act_col, fmt, "act_col", true))) return rc;
-  if (fmt == MGS_FMT_NVFP4 && want_dxq && !dx_group_amax)
-    return fail(MGS_ERR_INVALID_ARG, "dx_group_amax is required to quantize dx to NVFP4");
-  const bool act_rht = qbuf_rht(act_col) != 0;
-  if (fmt == MGS_FMT_NVFP4 && qbuf_requested(act_col) && !act_rht && !saved_group_amax)
-    return fail(MGS_ERR_UNSUPPORTED,
-                "NVFP4 recompute (act_col) needs saved_group_amax, the group amax of the forward");
-  if (dprobs || dx_col_sum || act_rht) {
-    const int64_t need = mgs::act_bwd_workspace_bytes(gt, wa, width_in);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-      return fail(MGS_ERR_INVALID_ARG, "%s needs a workspace of %lld bytes (got %lld%s)",
-                  dprobs ? "dprobs" : dx_col_sum ? "dx_col_sum" : "a transformed act_col", (long long)need,
-                  (long long)workspace_bytes, workspace ? "" : ", NULL");
-  }
-  mgs::QOut dxq = make_qout(dx_row, dx_col, width_in);
-  mgs::QOut aq = make_qout(nullptr, act_col, wa);
-  aq.amax = saved_group_amax;
-  return hip_status(mgs::launch_act_bwd(ah, fmt, gt, width_in, static_cast<const uint16_t*>(x_bf16),
-                                        static_cast<const uint16_t*>(dy_bf16), probs,
-                                        static_cast<uint16_t*>(dx_bf16), dxq, dx_group_amax, dprobs,
-                                        dx_col_sum, workspace, aq, static_cast<hipStream_t>(stream)));
+  return act_bwd_impl(act, fmt, groups, width_in, x_bf16, dy_bf16, probs, dx_bf16, dx_row, dx_col,
+                      dx_group_amax, dprobs, dx_col_sum, act_col, saved_group_amax, workspace,
+                      workspace_bytes, false, stream);
+}
+
+int mgs_grouped_scaled_act_bwd_noalloc(const mgs_act_params* act, int32_t fmt, const mgs_groups* groups,
+                                       int64_t width_in, const void* x_bf16, const void* dy_bf16,
+                                       const float* probs, void* dx_bf16, const mgs_qbuf* dx_row,
+                                       const mgs_qbuf* dx_col, float* dx_group_amax, float* dprobs,
+                                       float* dx_col_sum, const mgs_qbuf* act_col,
+                                       const float* saved_group_amax, void* stream) {
+  return act_bwd_impl(act, fmt, groups, width_in, x_bf16, dy_bf16, probs, dx_bf16, dx_row, dx_col,
+                      dx_group_amax, dprobs, dx_col_sum, act_col, saved_group_amax, nullptr, 0, true,
+                      stream);
 }
 
 int64_t mgs_act_bwd_workspace_bytes(const mgs_act_params* act, const mgs_groups* groups,

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_symbols():
         assert hasattr(lib, name), name
     assert set(_native.EXPORTED) == set(_declared_symbols())
-    assert _native.abi_version() == 6
+    assert _native.abi_version() == 7
 
 
 def test_qtensor_nbytes_layouts():
@@ -98,6 +98,25 @@ def test_argument_validation_act_bwd_and_recompute():
     short = torch.empty(need - 1, dtype=torch.uint8)
     _expect(-1, b, act, "mxfp8", [32], 256, FAKE, FAKE, FAKE, dx_col_sum=FAKE, workspace=short, stream=0,
             match="dx_col_sum needs a workspace")
+
+
+def test_noalloc_backward_validates_like_the_workspace_one_and_rejects_oversize():
+    """The allocation-free backward runs the same host validation, and rejects a request whose
+    workspace would exceed its static scratch before touching any device (no GPU needed here)."""
+    from moe_grouped_scaled_amd import _native as N
+    act = N.act_params("srelu")
+    b = N.grouped_scaled_act_bwd_noalloc
+    _expect(-1, b, act, "mxfp8", [32], 64, FAKE, None, FAKE, dx=FAKE, stream=0, match="dy_bf16")
+    _expect(-1, b, act, "mxfp8", [32], 64, FAKE, FAKE, FAKE, stream=0, match="no output")
+    _expect(-3, b, act, "nvfp4", [32], 64, FAKE, FAKE, FAKE, act_col=_FakeQ().q, stream=0,
+            match="saved_group_amax")
+    big = [4096] * 16                       # 65536 rows x 4096: 8 MiB dprobs + 8 MiB column partials
+    need = N.act_bwd_workspace_bytes(act, big, 4096)
+    assert need > N.NOALLOC_SCRATCH_BYTES
+    _expect(-2, b, act, "mxfp8", big, 4096, FAKE, FAKE, FAKE, dprobs=FAKE, stream=0, match="static scratch")
+    _expect(-2, b, act, "mxfp8", big, 4096, FAKE, FAKE, FAKE, dx_col_sum=FAKE, stream=0, match="static scratch")
+    # the bench workload's request fits
+    assert N.act_bwd_workspace_bytes(act, [2048] * 16, 4096) <= N.NOALLOC_SCRATCH_BYTES
 
 
 def test_argument_validation_quantize_col_sum():
