@@ -116,7 +116,9 @@ def mlp_step(kind, fmt, splits, x1, w1, b1, w2, b2, p, dy2, act_params=None, act
     return {
         "y1": y1, "a32": a32, "y2": y2, "da": da, "dy1": dy1_32, "dp": dp, "dx1": dx1,
         "dw1": dw1, "dw2": dw2, "db1": db1, "db2": db2,
-        "q_a": qa["raw"], "q_dy1": qdy1["raw"],
+        # the quantized operands of the six GEMMs (layouts of oracle.quant.quantize_grouped)
+        "q_x1": qx1["raw"], "q_w1": qw1["raw"], "q_a": qa["raw"], "q_w2": qw2["raw"],
+        "q_dy2": qdy2["raw"], "q_dy1": qdy1["raw"],
     }
 
 

@@ -310,6 +310,20 @@ BWD_CASES = [
 @pytest.mark.parametrize("kind,fmt,splits,width_in,std", BWD_CASES)
 def test_act_bwd_parity(N, kind, fmt, splits, width_in, std):
     d = workloads.act_case(kind, splits, width_in, seed=21, std=std)
+    check_bwd_against_oracle(N, kind, fmt, splits, width_in, d)
+
+
+def test_act_bwd_swiglu_zipf_full_size(N):
+    """The Zipf-split SwiGLU workload's backward at full size (8 experts, 8192 tokens, one expert
+    empty, FC1 out 2 x 2048, top-2 routing probabilities): dense, rowwise and columnwise dL/dx, dprobs,
+    the per-expert column sums and the recomputed FC2 input, all against the oracle on every row."""
+    d = workloads.make("swiglu_zipf")
+    assert int(d["splits"].sum()) == 8192 and 0 in d["splits"]
+    check_bwd_against_oracle(N, "swiglu", "mxfp8", list(map(int, d["splits"])), 4096, d)
+
+
+def check_bwd_against_oracle(N, kind, fmt, splits, width_in, d):
+    """Every output of the fused backward on d["x"], d["dy"], d["p"] against the oracle."""
     params = _params(kind)
     x = bf16_f64(d["x"])
     p = d["p"].astype(np.float64)

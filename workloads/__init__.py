@@ -102,7 +102,9 @@ def make(name, seed=0, tokens=None, act="srelu"):
                     hidden=7168, limit=7.0,
                     x=normal_bf16(rng, (m, 4096)), p=uniform_f32(rng, m),
                     w2=normal_bf16(rng, (32, 7168, 2048), 0.02),
-                    dy2=normal_bf16(rng, (m, 7168)))
+                    dy2=normal_bf16(rng, (m, 7168)),
+                    # upstream gradient of the activation output (isolated-kernel tests), drawn last
+                    dy=normal_bf16(rng, (m, 2048)))
     if name == "mlp_step":
         n = tokens or 32768
         e = 16
