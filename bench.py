@@ -159,9 +159,156 @@ def cpu_baseline(kind, fmt, seed=0):
                       "ffn 4096, same recipe; %.1f s wall" % (tok, dt)}
 
 
+def gemm_roofline_time(mode, splits, m_or_n, n, k, fmt, c_bytes):
+    """T* = sum over groups of max(FLOP_g / P, bytes_g / 8 TB/s) for one grouped GEMM launch:
+    operands read once (codes + scales) and the output written once.  FPROP / DGRAD (grouped over
+    M): group g is an [m_g x k] . [n x k]^T product; WGRAD (grouped over K): [m x m_g] . [n x m_g]^T
+    with an [m x n] output per group, written even for an empty group."""
+    per_el = (1 + 1 / 32) if fmt == "mxfp8" else (0.5 + 1 / 16)
+    peak = MFMA_PEAK_TFLOPS[fmt] * 1e12
+    t = 0.0
+    for mg in splits:
+        if mode == "wgrad":
+            flop = 2.0 * m_or_n * n * mg
+            byts = (m_or_n + n) * mg * per_el + m_or_n * n * c_bytes
+        else:
+            flop = 2.0 * mg * n * k
+            byts = (mg + n) * k * per_el + mg * n * c_bytes if mg else 0.0
+        t += max(flop / peak, byts / (HBM_PEAK_GBPS * 1e9))
+    return t
+
+
+def bench_zipf(args):
+    """The two Zipf-split workloads, each as its own JSON line:
+      swiglu_zipf  scaled SwiGLU forward + backward, MXFP8 rowwise and columnwise: 8 experts, 8192
+                   tokens in a Zipf(1.2) split with one empty expert, FC1 output 2 x 2048;
+      clamped_fc2  clamped SwiGLU (limit 7) forward + backward with FC2's grouped MXFP8 GEMMs (fprop,
+                   dgrad, wgrad): 32 experts, 65536 tokens in a Zipf(1.2) split with four empty
+                   experts, ffn 2048 (x2 gated), hidden 7168; the FC2 weight and the upstream gradient
+                   are quantized row + col in the step, recompute on (the backward regenerates FC2's
+                   columnwise input).
+    A step runs every launch of the workload once; the line reports each kernel's GB/s or TFLOP/s
+    and, per GEMM mode, T*/t with T* the per-group roofline time."""
+    import torch
+    import workloads
+    from moe_grouped_scaled_amd import _native as N
+
+    d = workloads.make(args.workload)
+    splits = list(map(int, d["splits"]))
+    e, m = len(splits), int(sum(splits))
+    w_in, w_a = 4096, 2048
+    kind = "swiglu" if args.workload == "swiglu_zipf" else "clamped_swiglu"
+    act = N.act_params(kind, limit=7.0)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x, p = dev(d["x"]), torch.from_numpy(d["p"]).cuda()
+    dy = dev(d["dy"])
+    fc2 = args.workload == "clamped_fc2"
+    if fc2:
+        hid = d["hidden"]
+        w2, dy2 = dev(d["w2"].reshape(e * hid, w_a)), dev(d["dy2"])
+    del d
+    ws = torch.empty(N.act_bwd_workspace_bytes(act, splits, w_in), dtype=torch.uint8, device="cuda")
+
+    def step():
+        if not fc2:
+            # forward with both copies (no GEMM consumes them here), backward with every output
+            ar, ac = N.QTensor("mxfp8", False, splits, w_a), N.QTensor("mxfp8", True, splits, w_a)
+            N.grouped_scaled_act_fwd(act, "mxfp8", splits, w_in, x, p, ar, ac)
+            dxr, dxc = N.QTensor("mxfp8", False, splits, w_in), N.QTensor("mxfp8", True, splits, w_in)
+            dx = torch.empty((m, w_in), dtype=torch.bfloat16, device="cuda")
+            dp = torch.empty(m, dtype=torch.float32, device="cuda")
+            N.grouped_scaled_act_bwd(act, "mxfp8", splits, w_in, x, dy, p, dx=dx, dx_row=dxr, dx_col=dxc,
+                                     dprobs=dp, workspace=ws)
+            return
+        w2r, w2c = N.QTensor("mxfp8", False, [hid] * e, w_a), N.QTensor("mxfp8", True, [hid] * e, w_a)
+        N.grouped_mx_quantize("mxfp8", [hid] * e, w_a, w2, w2r, w2c)
+        ar = N.QTensor("mxfp8", False, splits, w_a)
+        N.grouped_scaled_act_fwd(act, "mxfp8", splits, w_in, x, p, ar, None)
+        y2 = torch.empty((m, hid), dtype=torch.bfloat16, device="cuda")
+        N.grouped_gemm_mx("fprop", "mxfp8", splits, m, hid, w_a, ar, w2r, y2)
+        del ar, y2
+        g2r, g2c = N.QTensor("mxfp8", False, splits, hid), N.QTensor("mxfp8", True, splits, hid)
+        N.grouped_mx_quantize("mxfp8", splits, hid, dy2, g2r, g2c)
+        da = torch.empty((m, w_a), dtype=torch.bfloat16, device="cuda")
+        N.grouped_gemm_mx("dgrad", "mxfp8", splits, m, w_a, hid, g2r, w2c, da)
+        dxr, dxc = N.QTensor("mxfp8", False, splits, w_in), N.QTensor("mxfp8", True, splits, w_in)
+        ac = N.QTensor("mxfp8", True, splits, w_a)
+        dp = torch.empty(m, dtype=torch.float32, device="cuda")
+        N.grouped_scaled_act_bwd(act, "mxfp8", splits, w_in, x, da, p, dx_row=dxr, dx_col=dxc, dprobs=dp,
+                                 act_col=ac, workspace=ws)
+        dw2 = torch.empty((e, hid, w_a), dtype=torch.float32, device="cuda")
+        N.grouped_gemm_mx("wgrad", "mxfp8", splits, hid, w_a, m, g2c, ac, dw2)
+
+    for _ in range(args.warmup):
+        step()
+    timer = Timer(N)
+    torch.cuda.synchronize()
+    timer.enabled = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.enabled = False
+    dur = {k: float(np.mean(v)) for k, v in timer.durations().items()}
+    if not fc2:
+        fwd_b = act_fwd_bytes(m, w_in, w_a, "mxfp8", row=True, col=True)
+        bwd_b = act_bwd_bytes(m, w_in, w_a, "mxfp8", dense=True, row=True, col=True, dprobs=True,
+                              recompute=False)
+    else:
+        fwd_b = act_fwd_bytes(m, w_in, w_a, "mxfp8", row=True, col=False)
+        bwd_b = act_bwd_bytes(m, w_in, w_a, "mxfp8", dense=False, row=True, col=True, dprobs=True,
+                              recompute=True)
+    t_fwd, t_bwd = dur["grouped_scaled_act_fwd"], dur["grouped_scaled_act_bwd"]
+    kernels = {
+        "act_fwd": {"GB/s": fwd_b / t_fwd / 1e9, "frac_hbm": fwd_b / t_fwd / 1e9 / HBM_PEAK_GBPS,
+                    "us": t_fwd * 1e6, "bytes": fwd_b},
+        "act_bwd": {"GB/s": bwd_b / t_bwd / 1e9, "frac_hbm": bwd_b / t_bwd / 1e9 / HBM_PEAK_GBPS,
+                    "us": t_bwd * 1e6, "bytes": bwd_b},
+    }
+    ms = wall / args.steps * 1e3
+    if not fc2:
+        tot_b = fwd_b + bwd_b
+        value, unit = tot_b / (t_fwd + t_bwd) / 1e9, "GB/s"
+        roof = {"bound": "hbm", "achieved": bwd_b / t_bwd / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": bwd_b / t_bwd / 1e9 / HBM_PEAK_GBPS, "traffic": None}
+        wl = ("scaled SwiGLU fwd + bwd, MXFP8 row + col: 8 experts, 8192 tokens Zipf(1.2) split "
+              "(one empty), FC1 out 2 x 2048")
+    else:
+        flops = 2.0 * m * hid * w_a
+        gemm = {}
+        for mode, (mm, nn, kk, cb) in {"fprop": (m, hid, w_a, 2), "dgrad": (m, w_a, hid, 2),
+                                       "wgrad": (hid, w_a, m, 4)}.items():
+            t = dur["gemm_" + mode]
+            tstar = gemm_roofline_time(mode, splits, mm, nn, kk, "mxfp8", cb)
+            gemm[mode] = {"us": t * 1e6, "TFLOP/s": flops / t / 1e12,
+                          "frac_mfma": flops / t / 1e12 / MFMA_PEAK_TFLOPS["mxfp8"],
+                          "t_star_us": tstar * 1e6, "t_star_over_t": tstar / t}
+        kernels["gemm"] = gemm
+        kernels["mx_quantize_us"] = dur["grouped_mx_quantize"] * 1e6   # W2 and dY2, row + col, averaged
+        t_g = float(np.mean([dur["gemm_" + k] for k in ("fprop", "dgrad", "wgrad")]))
+        value, unit = 3 * flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": flops / t_g / 1e12, "peak": MFMA_PEAK_TFLOPS["mxfp8"],
+                "unit": "TFLOP/s", "frac": flops / t_g / 1e12 / MFMA_PEAK_TFLOPS["mxfp8"], "traffic": None}
+        wl = ("clamped SwiGLU (limit 7) fwd + bwd + FC2 grouped MXFP8 fprop/dgrad/wgrad: 32 experts, 65536 "
+              "tokens Zipf(1.2) split (four empty), ffn 2048 (x2 gated), hidden 7168, recompute on")
+    line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+            "config": {"workload": wl, "experts": e, "tokens": m, "splits": splits},
+            "roofline": roof, "kernels": kernels}
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default="mlp_step", choices=["mlp_step", "swiglu_zipf", "clamped_fc2"],
+                    help="mlp_step (default): the full expert-MLP training step; swiglu_zipf / clamped_fc2: the "
+                         "Zipf-split SwiGLU and clamped-SwiGLU + FC2 workloads, one line each")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--fmt", default="mxfp8", choices=["mxfp8", "nvfp4"])
@@ -191,6 +338,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.workload != "mlp_step":
+        bench_zipf(args)
+        return
     d = workloads.make("mlp_step", seed=0, act=args.act)
     splits = list(map(int, d["splits"]))
     e, h, f = 16, d["hidden"], d["ffn"]

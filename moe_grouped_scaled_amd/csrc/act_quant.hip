@@ -203,19 +203,13 @@ __device__ __forceinline__ ColDst col_dst(const QOut& q, int64_t w, int64_t tota
 template <int FMT>
 __device__ __forceinline__ void quant_row(const float (&v)[8], const RowDst& d, int i, bool rv,
                                           float s_enc) {
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  float m = absmax8(v);
   if constexpr (FMT == MGS_FMT_MXFP8) {
     m = row4_max(m);
-    const uint32_t c = mx_scale_code(m);
-    const float inv = mx_inv_scale(c);
-    uint2 q;
-    q.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    q.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    const Mx8 e = mx_encode8(v, m);
     const bool sv = rv && d.sc_lane;
-    bst8(q, d.data, rv ? d.dvo : MASKED, i * d.dpitch);
-    bst1(c, d.scales, sv ? d.svo : MASKED, i * d.spitch);
+    bst8(e.q, d.data, rv ? d.dvo : MASKED, i * d.dpitch);
+    bst1(e.code, d.scales, sv ? d.svo : MASKED, i * d.spitch);
 #pragma unroll
     for (uint32_t t = 1; t <= 3; ++t) bst1(0, d.scales, sv && t <= d.pad ? d.svo + t : MASKED, i * d.spitch);
   } else {
@@ -234,18 +228,12 @@ __device__ __forceinline__ void quant_row(const float (&v)[8], const RowDst& d, 
 template <int FMT>
 __device__ __forceinline__ void quant_col(const float (&v)[8], const ColDst& d, int j, bool valid,
                                           float s_enc) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  float m = absmax8(v);
   if constexpr (FMT == MGS_FMT_MXFP8) {
     m = quad_max(m);
-    const uint32_t c = mx_scale_code(m);
-    const float inv = mx_inv_scale(c);
-    uint2 q;
-    q.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    q.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-    bst8(q, d.data, valid ? d.dvo : MASKED, j * d.dpitch);
-    bst1(c, d.scales, valid && d.sc_lane ? d.svo : MASKED, j * d.spitch);
+    const Mx8 e = mx_encode8(v, m);
+    bst8(e.q, d.data, valid ? d.dvo : MASKED, j * d.dpitch);
+    bst1(e.code, d.scales, valid && d.sc_lane ? d.svo : MASKED, j * d.spitch);
   } else {
     m = pair1_max(m);
     const NvBlock b = nv_block(m, s_enc);
@@ -491,18 +479,12 @@ __device__ __forceinline__ void stage_col(const float (&v)[8], uint8_t* st, cons
                                           float s_enc) {
   constexpr int P = Stage<FMT>::PITCH;
   const int c = 8 * bp.cc + j;
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  float m = absmax8(v);
   if constexpr (FMT == MGS_FMT_MXFP8) {
     m = quad_max(m);
-    const uint32_t code = mx_scale_code(m);
-    const float inv = mx_inv_scale(code);
-    uint2 q;
-    q.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    q.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-    *reinterpret_cast<uint2*>(st + c * P + 32 * bp.wave + bp.lr0) = q;
-    if (bp.lr0 == 0) st[BLOCK_COLS * P + 4 * c + bp.wave] = (uint8_t)code;
+    const Mx8 e = mx_encode8(v, m);
+    *reinterpret_cast<uint2*>(st + c * P + 32 * bp.wave + bp.lr0) = e.q;
+    if (bp.lr0 == 0) st[BLOCK_COLS * P + 4 * c + bp.wave] = (uint8_t)e.code;
   } else {
     m = pair1_max(m);
     const NvBlock b = nv_block(m, s_enc);
@@ -683,6 +665,12 @@ __device__ __forceinline__ float dx_gate(const ActArgs& aa, float g, float u, fl
     float dg, du;
     dact_gated<KIND>(g, u, aa, a, dg, du);
     return (dg * dd) * p;
+  } else if constexpr (KIND == MGS_ACT_SRELU) {
+    // (2 r dy) p computed as (r dy)(2 p): r dy is exact (two BF16 values) and so is 2 p, so both
+    // round once, to the same value
+    const float r = relu(g);
+    a = r * r;
+    return (r * dd) * (p + p);
   } else {
     a = act_unary<KIND>(g, aa);
     return (dact_unary<KIND>(g, aa) * dd) * p;
@@ -771,7 +759,7 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
       float a;
       const float dd = bf16_at(dyt[i], j);
       d[i][j] = dx_gate<KIND>(aa, bf16_at(xg[i], j), GATED ? bf16_at(xu[GATED ? i : 0], j) : 0.0f, dd, p[i], a);
-      dpacc[i] += dd * a;
+      dpacc[i] = __builtin_fmaf(dd, a, dpacc[i]);
     }
     pin(dpacc[i]);
     if (dx) bst16(pack8_bf16(d[i]), dxv.r, rv ? dxv.vo : MASKED, i * dxv.ld2);

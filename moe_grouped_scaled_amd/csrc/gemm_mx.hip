@@ -23,6 +23,7 @@
 // accumulators per lane in AGPRs), K steps of 128 and double-buffered direct-to-LDS loads.  The MFMA
 // is issued with B as its first operand so each lane's accumulator holds runs of 4 consecutive output
 // columns of one row (one 16-byte FP32 / 8-byte BF16 store each).
+#include <algorithm>
 #include <type_traits>
 
 #include "mgs_device.h"
@@ -192,12 +193,13 @@ __device__ __forceinline__ U2 swap32(uint32_t a, uint32_t b) {
   const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
   return U2{r[0], r[1]};
 }
-// max over the lanes l, l ^ 16, l ^ 32, l ^ 48
+// max over the lanes l, l ^ 16, l ^ 32, l ^ 48 of a non-negative value (its bits order like
+// unsigned integers)
 __device__ __forceinline__ float max_over_rows(float m) {
   U2 r = swap16(__float_as_uint(m), __float_as_uint(m));
-  m = fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
-  r = swap32(__float_as_uint(m), __float_as_uint(m));
-  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+  const uint32_t u = umax(r.x, r.y);
+  r = swap32(u, u);
+  return __uint_as_float(umax(r.x, r.y));
 }
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -235,14 +237,15 @@ __device__ __forceinline__ void store_values(const TileJob& j, int row, int col,
 
 template <int TM, int TN>
 __device__ __forceinline__ void write_zero_tile(const TileJob& j, const GemmArgs& ga) {
-  // empty group in WGRAD: dW_g = 0 (unchanged when accumulating)
+  // empty group in WGRAD: dW_g = 0 (unchanged when accumulating); four columns per store (the
+  // tile's valid column count, like N, is a multiple of 32)
   if (ga.accumulate) return;
-  for (int idx = threadIdx.x; idx < TM * TN; idx += blockDim.x) {
-    const int r = idx / TN, c = idx - (idx / TN) * TN;
+  for (int idx = threadIdx.x; idx < TM * (TN / 4); idx += blockDim.x) {
+    const int r = idx / (TN / 4), c = 4 * (idx - r * (TN / 4));
     if (r >= j.a.rows || c >= j.b.rows) continue;
     const int64_t gr = j.crow0 + r, gc = j.ccol0 + c;
-    if (j.c32) j.c32[gr * j.ldc + gc] = 0.0f;
-    else j.c16[gr * j.ldc + gc] = 0;
+    if (j.c32) st16(j.c32 + gr * j.ldc + gc, 0u, 0u, 0u, 0u);
+    else *reinterpret_cast<uint2*>(j.c16 + gr * j.ldc + gc) = make_uint2(0u, 0u);
   }
 }
 
@@ -301,6 +304,22 @@ __device__ __forceinline__ int xcd_remap_gemm(int b, int n) {
   int q = n >> 3, r = n & 7;
   int x = b & 7, i = b >> 3;
   return x * q + min(x, r) + i;
+}
+
+// The tile workgroup b takes under the table's schedule (see GemmTable); false: none.
+__device__ __forceinline__ bool schedule_tile(const GemmTable& tt, int b, int nb, int* tile) {
+  if (!tt.interleave) {
+    *tile = xcd_remap_gemm(b, nb);
+    return true;
+  }
+  const int s = b / tt.stride;
+  const int g = tt.order[s];
+  const int j = b - s * tt.stride;
+  const int t = tt.tile_off[g + 1] - tt.tile_off[g];
+  const int q = t >> 3, r = t & 7, x = j & 7, i = j >> 3;
+  if (i >= q + (x < r ? 1 : 0)) return false;
+  *tile = tt.tile_off[g] + x * q + min(x, r) + i;
+  return true;
 }
 
 // Scaled FP8 MFMA with the accumulator pinned to AGPRs.  Written as inline assembly because the
@@ -376,16 +395,9 @@ __device__ __forceinline__ void epilogue_act(const TileJob& j, const GemmArgs& g
       // C: 16 contiguous bytes of the block's 64 per lane
       const U2 cx = swap16(w[1].x, w[0].x), cy = swap16(w[1].y, w[0].y);
       if (rok && bok) st16(reinterpret_cast<uint8_t*>(crow) + 64 * b + c16_off, cx.x, cy.x, cx.y, cy.y);
-      float m = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(y[t]));
-      m = max_over_rows(m);
-      const uint32_t c = mx_scale_code(m);
-      const float inv = mx_inv_scale(c);
-      const uint32_t q0 = e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
-      const uint32_t q1 = e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
-      pr[b] = swap16(q1, q0);
-      sdw |= (bok ? c : 0u) << (8 * b);
+      const Mx8 enc = mx_encode8(y, max_over_rows(absmax8(y)));
+      pr[b] = swap16(enc.q.y, enc.q.x);
+      sdw |= (bok ? enc.code : 0u) << (8 * b);
     }
     // codes: blocks (0, 1) and (2, 3); lane q writes 16 bytes of block b + q / 2
 #pragma unroll
@@ -553,7 +565,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint2 bias_lds[BN2 / 4];
-  const int tile = xcd_remap_gemm(blockIdx.x, gridDim.x);
+  int tile;
+  if (!schedule_tile(tt, blockIdx.x, gridDim.x, &tile)) return;
   const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
   if (j.k == 0) {
     write_zero_tile<BM2, BN2>(j, ga);
@@ -802,7 +815,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_STAGE];
   __shared__ __attribute__((aligned(16))) uint2 bias_lds[BN2 / 4];
-  const int tile = xcd_remap_gemm(blockIdx.x, gridDim.x);
+  int tile;
+  if (!schedule_tile(tt, blockIdx.x, gridDim.x, &tile)) return;
   const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
   if (j.k == 0) {
     write_zero_tile<BM2, BN2>(j, ga);
@@ -983,10 +997,49 @@ void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
 
 namespace {
 
+// Schedule of a K-grouped (WGRAD) launch.  Every group has the same tiles but its own K, so a
+// contiguous range of the tile sequence per XCD can leave one XCD with several times the mean work
+// (a Zipf-skewed split puts a third of the tokens in one expert).  Cost of a tile in K steps, plus
+// about four steps for the epilogue (one for an empty group's zero tile); when the heaviest XCD's
+// contiguous range costs more than 5 % above the mean, the groups are dealt over all XCDs instead,
+// largest K first, so each XCD holds an eighth of every group (greedy largest-first list scheduling
+// over the XCDs' CUs, within about one tile of the ideal on such splits) while the tiles it has in
+// flight still form a compact block of one group.
+void schedule_k_grouped(GemmTable& tt) {
+  const int e = tt.num_groups;
+  int64_t cost[MGS_MAX_GROUPS];
+  for (int g = 0; g < e; ++g) {
+    const int64_t steps = (tt.tok_off[g + 1] - tt.tok_off[g] + BK - 1) / BK;
+    cost[g] = steps ? steps + 4 : 1;
+  }
+  // the contiguous schedule: XCD x takes tiles [x q + min(x, r), (x + 1) q + min(x + 1, r))
+  const int64_t n = tt.total_tiles, q = n / 8, r = n % 8;
+  int64_t total = 0, worst = 0;
+  for (int g = 0; g < e; ++g) total += cost[g] * (tt.tile_off[g + 1] - tt.tile_off[g]);
+  for (int x = 0; x < 8; ++x) {
+    const int64_t a = x * q + std::min<int64_t>(x, r), b = (x + 1) * q + std::min<int64_t>(x + 1, r);
+    int64_t c = 0;
+    for (int g = 0; g < e; ++g) {
+      const int64_t lo = std::max<int64_t>(a, tt.tile_off[g]), hi = std::min<int64_t>(b, tt.tile_off[g + 1]);
+      if (hi > lo) c += cost[g] * (hi - lo);
+    }
+    worst = std::max(worst, c);
+  }
+  if (e < 2 || 8 * worst * 100 <= total * 105) return;
+  int order[MGS_MAX_GROUPS];
+  for (int g = 0; g < e; ++g) order[g] = g;
+  std::stable_sort(order, order + e, [&](int a, int b) { return cost[a] > cost[b]; });
+  for (int s = 0; s < e; ++s) tt.order[s] = (uint8_t)order[s];
+  // every group of a K-grouped launch has the same tile count
+  tt.stride = (tt.tile_off[1] - tt.tile_off[0] + 7) / 8 * 8;
+  tt.interleave = 1;
+  tt.grid = tt.stride * e;
+}
+
 // Tile table for one launch: tiles of group g are [tile_off[g], tile_off[g+1]), ordered row-tile
 // major (column tiles fastest) so neighbouring tiles share their A rows.
 GemmTable make_table(const GemmArgs& ga, const GroupTable& gt, int tm, int tn) {
-  GemmTable tt;
+  GemmTable tt{};
   tt.num_groups = gt.num_groups;
   const int64_t ntn = (ga.n + tn - 1) / tn;
   int64_t tiles = 0;
@@ -1005,6 +1058,9 @@ GemmTable make_table(const GemmArgs& ga, const GroupTable& gt, int tm, int tn) {
                                                          : gt.row_off[gt.num_groups];
   tt.tile_off[gt.num_groups] = (int32_t)tiles;
   tt.total_tiles = (int32_t)tiles;
+  tt.interleave = 0;
+  tt.grid = (int32_t)tiles;
+  if (ga.mode == MGS_GEMM_WGRAD) schedule_k_grouped(tt);
   return tt;
 }
 
@@ -1018,11 +1074,11 @@ hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t st)
   if (ga.fmt == MGS_FMT_MXFP8) {
     const GemmTable tt = make_table(ga, gt, BM2, BN2);
     if (tt.total_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_mxfp8_256_kernel, dim3((unsigned)tt.total_tiles), dim3(256), 0, st, ga, tt);
+    hipLaunchKernelGGL(gemm_mxfp8_256_kernel, dim3((unsigned)tt.grid), dim3(256), 0, st, ga, tt);
   } else {
     const GemmTable tt = make_table(ga, gt, BM2, BN2);
     if (tt.total_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_nvfp4_256_kernel, dim3((unsigned)tt.total_tiles), dim3(256), 0, st, ga, tt);
+    hipLaunchKernelGGL(gemm_nvfp4_256_kernel, dim3((unsigned)tt.grid), dim3(256), 0, st, ga, tt);
   }
   return hipGetLastError();
 }

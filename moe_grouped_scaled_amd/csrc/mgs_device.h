@@ -55,20 +55,45 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// max over the 4 lanes of a quad
+// The lane maxima below are taken over block maxima of magnitudes (non-negative FP32 values), whose
+// bit patterns order like unsigned integers: an integer maximum needs none of the NaN-quieting copies
+// the compiler puts before a float maximum of a value it cannot prove canonical (a DPP result).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// max over the 4 lanes of a quad (v >= 0)
 __device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
-  return fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  uint32_t u = __float_as_uint(v);
+  u = umax(u, dpp_u<DPP_QUAD_XOR1>(u));
+  return __uint_as_float(umax(u, dpp_u<DPP_QUAD_XOR2>(u)));
 }
-// max over the 2 lanes (l, l^1)
-__device__ __forceinline__ float pair1_max(float v) { return fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v)); }
-// max over the 4 lanes {l mod 4 + 4k} of each 16-lane row
+// max over the 2 lanes (l, l^1) (v >= 0)
+__device__ __forceinline__ float pair1_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return __uint_as_float(umax(u, dpp_u<DPP_QUAD_XOR1>(u)));
+}
+// max over the 4 lanes {l mod 4 + 4k} of each 16-lane row (v >= 0)
 __device__ __forceinline__ float row4_max(float v) {
-  v = fmaxf(v, dpp_f<DPP_ROW_ROR4>(v));
-  return fmaxf(v, dpp_f<DPP_ROW_ROR8>(v));
+  uint32_t u = __float_as_uint(v);
+  u = umax(u, dpp_u<DPP_ROW_ROR4>(u));
+  return __uint_as_float(umax(u, dpp_u<DPP_ROW_ROR8>(u)));
 }
-// max over the 2 lanes (l, l^4)
-__device__ __forceinline__ float pair4_max(float v) { return fmaxf(v, __shfl_xor(v, 4)); }
+// max over the 2 lanes (l, l^4) (v >= 0)
+__device__ __forceinline__ float pair4_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return __uint_as_float(umax(u, (uint32_t)__shfl_xor((int)u, 4)));
+}
+
+// relu(x) = max(x, +0) on the bit pattern: negative values (sign bit set, negative as integers),
+// -0 included, give +0.  No NaN-quieting copy is needed, unlike a float maximum of an unpacked BF16
+// value.
+__device__ __forceinline__ float relu(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
 
 // ------------------------------------------------------------------------------------------ MXFP8
 
@@ -80,19 +105,50 @@ __device__ __forceinline__ uint32_t mx_scale_code(float amax) {
   return (uint32_t)(e > 8 ? e - 8 : 0);
 }
 
-// 2^(127 - code): the exact reciprocal of the block scale, for code in [0, 246]
-__device__ __forceinline__ float mx_inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+// The block scale 2^(code - 127) as an FP32 number (the subnormal 2^-127 for code 0), code in [0, 246]
+__device__ __forceinline__ float mx_scale_value(uint32_t code) {
+  return __builtin_amdgcn_ldexpf(1.0f, (int)code - 127);
+}
 
-// four FP32 values -> four E4M3 codes (byte i = value i), RNE, saturating at +-448.  The hardware
-// convert rounds to nearest-even but does not saturate, so values are clamped first.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
+// max |v_i| of eight values, as three-input maxima
+__device__ __forceinline__ float absmax8(const float (&v)[8]) {
+  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  m = fmaxf(fmaxf(m, fabsf(v[3])), fabsf(v[4]));
+  m = fmaxf(fmaxf(m, fabsf(v[5])), fabsf(v[6]));
+  return fmaxf(m, fabsf(v[7]));
+}
+
+// four FP32 values -> four E4M3 codes of value / s (byte i = value i), s = 2^(code - 127) the block
+// scale, RNE, saturating at +-448.  The gfx950 scaled convert divides by the power of two s exactly and
+// rounds to nearest-even, but does not saturate (beyond 448 it gives the NaN code), so the values are
+// clamped to +-448 s first (`bound` = 448 s, exact).  Checked on the device for every scale code 0..246
+// over 2^20 values each: bit for bit the codes of clamping value * 2^(127 - code) at +-448 and
+// converting with the unscaled convert.
+typedef short mgs_v2s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3x4_scaled(float a, float b, float c, float d, float s, float bound) {
+  a = __builtin_amdgcn_fmed3f(a, -bound, bound);
+  b = __builtin_amdgcn_fmed3f(b, -bound, bound);
+  c = __builtin_amdgcn_fmed3f(c, -bound, bound);
+  d = __builtin_amdgcn_fmed3f(d, -bound, bound);
+  mgs_v2s w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, s, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, s, true);
+  return __builtin_bit_cast(uint32_t, w);
+}
+
+// MXFP8 encode of the eight values a lane holds of one 32-element block whose maximum magnitude is
+// `amax`: the E8M0 scale code, and the eight E4M3 codes (value 2k in byte k % 4 of dword k / 4)
+struct Mx8 {
+  uint32_t code;
+  uint2 q;
+};
+__device__ __forceinline__ Mx8 mx_encode8(const float (&v)[8], float amax) {
+  Mx8 r;
+  r.code = mx_scale_code(amax);
+  const float s = mx_scale_value(r.code), bound = 448.0f * s;
+  r.q.x = e4m3x4_scaled(v[0], v[1], v[2], v[3], s, bound);
+  r.q.y = e4m3x4_scaled(v[4], v[5], v[6], v[7], s, bound);
+  return r;
 }
 
 // E4M3 code of one non-negative value (RNE, saturating)
@@ -176,14 +232,14 @@ __device__ __forceinline__ float act_unary(float x, const ActArgs& aa) {
   if constexpr (KIND == MGS_ACT_IDENTITY) {
     return x;
   } else if constexpr (KIND == MGS_ACT_SRELU) {
-    float r = fmaxf(x, 0.0f);
+    const float r = relu(x);
     return r * r;
   } else if constexpr (KIND == MGS_ACT_GELU) {
     return 0.5f * x * (1.0f + erff(x * INV_SQRT2));
   } else if constexpr (KIND == MGS_ACT_SIGMOID) {
     return sigmoidf_(x);
   } else {
-    float r = fmaxf(x, 0.0f);
+    const float r = relu(x);
     float t = aa.s * tanh_nonneg(r * aa.inv_s);
     return t * t;
   }
@@ -195,7 +251,7 @@ __device__ __forceinline__ float dact_unary(float x, const ActArgs& aa) {
   if constexpr (KIND == MGS_ACT_IDENTITY) {
     return 1.0f;
   } else if constexpr (KIND == MGS_ACT_SRELU) {
-    float r = fmaxf(x, 0.0f);
+    const float r = relu(x);
     return r + r;
   } else if constexpr (KIND == MGS_ACT_GELU) {
     // Phi(x) + x phi(x)
@@ -204,7 +260,7 @@ __device__ __forceinline__ float dact_unary(float x, const ActArgs& aa) {
     float sg = sigmoidf_(x);
     return sg * (1.0f - sg);
   } else {
-    float r = fmaxf(x, 0.0f);
+    const float r = relu(x);
     float t = tanh_nonneg(r * aa.inv_s);
     float d = (aa.s + aa.s) * t * (1.0f - t * t);
     return x > 0.0f ? d : 0.0f;

@@ -56,6 +56,17 @@ struct GemmTable {
   int32_t total_tiles;
   int32_t tile_off[MGS_MAX_GROUPS + 1];  // cumulative tiles per group
   int32_t tok_off[MGS_MAX_GROUPS + 1];   // M-grouped: row offsets; K-grouped: padded token offsets
+  // Workgroup schedule (workgroups are dealt to the 8 XCDs round-robin by index).
+  //   interleave == 0: each XCD takes a contiguous range of the tile sequence (group by group).
+  //   interleave == 1 (K-grouped launches, where every group has the same tiles but its own K):
+  //     groups in the order `order` (largest K first); group order[s] owns workgroups
+  //     s * stride .. s * stride + stride - 1 (stride = the group's tile count rounded up to a
+  //     multiple of 8); its workgroup j goes to XCD j % 8 and takes the (j / 8)-th tile of that XCD's
+  //     contiguous eighth of the group's tiles; workgroups past the end of an eighth do nothing.
+  int32_t interleave;
+  int32_t grid;                          // workgroups of the launch
+  int32_t stride;
+  uint8_t order[MGS_MAX_GROUPS];
 };
 
 struct GemmArgs {
