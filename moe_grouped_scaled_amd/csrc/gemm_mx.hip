@@ -648,14 +648,20 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
       return v8i{(int)(x0.x & mlo), (int)(x0.y & mlo), (int)(x0.z & mlo), (int)(x0.w & mlo),
                  (int)(x1.x & mhi), (int)(x1.y & mhi), (int)(x1.z & mhi), (int)(x1.w & mhi)};
     };
-    uint4 alo = half(pa, 0, swz_lo), ahi = half(pa, 0, swz_hi);
+    // the step's first reads in the order the MFMAs of fragment row 0 use them, scales first (the
+    // scheduling fences keep that order): each of those MFMAs then waits only for its own B fragment
+    // instead of all eight
     int csn = psa[0];
-    v8i bfr[8];
     int csb[8];
 #pragma unroll
+    for (int f = 0; f < 8; ++f) csb[f] = psb[f * 64];
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 alo = half(pa, 0, swz_lo), ahi = half(pa, 0, swz_hi);
+    v8i bfr[8];
+#pragma unroll
     for (int f = 0; f < 8; ++f) {
+      __builtin_amdgcn_sched_barrier(0);
       bfr[f] = join(half(pb, f, swz_lo), half(pb, f, swz_hi));
-      csb[f] = psb[f * 64];
     }
 #pragma unroll
     for (int fm = 0; fm < 8; ++fm) {
