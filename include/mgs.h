@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MGS_ABI_VERSION 7
+#define MGS_ABI_VERSION 8
 #define MGS_MAX_GROUPS 256
 /* Size of the static per-device scratch of mgs_grouped_scaled_act_bwd_noalloc (16 MiB). */
 #define MGS_NOALLOC_SCRATCH_BYTES ((int64_t)16 << 20)
@@ -116,9 +116,26 @@ typedef struct {
   float beta;    /* CLAMPED_SWIGLU up-projection offset (default 0) */
 } mgs_act_params;
 
+/* Row groups.  Host split sizes: split_sizes points to them; max_rows and dev_table are ignored.
+ *
+ * Device-resident split sizes (split_sizes == NULL): the graph-safe form.  [P2] Greptile summary,
+ * third bullet (GroupedLinear's graph-safe forward, _fuser_forward_graph_safe): the split sizes stay in
+ * device memory, so a captured HIP graph can be replayed for a different routing without a host sync.
+ *   max_rows   row capacity (> 0): every layout is strided for it, so buffer sizes do not depend on the
+ *              split sizes -- rowwise tensors have max_rows rows (rows past the sum are neither read nor
+ *              written), columnwise tensors a padded token count of 128 * (ceil(max_rows / 128) +
+ *              num_groups), rowwise MXFP8 scales are K-step grouped over max_rows rows, and an
+ *              M-grouped GEMM's m (a WGRAD's k) is max_rows.  mgs_qtensor_nbytes and the workspace-size
+ *              calls return the capacity sizes.
+ *   dev_table  DEVICE buffer of mgs_groups_table_bytes() bytes holding the offsets, written on the
+ *              stream by mgs_groups_update (call it after every change of the split sizes; kernels of
+ *              the calls enqueued after it read them).  Calls sharing a dev_table must not overlap.
+ * MXFP8 only: NVFP4 tensors, the FP32-input forward and mgs_grouped_col_sum return MGS_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t num_groups;         /* 1 .. MGS_MAX_GROUPS */
-  const int64_t* split_sizes; /* host array [num_groups], each >= 0 */
+  const int64_t* split_sizes; /* host array [num_groups], each >= 0; NULL: device-resident (above) */
+  int64_t max_rows;
+  void* dev_table;
 } mgs_groups;
 
 /* One orientation (rowwise or columnwise) of a grouped quantized tensor; see the layouts above. */
@@ -135,6 +152,17 @@ typedef struct {
    * amax (see group_amax below); the GEMM reads such a copy like any other. */
   uint32_t rht;
 } mgs_qbuf;
+
+/* Bytes of the device table of device-resident split sizes (mgs_groups.dev_table). */
+int64_t mgs_groups_table_bytes(void);
+
+/* Device-resident split sizes: enqueues on `stream` the computation of groups->dev_table from
+ * split_sizes_dev (DEVICE int64 [num_groups]).  status_dev (DEVICE int32, nullable) receives 0, or 1
+ * when a split size is negative or their sum exceeds max_rows; the table then holds empty groups, so
+ * the calls that follow write no output rows (a WGRAD writes zero weight gradients).  The host cannot
+ * see this without a synchronization: read status_dev after the step. */
+int mgs_groups_update(const mgs_groups* groups, const int64_t* split_sizes_dev, int32_t* status_dev,
+                      void* stream);
 
 /* Library ABI version (MGS_ABI_VERSION). */
 int mgs_abi_version(void);

@@ -39,7 +39,8 @@ class ActParams(ctypes.Structure):
 
 
 class Groups(ctypes.Structure):
-    _fields_ = [("num_groups", ctypes.c_int32), ("split_sizes", ctypes.POINTER(ctypes.c_int64))]
+    _fields_ = [("num_groups", ctypes.c_int32), ("split_sizes", ctypes.POINTER(ctypes.c_int64)),
+                ("max_rows", ctypes.c_int64), ("dev_table", ctypes.c_void_p)]
 
 
 class QBuf(ctypes.Structure):
@@ -59,6 +60,8 @@ def _load():
     pact, pgr, pq = ctypes.POINTER(ActParams), ctypes.POINTER(Groups), ctypes.POINTER(QBuf)
     sig = {
         "mgs_abi_version": (ctypes.c_int, []),
+        "mgs_groups_table_bytes": (i64, []),
+        "mgs_groups_update": (ctypes.c_int, [pgr, vp, vp, vp]),
         "mgs_last_error": (ctypes.c_char_p, []),
         "mgs_qtensor_nbytes": (i64, [i32, i32, pgr, i64, i32]),
         "mgs_grouped_scaled_act_fwd": (ctypes.c_int, [pact, i32, pgr, i64, vp, vp, pq, pq, vp, vp]),
@@ -84,7 +87,8 @@ def _load():
 
 
 LIB = _load()
-EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
+EXPORTED = ("mgs_abi_version", "mgs_last_error", "mgs_groups_table_bytes", "mgs_groups_update",
+            "mgs_qtensor_nbytes", "mgs_grouped_scaled_act_fwd",
             "mgs_grouped_scaled_act_fwd_f32",
             "mgs_grouped_scaled_act_bwd", "mgs_grouped_scaled_act_bwd_noalloc", "mgs_act_bwd_workspace_bytes", "mgs_grouped_mx_quantize",
             "mgs_grouped_mx_quantize_workspace_bytes", "mgs_grouped_gemm_mx", "mgs_grouped_gemm_mx_fprop_act",
@@ -105,12 +109,37 @@ def abi_version():
     return LIB.mgs_abi_version()
 
 
+class DeviceGroups:
+    """Device-resident split sizes (graph-safe calls; MXFP8).  `splits` is a device int64 tensor the
+    caller fills (copy_ works under graph replay); update() enqueues the offsets computation on the
+    stream, and every call given this object afterwards reads them.  Layouts are strided for the row
+    capacity `max_rows`; `status` (device int32) turns 1 when the splits are invalid (negative, or
+    their sum above the capacity), in which case the calls write no rows."""
+
+    def __init__(self, num_groups, max_rows, device="cuda"):
+        self.num_groups, self.max_rows = int(num_groups), int(max_rows)
+        self.splits = torch.zeros(self.num_groups, dtype=torch.int64, device=device)
+        self.table = torch.empty(int(LIB.mgs_groups_table_bytes()), dtype=torch.uint8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def __len__(self):
+        return self.num_groups
+
+    def update(self, stream=None):
+        g = _GroupsArg(self)
+        _check(LIB.mgs_groups_update(g.ref, self.splits.data_ptr(), self.status.data_ptr(), _stream(stream)))
+
+
 class _GroupsArg:
     """Keeps the int64 split array alive for the duration of a call."""
 
     def __init__(self, split_sizes):
+        if isinstance(split_sizes, DeviceGroups):
+            self.arr = None
+            self.struct = Groups(split_sizes.num_groups, None, split_sizes.max_rows, split_sizes.table.data_ptr())
+            return
         self.arr = np.ascontiguousarray(np.asarray(split_sizes, dtype=np.int64))
-        self.struct = Groups(len(self.arr), self.arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        self.struct = Groups(len(self.arr), self.arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 0, None)
 
     @property
     def ref(self):
@@ -145,7 +174,6 @@ class QTensor:
         """`rht` (NVFP4 columnwise only): 16-bit sign mask of the Hadamard transform of the copy."""
         self.fmt, self.colwise, self.width = fmt, bool(colwise), int(width)
         self.rht = 0 if rht is None else RHT_ON | (int(rht) & 0xFFFF)
-        self.split_sizes = np.asarray(split_sizes, dtype=np.int64)
         nd = qtensor_nbytes(fmt, colwise, split_sizes, width, "data")
         ns = qtensor_nbytes(fmt, colwise, split_sizes, width, "scales")
         ng = qtensor_nbytes(fmt, colwise, split_sizes, width, "group_scale")

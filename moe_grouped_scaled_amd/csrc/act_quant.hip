@@ -32,7 +32,8 @@ struct PanelInfo {
   int64_t mp;   // padded token count of the group
 };
 
-__device__ __forceinline__ PanelInfo find_panel(const GroupTable& gt, int panel) {
+template <typename Table>
+__device__ __forceinline__ PanelInfo find_panel_in(const Table& gt, int panel) {
   int lo = 0, hi = gt.num_groups;  // panel_off[lo] <= panel < panel_off[hi]
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
@@ -47,6 +48,16 @@ __device__ __forceinline__ PanelInfo find_panel(const GroupTable& gt, int panel)
   pi.coff = (int64_t)PANEL_ROWS * gt.panel_off[lo];
   pi.mp = (int64_t)PANEL_ROWS * (gt.panel_off[lo + 1] - gt.panel_off[lo]);
   return pi;
+}
+
+// The panel's group and offsets, from the device copy of the table when the split sizes are
+// device-resident (DEV), else from the table passed by value.  DEV is a template parameter so that a
+// kernel reads one table only (a pointer chosen at run time between the argument and device memory
+// made the compiler copy the argument table to scratch).
+template <bool DEV>
+__device__ __forceinline__ PanelInfo find_panel(const GroupTable& gt, int panel) {
+  if constexpr (DEV) return find_panel_in(*gt.dev, panel);
+  else return find_panel_in(gt, panel);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous range of
@@ -446,6 +457,7 @@ struct Stage {
 };
 
 struct BlockPos {
+  bool ok;        // the workgroup has a block (false: it exits at once)
   PanelInfo pi;   // the wave's panel
   int gb;         // 128-token block index over all groups (columnwise padded rows / 128)
   int blk;        // 128-token block index within the group
@@ -455,14 +467,24 @@ struct BlockPos {
   int64_t col;    // the lane's first column
 };
 
+template <bool DEV>
 __device__ __forceinline__ BlockPos block_pos(const GroupTable& gt, int n_ct) {
   BlockPos bp;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  // Blocks in use: the whole grid, or with device-resident split sizes (a grid sized for the row
+  // capacity) those of the actual panels.  Each XCD takes a contiguous range of them (workgroups are
+  // dealt to the 8 XCDs round-robin); workgroups past the end of their XCD's range have no block.
+  int n;
+  if constexpr (DEV) n = n_ct * (gt.dev->num_panels >> 2);
+  else n = (int)gridDim.x;
+  const int x = blockIdx.x & 7, i = blockIdx.x >> 3, q = n >> 3, r = n & 7;
+  bp.ok = i < q + (x < r ? 1 : 0);
+  if (!bp.ok) return bp;
+  const int t = x * q + min(x, r) + i;
   const int b = t / n_ct;
   bp.ct = t - b * n_ct;
   bp.lane = threadIdx.x & 63;
   bp.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  bp.pi = find_panel(gt, 4 * b + bp.wave);
+  bp.pi = find_panel<DEV>(gt, 4 * b + bp.wave);
   bp.gb = b;
   bp.blk = bp.pi.lpanel >> 2;
   bp.lr0 = 8 * (bp.lane & 3);
@@ -608,7 +630,7 @@ __device__ __forceinline__ void cs_flush(const float* lds, float* __restrict__ p
   }
 }
 
-template <int KIND, int FMT, bool XF32>
+template <int KIND, int FMT, bool XF32, bool DEV>
 __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
                                                       const void* __restrict__ x,
                                                       const float* __restrict__ probs,
@@ -617,7 +639,8 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(ActArgs aa, GroupTable gt,
   __shared__ __attribute__((aligned(16))) uint8_t stage[Stage<FMT>::BYTES];
   __shared__ __attribute__((aligned(16))) float cs_lds[4 * BLOCK_COLS];
   const int64_t wa = out.width;
-  const BlockPos bp = block_pos(gt, n_ct);
+  const BlockPos bp = block_pos<DEV>(gt, n_ct);
+  if (!bp.ok) return;
   const PanelInfo& pi = bp.pi;
   const bool valid = bp.col < wa;
   float s_enc = 1.0f, s_enc_col = 1.0f;
@@ -685,7 +708,7 @@ __device__ __forceinline__ float dx_up(const ActArgs& aa, float g, float u, floa
   return (du * dd) * p;
 }
 
-template <int KIND, int FMT>
+template <int KIND, int FMT, bool DEV>
 __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
                                                       const uint16_t* __restrict__ x,
                                                       const uint16_t* __restrict__ dy,
@@ -703,7 +726,8 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
   uint8_t* st_dx = stage;
   uint8_t* st_up = stage + SB;
   uint8_t* st_act = stage + (GATED ? 2 : 1) * SB;
-  const BlockPos bp = block_pos(gt, n_ct);
+  const BlockPos bp = block_pos<DEV>(gt, n_ct);
+  if (!bp.ok) return;
   const PanelInfo& pi = bp.pi;
   const int lr0 = bp.lr0;
   const int64_t col = bp.col;
@@ -863,21 +887,31 @@ __device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_
   return s;
 }
 
-// dprobs[r] = sum over column tiles of the partials, in tile order
+// dprobs[r] = sum over column tiles of the partials, in tile order.  `rows` is the row stride of the
+// partials; with device-resident split sizes (`dev` non-null) only the rows in use are written.
 __global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* __restrict__ part, int n_ct,
-                                                            int rows, float* __restrict__ dprobs) {
+                                                            int rows, const GroupTable* __restrict__ dev,
+                                                            float* __restrict__ dprobs) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+  if (r >= (dev ? dev->total_rows : rows)) return;
   dprobs[r] = ordered_sum(part + r, rows, n_ct);
 }
 
 // out[g, c] = sum of the partial sums of group g's 128-token blocks, in block order.
+template <bool DEV>
 __global__ __launch_bounds__(256) void col_sum_reduce_kernel(const float* __restrict__ part, GroupTable gt,
                                                              int64_t width, float* __restrict__ out) {
   const int g = blockIdx.y;
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= width) return;
-  const int b0 = gt.panel_off[g] >> 2, b1 = gt.panel_off[g + 1] >> 2;
+  int b0, b1;
+  if constexpr (DEV) {
+    b0 = gt.dev->panel_off[g] >> 2;
+    b1 = gt.dev->panel_off[g + 1] >> 2;
+  } else {
+    b0 = gt.panel_off[g] >> 2;
+    b1 = gt.panel_off[g + 1] >> 2;
+  }
   out[(int64_t)g * width + c] = ordered_sum(part + (int64_t)b0 * width + c, width, b1 - b0);
 }
 
@@ -945,7 +979,8 @@ __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable 
                                                          int cpw, float* __restrict__ amax, uint32_t rht) {
   constexpr bool GATED = is_gated<KIND>();
   __shared__ float wmax[2][4];
-  const BlockPos bp = block_pos(gt, (n_chunks + cpw - 1) / cpw);
+  const BlockPos bp = block_pos<false>(gt, (n_chunks + cpw - 1) / cpw);
+  if (!bp.ok) return;
   const PanelInfo& pi = bp.pi;
   const int lr0 = bp.lr0;
   float p[8];
@@ -1079,10 +1114,15 @@ template <int KIND, bool XF32>
 void fwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, const GroupTable& gt,
                       const void* x, const float* probs, int64_t width_in, const QOut& out,
                       float* cs_part, int n_ct, uint16_t* x_copy) {
-  if (fmt == MGS_FMT_MXFP8)
-    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8, XF32>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
-  else
-    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_NVFP4, XF32>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+  if (gt.dev) {
+    // device-resident split sizes: MXFP8 from a BF16 input only (checked by the caller)
+    if constexpr (!XF32)
+      hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8, false, true>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+  } else if (fmt == MGS_FMT_MXFP8) {
+    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8, XF32, false>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+  } else {
+    hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_NVFP4, XF32, false>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+  }
 }
 
 template <int KIND>
@@ -1098,15 +1138,18 @@ void bwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, con
                       const uint16_t* x, const uint16_t* dy, const float* probs, int64_t width_in,
                       int64_t wa, uint16_t* dx, const QOut& dxq, float* dp_part, float* cs_part,
                       const QOut& actq, int n_ct) {
-  if (fmt == MGS_FMT_MXFP8)
-    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
+  if (gt.dev)  // device-resident split sizes: MXFP8 only (checked by the caller)
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
+  else if (fmt == MGS_FMT_MXFP8)
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
   else
-    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
 }
 
 void launch_col_sum_reduce(const GroupTable& gt, int64_t width, const float* part, float* out, hipStream_t st) {
   const dim3 grid((unsigned)((width + 255) / 256), (unsigned)gt.num_groups);
-  hipLaunchKernelGGL(col_sum_reduce_kernel, grid, dim3(256), 0, st, part, gt, width, out);
+  if (gt.dev) hipLaunchKernelGGL(col_sum_reduce_kernel<true>, grid, dim3(256), 0, st, part, gt, width, out);
+  else hipLaunchKernelGGL(col_sum_reduce_kernel<false>, grid, dim3(256), 0, st, part, gt, width, out);
 }
 
 ActArgs to_args(const ActHost& a) { return ActArgs{a.kind, a.s, a.inv_s, a.limit, a.alpha, a.beta}; }
@@ -1195,7 +1238,7 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
   }
   if (dprobs && gt.total_rows > 0)
     hipLaunchKernelGGL(dprobs_reduce_kernel, dim3((unsigned)((gt.total_rows + 255) / 256)), dim3(256), 0, st,
-                       part, n_ct, gt.total_rows, dprobs);
+                       part, n_ct, gt.total_rows, gt.dev, dprobs);
   if (dx_col_sum) launch_col_sum_reduce(gt, width_in, cs_part, dx_col_sum, st);
   return hipGetLastError();
 }
@@ -1216,6 +1259,51 @@ int64_t act_bwd_rht_offset(const GroupTable& gt, int64_t wa, int64_t width_in) {
 
 int64_t act_bwd_workspace_bytes(const GroupTable& gt, int64_t wa, int64_t width_in) {
   return act_bwd_rht_offset(gt, wa, width_in) + 8 * (int64_t)gt.num_groups;
+}
+
+namespace {
+
+// Group table from device-resident split sizes (one workgroup): row offsets, padded columnwise panel
+// offsets and their totals, for the calls of a captured graph whose routing changes between replays.
+// A negative split or a sum above the capacity sets status 1 and leaves every group empty.
+__global__ __launch_bounds__(256) void groups_update_kernel(int e, const int64_t* __restrict__ splits,
+                                                            int64_t max_rows, GroupTable* __restrict__ out,
+                                                            int32_t* __restrict__ status) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int g = threadIdx.x; g < e; g += blockDim.x)
+    if (splits[g] < 0) atomicOr(&bad, 1);
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int64_t rows = 0, panels = 0;
+  if (!bad) {
+    for (int g = 0; g < e; ++g) rows += splits[g];
+    if (rows > max_rows) bad = 1;
+  }
+  rows = 0;
+  for (int g = 0; g < e; ++g) {
+    out->row_off[g] = (int32_t)rows;
+    out->panel_off[g] = (int32_t)panels;
+    const int64_t m = bad ? 0 : splits[g];
+    rows += m;
+    panels += (m + COL_ALIGN - 1) / COL_ALIGN * (COL_ALIGN / PANEL_ROWS);
+  }
+  out->row_off[e] = (int32_t)rows;
+  out->panel_off[e] = (int32_t)panels;
+  out->num_groups = e;
+  out->num_panels = (int32_t)panels;
+  out->total_rows = (int32_t)rows;
+  out->dev = nullptr;
+  if (status) *status = bad;
+}
+
+}  // namespace
+
+hipError_t launch_groups_update(int num_groups, const int64_t* splits, int64_t max_rows, GroupTable* out,
+                                int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(groups_update_kernel, dim3(1), dim3(256), 0, st, num_groups, splits, max_rows, out, status);
+  return hipGetLastError();
 }
 
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,

@@ -71,8 +71,8 @@ constexpr int TILE_BLOCK_N = 4;
 //   FPROP B:         rowwise qtensor [E * n x k]             (scale matrix: all E * n rows)
 //   DGRAD B:         columnwise qtensor of an [E * k x n] weight: per group [n x kp], kp = roundup(k, 128)
 //   WGRAD A / B:     columnwise qtensors of widths m / n: per group [m x mp_g] / [n x mp_g]
-template <int TM, int TN>
-__device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable& tt, int tile) {
+template <int TM, int TN, typename Table>
+__device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const Table& tt, int tile) {
   int lo = 0, hi = tt.num_groups;  // tile_off[lo] <= tile < tile_off[hi]
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
@@ -140,13 +140,13 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const GemmTable&
     j.a.ld = ga.k / ediv;
     j.a.data = ga.a_data + arow0 * j.a.ld;
     j.a.sbase = ga.a_scales;
-    j.a.srows = tt.tok_off[tt.num_groups];
+    j.a.srows = tt.layout_rows;   // the K-step grouped scales are strided for the layout's rows
     j.a.srow0 = arow0;
     j.a.sld = ga.k / sblk;
     const int64_t rows_all = tt.tok_off[tt.num_groups];
     const int64_t nks = (ga.k + BK - 1) / BK;  // K steps (rowwise MXFP8 scales: 4 bytes per row and step)
     j.a.avail = (rows_all - arow0) * j.a.ld;
-    j.a.savail = nv ? rows_all * j.a.sld : 4 * rows_all * nks;
+    j.a.savail = nv ? rows_all * j.a.sld : 4 * (int64_t)tt.layout_rows * nks;
     if (ga.mode == MGS_GEMM_FPROP) {
       j.b.ld = ga.k / ediv;
       j.b.data = ga.b_data + ((int64_t)g * ga.n + brow0) * j.b.ld;
@@ -306,13 +306,19 @@ __device__ __forceinline__ int xcd_remap_gemm(int b, int n) {
   return x * q + min(x, r) + i;
 }
 
-// The tile workgroup b takes under the table's schedule (see GemmTable); false: none.
-__device__ __forceinline__ bool schedule_tile(const GemmTable& tt, int b, int nb, int* tile) {
+// The tile workgroup b takes under the table's schedule (see GemmTable); false: none.  Contiguous
+// schedule: XCD b % 8 takes its eighth of the tile sequence; with device-resident split sizes the grid
+// is sized for the capacity, so workgroups past the end of their XCD's eighth have no tile.
+template <typename Table>
+__device__ __forceinline__ bool schedule_tile(const Table& tt, int b, int* tile) {
   if (!tt.interleave) {
-    *tile = xcd_remap_gemm(b, nb);
+    const int n = tt.total_tiles, q = n >> 3, r = n & 7, x = b & 7, i = b >> 3;
+    if (i >= q + (x < r ? 1 : 0)) return false;
+    *tile = x * q + min(x, r) + i;
     return true;
   }
   const int s = b / tt.stride;
+  if (s >= tt.num_groups) return false;
   const int g = tt.order[s];
   const int j = b - s * tt.stride;
   const int t = tt.tile_off[g + 1] - tt.tile_off[g];
@@ -566,8 +572,14 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint2 bias_lds[BN2 / 4];
   int tile;
-  if (!schedule_tile(tt, blockIdx.x, gridDim.x, &tile)) return;
-  const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
+  TileJob j;
+  if (tt.dev) {
+    if (!schedule_tile(*tt.dev, blockIdx.x, &tile)) return;
+    j = make_job<BM2, BN2>(ga, *tt.dev, tile);
+  } else {
+    if (!schedule_tile(tt, blockIdx.x, &tile)) return;
+    j = make_job<BM2, BN2>(ga, tt, tile);
+  }
   if (j.k == 0) {
     write_zero_tile<BM2, BN2>(j, ga);
     return;
@@ -822,7 +834,7 @@ void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_STAGE];
   __shared__ __attribute__((aligned(16))) uint2 bias_lds[BN2 / 4];
   int tile;
-  if (!schedule_tile(tt, blockIdx.x, gridDim.x, &tile)) return;
+  if (!schedule_tile(tt, blockIdx.x, &tile)) return;
   const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
   if (j.k == 0) {
     write_zero_tile<BM2, BN2>(j, ga);
@@ -1066,17 +1078,104 @@ GemmTable make_table(const GemmArgs& ga, const GroupTable& gt, int tm, int tn) {
   tt.total_tiles = (int32_t)tiles;
   tt.interleave = 0;
   tt.grid = (int32_t)tiles;
+  tt.layout_rows = gt.total_rows;
   if (ga.mode == MGS_GEMM_WGRAD) schedule_k_grouped(tt);
   return tt;
+}
+
+// Tiles of a grid sized for the row capacity (device-resident split sizes): M-grouped launches have
+// at most ceil(capacity / TM) + E tile rows; K-grouped ones E groups of equal tiles, dealt in steps
+// of 8 by the interleaved schedule; 8 more workgroups cover the per-XCD rounding of the contiguous one.
+int64_t capacity_grid(const GemmArgs& ga, const GroupTable& gt, int tm, int tn) {
+  const int64_t ntn = (ga.n + tn - 1) / tn;
+  if (ga.mode == MGS_GEMM_WGRAD) return (int64_t)gt.num_groups * (((ga.m + tm - 1) / tm * ntn + 7) / 8 * 8) + 8;
+  return (((int64_t)gt.total_rows + tm - 1) / tm + gt.num_groups) * ntn + 8;
+}
+
+// The tile table of one launch built on the device from the device group table `gd` (one
+// workgroup): the same tables make_table and schedule_k_grouped build on the host.
+__global__ __launch_bounds__(256) void gemm_table_kernel(const GroupTable* __restrict__ gd, int mode,
+                                                         int64_t m, int64_t n, int tm, int tn,
+                                                         int layout_rows, GemmTable* __restrict__ out) {
+  __shared__ int64_t cost[MGS_MAX_GROUPS];
+  __shared__ int interleave;
+  const int e = gd->num_groups;
+  const int64_t ntn = (n + tn - 1) / tn;
+  if (threadIdx.x == 0) {
+    int64_t tiles = 0;
+    for (int g = 0; g < e; ++g) {
+      out->tile_off[g] = (int32_t)tiles;
+      if (mode == MGS_GEMM_WGRAD) {
+        out->tok_off[g] = PANEL_ROWS * gd->panel_off[g];
+        tiles += (m + tm - 1) / tm * ntn;
+      } else {
+        out->tok_off[g] = gd->row_off[g];
+        tiles += (gd->row_off[g + 1] - gd->row_off[g] + tm - 1) / tm * ntn;
+      }
+    }
+    out->tok_off[e] = mode == MGS_GEMM_WGRAD ? PANEL_ROWS * gd->panel_off[e] : gd->row_off[e];
+    out->tile_off[e] = (int32_t)tiles;
+    out->num_groups = e;
+    out->total_tiles = (int32_t)tiles;
+    out->grid = 0;
+    out->stride = 0;
+    out->layout_rows = layout_rows;
+    out->dev = nullptr;
+    interleave = 0;
+    if (mode == MGS_GEMM_WGRAD && e > 1) {
+      // the host's rule (schedule_k_grouped): deal the groups over the XCDs when the contiguous
+      // ranges leave one XCD more than 5 % above the mean cost
+      int64_t total = 0, worst = 0;
+      for (int g = 0; g < e; ++g) {
+        const int64_t steps = (PANEL_ROWS * (int64_t)(gd->panel_off[g + 1] - gd->panel_off[g]) + BK - 1) / BK;
+        cost[g] = steps ? steps + 4 : 1;
+        total += cost[g] * (out->tile_off[g + 1] - out->tile_off[g]);
+      }
+      const int64_t q = tiles / 8, r = tiles % 8;
+      for (int x = 0; x < 8; ++x) {
+        const int64_t a = x * q + (x < r ? x : r), b = (x + 1) * q + (x + 1 < r ? x + 1 : r);
+        int64_t c = 0;
+        for (int g = 0; g < e; ++g) {
+          const int64_t lo = a > out->tile_off[g] ? a : out->tile_off[g];
+          const int64_t hi = b < out->tile_off[g + 1] ? b : out->tile_off[g + 1];
+          if (hi > lo) c += cost[g] * (hi - lo);
+        }
+        worst = c > worst ? c : worst;
+      }
+      interleave = 8 * worst * 100 > total * 105 ? 1 : 0;
+    }
+    out->interleave = interleave;
+    if (interleave) out->stride = (int32_t)(((m + tm - 1) / tm * ntn + 7) / 8 * 8);
+  }
+  __syncthreads();
+  if (!interleave) return;
+  // largest cost first, ties in group order (a stable order): group g's rank among the groups
+  for (int g = threadIdx.x; g < e; g += blockDim.x) {
+    int rank = 0;
+    for (int h = 0; h < e; ++h) rank += (cost[h] > cost[g] || (cost[h] == cost[g] && h < g)) ? 1 : 0;
+    out->order[rank] = (uint8_t)g;
+  }
 }
 
 }  // namespace
 
 int64_t gemm_tile_count(const GemmArgs& ga, const GroupTable& gt) {
+  if (gt.dev) return capacity_grid(ga, gt, BM2, BN2);
   return make_table(ga, gt, BM2, BN2).total_tiles;
 }
 
-hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t st, GemmTable* dev_gemm_table) {
+  if (gt.dev) {
+    // device-resident split sizes: the launch's table is built on the device first
+    hipLaunchKernelGGL(gemm_table_kernel, dim3(1), dim3(256), 0, st, gt.dev, ga.mode, ga.m, ga.n, BM2, BN2,
+                       gt.total_rows, dev_gemm_table);
+    GemmTable tt{};
+    tt.dev = dev_gemm_table;
+    const int64_t grid = capacity_grid(ga, gt, BM2, BN2);
+    if (ga.fmt == MGS_FMT_MXFP8)
+      hipLaunchKernelGGL(gemm_mxfp8_256_kernel, dim3((unsigned)grid), dim3(256), 0, st, ga, tt);
+    return hipGetLastError();
+  }
   if (ga.fmt == MGS_FMT_MXFP8) {
     const GemmTable tt = make_table(ga, gt, BM2, BN2);
     if (tt.total_tiles == 0) return hipSuccess;

@@ -40,14 +40,31 @@ bool valid_fmt(int32_t fmt) { return fmt == MGS_FMT_MXFP8 || fmt == MGS_FMT_NVFP
 
 bool is_gated(int kind) { return kind == MGS_ACT_SWIGLU || kind == MGS_ACT_CLAMPED_SWIGLU || kind == MGS_ACT_GLU; }
 
-// Validates the groups and fills the panel table.  Returns MGS_OK or an error code.
+// Byte offset of the GEMM tile table after the group table in a device table.
+constexpr int64_t kDevGemmTableOffset = (sizeof(mgs::GroupTable) + 255) / 256 * 256;
+
+// Validates the groups and fills the panel table.  Returns MGS_OK or an error code.  Device-resident
+// split sizes: the table describes the layout for the row capacity (total_rows = max_rows, num_panels
+// = the padded-panel bound) and points to the device table holding the actual offsets.
 int build_groups(const mgs_groups* groups, mgs::GroupTable* gt, int64_t* total_rows) {
   if (!groups) return fail(MGS_ERR_INVALID_ARG, "groups is NULL");
   if (groups->num_groups < 1 || groups->num_groups > MGS_MAX_GROUPS)
     return fail(MGS_ERR_INVALID_ARG, "num_groups %d outside [1, %d]", groups->num_groups, MGS_MAX_GROUPS);
-  if (!groups->split_sizes) return fail(MGS_ERR_INVALID_ARG, "split_sizes is NULL");
   std::memset(gt, 0, sizeof *gt);
   gt->num_groups = groups->num_groups;
+  if (!groups->split_sizes) {
+    if (!groups->dev_table)
+      return fail(MGS_ERR_INVALID_ARG, "split_sizes is NULL and no dev_table for device-resident split sizes");
+    const int64_t cap = groups->max_rows;
+    if (cap <= 0 || cap > INT32_MAX - 64 - (int64_t)mgs::COL_ALIGN * (groups->num_groups + 1))
+      return fail(MGS_ERR_SHAPE, "max_rows = %lld outside [1, 2^31 - 64 - 128 (E + 1)]", (long long)cap);
+    gt->total_rows = (int32_t)cap;
+    gt->num_panels = (int32_t)(((cap + mgs::COL_ALIGN - 1) / mgs::COL_ALIGN + groups->num_groups) *
+                               (mgs::COL_ALIGN / mgs::PANEL_ROWS));
+    gt->dev = static_cast<const mgs::GroupTable*>(groups->dev_table);
+    *total_rows = cap;
+    return MGS_OK;
+  }
   int64_t rows = 0, panels = 0;
   for (int g = 0; g < groups->num_groups; ++g) {
     const int64_t m = groups->split_sizes[g];
@@ -77,6 +94,9 @@ int check_width(int64_t w, const char* what) {
 // columnwise matrix (padded rows x width codes) and the whole rowwise MXFP8 scale array must fit.
 int check_extent(const mgs::GroupTable& gt, int64_t width, const char* what) {
   const int64_t lim = (int64_t)1 << 31;
+  if (gt.dev && (int64_t)mgs::PANEL_ROWS * gt.num_panels * width >= lim)
+    return fail(MGS_ERR_SHAPE, "max_rows x %s too large: one group's padded columnwise matrix could reach 2^31 "
+                "elements", what);
   for (int g = 0; g < gt.num_groups; ++g) {
     const int64_t padded = (int64_t)mgs::PANEL_ROWS * (gt.panel_off[g + 1] - gt.panel_off[g]);
     if (padded * width >= lim)
@@ -142,6 +162,18 @@ mgs::QOut make_qout(const mgs_qbuf* row, const mgs_qbuf* col, int64_t width) {
   return q;
 }
 
+bool device_splits(const mgs::GroupTable& gt) { return gt.dev != nullptr; }
+
+mgs::GemmTable* dev_gemm_table(const mgs_groups* groups) {
+  return groups->split_sizes ? nullptr
+                             : reinterpret_cast<mgs::GemmTable*>(static_cast<uint8_t*>(groups->dev_table) +
+                                                                 kDevGemmTableOffset);
+}
+
+int unsupported_with_device_splits(const char* what) {
+  return fail(MGS_ERR_UNSUPPORTED, "%s is not available with device-resident split sizes (MXFP8 only)", what);
+}
+
 int hip_status(hipError_t e) {
   if (e != hipSuccess) return fail(MGS_ERR_HIP, "HIP launch error: %s", hipGetErrorString(e));
   return ok();
@@ -186,6 +218,7 @@ int act_bwd_impl(const mgs_act_params* act, int32_t fmt, const mgs_groups* group
   mgs::GroupTable gt;
   int64_t rows = 0;
   if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
@@ -236,6 +269,22 @@ extern "C" {
 
 int mgs_abi_version(void) { return MGS_ABI_VERSION; }
 
+int64_t mgs_groups_table_bytes(void) { return kDevGemmTableOffset + (int64_t)sizeof(mgs::GemmTable); }
+
+int mgs_groups_update(const mgs_groups* groups, const int64_t* split_sizes_dev, int32_t* status_dev,
+                      void* stream) {
+  if (!groups) return fail(MGS_ERR_INVALID_ARG, "groups is NULL");
+  if (groups->split_sizes) return fail(MGS_ERR_INVALID_ARG, "groups has host split sizes (split_sizes must be NULL)");
+  mgs::GroupTable gt;
+  int64_t rows = 0;
+  int rc = build_groups(groups, &gt, &rows);
+  if (rc) return rc;
+  if (!split_sizes_dev) return fail(MGS_ERR_INVALID_ARG, "split_sizes_dev is NULL");
+  return hip_status(mgs::launch_groups_update(groups->num_groups, split_sizes_dev, groups->max_rows,
+                                              static_cast<mgs::GroupTable*>(groups->dev_table), status_dev,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char* mgs_last_error(void) { return g_err; }
 
 int64_t mgs_qtensor_nbytes(int32_t fmt, int32_t colwise, const mgs_groups* groups, int64_t width,
@@ -270,6 +319,7 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
   mgs::GroupTable gt;
   int64_t rows = 0;
   if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
@@ -297,6 +347,7 @@ int mgs_grouped_scaled_act_fwd_f32(const mgs_act_params* act, int32_t fmt, const
   mgs::GroupTable gt;
   int64_t rows = 0;
   if ((rc = build_groups(groups, &gt, &rows))) return rc;
+  if (device_splits(gt)) return unsupported_with_device_splits("the FP32-input forward");
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
@@ -363,6 +414,7 @@ int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width
   int64_t rows = 0;
   int rc = build_groups(groups, &gt, &rows);
   if (rc) return rc;
+  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if ((rc = check_width(width, "width"))) return rc;
   if ((rc = check_extent(gt, width, "width"))) return rc;
   if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
@@ -413,6 +465,7 @@ int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int
   int64_t rows = 0;
   int rc = build_groups(groups, &gt, &rows);
   if (rc) return rc;
+  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if (!a || !a->data || !a->scales) return fail(MGS_ERR_INVALID_ARG, "operand A (data, scales) is NULL");
   if (!b || !b->data || !b->scales) return fail(MGS_ERR_INVALID_ARG, "operand B (data, scales) is NULL");
   if (fmt == MGS_FMT_NVFP4 && (!a->group_scale || !b->group_scale))
@@ -444,7 +497,7 @@ int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int
   ga.accumulate = accumulate != 0;
   ga.bias = static_cast<const uint16_t*>(bias_bf16);
   if (mgs::gemm_tile_count(ga, gt) > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
-  return hip_status(mgs::launch_gemm(ga, gt, static_cast<hipStream_t>(stream)));
+  return hip_status(mgs::launch_gemm(ga, gt, static_cast<hipStream_t>(stream), dev_gemm_table(groups)));
 }
 
 int mgs_grouped_gemm_mx_fprop_act(const mgs_groups* groups, int64_t m, int64_t n, int64_t k,
@@ -496,7 +549,7 @@ int mgs_grouped_gemm_mx_fprop_act(const mgs_groups* groups, int64_t m, int64_t n
   ga.act_data = static_cast<uint8_t*>(out_row->data);
   ga.act_scales = static_cast<uint8_t*>(out_row->scales);
   if (mgs::gemm_tile_count(ga, gt) > INT32_MAX / 2) return fail(MGS_ERR_SHAPE, "too many tiles");
-  return hip_status(mgs::launch_gemm(ga, gt, static_cast<hipStream_t>(stream)));
+  return hip_status(mgs::launch_gemm(ga, gt, static_cast<hipStream_t>(stream), dev_gemm_table(groups)));
 }
 
 int mgs_grouped_col_sum(const mgs_groups* groups, int64_t width, const void* x_bf16, float* out,
@@ -505,6 +558,7 @@ int mgs_grouped_col_sum(const mgs_groups* groups, int64_t width, const void* x_b
   int64_t rows = 0;
   int rc = build_groups(groups, &gt, &rows);
   if (rc) return rc;
+  if (device_splits(gt)) return unsupported_with_device_splits("mgs_grouped_col_sum");
   if (width <= 0 || width % 8 != 0) return fail(MGS_ERR_SHAPE, "width must be a positive multiple of 8");
   if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
   if (!out) return fail(MGS_ERR_INVALID_ARG, "out is NULL");

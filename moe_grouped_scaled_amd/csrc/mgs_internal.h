@@ -21,12 +21,20 @@ constexpr int COL_ALIGN = 128;
 //   panel_off[g] = sum_{h<g} roundup(m_h, 128) / 32         (E + 1 entries); the padded columnwise
 //                  token offset of group g is 32 * panel_off[g] and its padded length
 //                  32 * (panel_off[g+1] - panel_off[g]); panels past a group's last row are padding.
+//
+// Device-resident split sizes (graph-safe calls): the table passed by value then describes the
+// layout for a row capacity -- total_rows = the capacity, num_panels = an upper bound of the padded
+// panels -- and `dev` points to a copy in device memory that holds the actual offsets, written by
+// groups_update_kernel from the device split sizes.  Kernels take offsets (row_off, panel_off and the
+// actual counts) from *dev and layout strides and extents from the by-value table; null `dev`: both
+// are the by-value table.
 struct GroupTable {
   int32_t num_groups;
   int32_t num_panels;
   int32_t total_rows;
   int32_t row_off[MGS_MAX_GROUPS + 1];
   int32_t panel_off[MGS_MAX_GROUPS + 1];
+  const GroupTable* dev;
 };
 
 // One quantized output (rowwise and/or columnwise copies) of logical width `width`.
@@ -66,7 +74,13 @@ struct GemmTable {
   int32_t interleave;
   int32_t grid;                          // workgroups of the launch
   int32_t stride;
+  // rows of the layout the M-grouped operand A's rowwise MXFP8 scales are strided for (the rows in
+  // use, or the row capacity with device-resident split sizes)
+  int32_t layout_rows;
   uint8_t order[MGS_MAX_GROUPS];
+  // device-resident split sizes: the table of this launch in device memory (written by
+  // gemm_table_kernel just before it); the by-value fields are then unused
+  const GemmTable* dev;
 };
 
 struct GemmArgs {
@@ -121,8 +135,16 @@ int64_t act_bwd_workspace_bytes(const GroupTable& gt, int64_t wa, int64_t width_
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,
                           hipStream_t stream);
 
-// Builds the per-group tile table for the kernel variant of `ga.fmt` and launches it.
-hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t stream);
+// Builds the per-group tile table for the kernel variant of `ga.fmt` and launches it.  With
+// device-resident split sizes (gt.dev) the table is built on the device into `dev_gemm_table` first.
+hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t stream,
+                       GemmTable* dev_gemm_table = nullptr);
 int64_t gemm_tile_count(const GemmArgs& ga, const GroupTable& gt);
+
+// Device-resident split sizes: the actual group table from `splits` (device int64 [E]) into `out`
+// (device), capacity `max_rows`; status (device int32): 0, or 1 when a split is negative or the
+// sum exceeds the capacity (the table then describes empty groups, so every call writes nothing).
+hipError_t launch_groups_update(int num_groups, const int64_t* splits, int64_t max_rows, GroupTable* out,
+                                int32_t* status, hipStream_t stream);
 
 }  // namespace mgs

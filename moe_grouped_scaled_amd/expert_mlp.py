@@ -103,7 +103,14 @@ class ExpertMLP:
 
     # ------------------------------------------------------------------ forward
     def forward(self, x1, probs, splits):
+        """`splits`: host split sizes, or an N.DeviceGroups (device-resident split sizes, MXFP8): then
+        x1 and probs have the capacity's rows, only the first sum(splits) of which are used, and the
+        step enqueues the offsets computation first, so that a captured graph of the step follows the
+        split sizes held in the device tensor at each replay."""
         e, h, f, f_in = self.e, self.h, self.f, self.f_in
+        if isinstance(splits, N.DeviceGroups):
+            assert self.fmt == "mxfp8" and not self.fc1_fp32_act, "device-resident split sizes: MXFP8, BF16 FC1 output"
+            splits.update()
         m = x1.shape[0]
         fmt = self.fmt
         wsplit1, wsplit2 = [f_in] * e, [h] * e
@@ -135,7 +142,8 @@ class ExpertMLP:
         y2 = torch.empty((m, h), dtype=torch.bfloat16, device="cuda")
         N.grouped_gemm_mx("fprop", fmt, splits, m, h, f, a_row, w2_row, y2, bias=self.b2)
         del a_row, w2_row
-        self.ctx = dict(splits=list(map(int, splits)), m=m, y1=y1, probs=probs, a_col=a_col,
+        self.ctx = dict(splits=splits if isinstance(splits, N.DeviceGroups) else list(map(int, splits)), m=m, y1=y1,
+                        probs=probs, a_col=a_col,
                         a_amax=a_amax, x1_col=x1_col, w1_col=w1_col, w2_col=w2_col)
         return y2
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_symbols():
         assert hasattr(lib, name), name
     assert set(_native.EXPORTED) == set(_declared_symbols())
-    assert _native.abi_version() == 7
+    assert _native.abi_version() == 8
 
 
 def test_qtensor_nbytes_layouts():
@@ -227,3 +227,53 @@ def test_last_error_is_cleared_on_success():
     assert "multiple of 32" in N.last_error()
     N.qtensor_nbytes("mxfp8", False, [32], 32, "data")
     assert N.last_error() == ""
+
+
+class _FakeTable:
+    def data_ptr(self):
+        return FAKE
+
+
+def _fake_device_groups(e, cap):
+    """A DeviceGroups whose device table is a never-dereferenced address (host validation only)."""
+    from moe_grouped_scaled_amd import _native as N
+    dg = N.DeviceGroups.__new__(N.DeviceGroups)
+    dg.num_groups, dg.max_rows, dg.table = e, cap, _FakeTable()
+    return dg
+
+
+def test_device_resident_splits_validation_and_capacity_layouts():
+    """With device-resident split sizes the layouts are those of the row capacity: rowwise copies
+    hold max_rows rows, columnwise ones the padded bound 128 (ceil(max_rows / 128) + E) rows; the
+    GEMMs take m (k for WGRAD) = max_rows; NVFP4, the FP32-input forward and the standalone column
+    sum are refused; the offsets update needs device split sizes and a device table."""
+    from moe_grouped_scaled_amd import _native as N
+    assert N.LIB.mgs_groups_table_bytes() >= 2 * (2 * 65 + 4) * 4
+    e, cap, w = 4, 300, 96
+    dg = _fake_device_groups(e, cap)
+    assert N.qtensor_nbytes("mxfp8", False, dg, w, "data") == cap * w
+    assert N.qtensor_nbytes("mxfp8", True, dg, w, "data") == 128 * (-(-cap // 128) + e) * w
+    assert N.qtensor_nbytes("mxfp8", False, dg, w, "scales") >= cap * w // 32
+    assert N.act_bwd_workspace_bytes(N.act_params("srelu"), dg, w) >= \
+        N.act_bwd_workspace_bytes(N.act_params("srelu"), [cap - 3 * 64 - 1, 64, 64, 64], w)
+    q = _FakeQ().q
+    act = N.act_params("srelu")
+    _expect(-3, N.grouped_scaled_act_fwd, act, "nvfp4", dg, w, FAKE, FAKE, out_row=q, group_amax=FAKE,
+            stream=0, match="device-resident")
+    _expect(-3, N.grouped_scaled_act_fwd_f32, act, "mxfp8", dg, w, FAKE, FAKE, out_row=q, stream=0,
+            match="FP32-input")
+    _expect(-3, N.grouped_col_sum, dg, w, FAKE, FAKE, stream=0, match="device-resident")
+    _expect(-3, N.grouped_mx_quantize, "nvfp4", dg, w, FAKE, out_row=q, group_amax=FAKE, stream=0)
+    import torch
+    c = torch.empty(1, dtype=torch.float32)
+    _expect(-2, N.grouped_gemm_mx, "fprop", "mxfp8", dg, cap - 1, 64, 64, q, q, c, stream=0, match="split sum")
+    _expect(-2, N.grouped_gemm_mx, "wgrad", "mxfp8", dg, 64, 64, cap + 1, q, q, c, stream=0, match="split sum")
+    _expect(-2, N.qtensor_nbytes, "mxfp8", False, _fake_device_groups(e, 0), w, "data", match="max_rows")
+    g = N._GroupsArg([1, 2, 3, 4])
+    assert N.LIB.mgs_groups_update(g.ref, FAKE, None, None) == -1
+    assert "host split sizes" in N.last_error()
+    g = N._GroupsArg(dg)
+    assert N.LIB.mgs_groups_update(g.ref, None, None, None) == -1
+    assert "split_sizes_dev" in N.last_error()
+    g.struct.dev_table = None
+    assert N.LIB.mgs_groups_update(g.ref, FAKE, None, None) == -1
