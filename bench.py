@@ -68,12 +68,21 @@ def act_bwd_bytes(m, w_in, w_a, fmt, dense=True, row=True, col=True, dprobs=True
 
 class Timer:
     """Wraps the binding's entry points to record HIP events around every call on the stream the
-    library launches on (torch's current stream)."""
+    library launches on (torch's current stream).
+
+    The events come from a pool created with the Timer, before the warm-up steps.  Creating timing
+    events during the timed steps, or creating none at all, left one ~35 ms host stall in the timed
+    region about 140 kernel dispatches after the synchronization that opens it: the GPU drained and
+    idled, and its clocks took the next ~15 launches to recover (one launch measured 15-50 ms, the
+    step 4.9-5.1 instead of 4.25 ms).  With the pool created first, no stall occurs."""
+
+    POOL = 4000
 
     def __init__(self, N):
         import torch
         self.torch, self.N = torch, N
         self.records = []
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(self.POOL)]
         self.enabled = False
         self._orig = {}
         for name in ("grouped_scaled_act_fwd", "grouped_scaled_act_fwd_f32", "grouped_scaled_act_bwd",
@@ -88,7 +97,10 @@ class Timer:
         def wrapped(*a, **kw):
             if not self.enabled:
                 return orig(*a, **kw)
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if len(self.pool) >= 2:
+                s, e = self.pool.pop(), self.pool.pop()
+            else:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
             r = orig(*a, **kw)
             e.record()
@@ -242,9 +254,9 @@ def bench_zipf(args):
         dw2 = torch.empty((e, hid, w_a), dtype=torch.float32, device="cuda")
         N.grouped_gemm_mx("wgrad", "mxfp8", splits, hid, w_a, m, g2c, ac, dw2)
 
+    timer = Timer(N)
     for _ in range(args.warmup):
         step()
-    timer = Timer(N)
     torch.cuda.synchronize()
     timer.enabled = True
     t0 = time.perf_counter()
@@ -386,9 +398,9 @@ def main():
         mlp.backward(dy2)
         mlp.backward_dw()
 
+    timer = Timer(N)
     for _ in range(args.warmup):
         step()
-    timer = Timer(N)
     torch.cuda.synchronize()
     timer.enabled = True
     t0 = time.perf_counter()
