@@ -139,8 +139,12 @@ __device__ __forceinline__ Bf16View bf16_view(const uint16_t* p, int64_t ld, int
 struct RowDst {
   rsrc_t data, scales;
   uint32_t dvo, dpitch, svo, spitch;
-  uint32_t pad;  // MXFP8: zero bytes to write after the row's last scale (rest of the K step)
-  bool sc_lane;  // this lane writes its block's scale
+  uint32_t pad;     // MXFP8 byte mode: zero bytes to write after the row's last scale (rest of the K step)
+  bool sc_lane;     // byte mode: this lane writes its block's scale
+  // MXFP8 dword mode (the workgroup's 128 columns are one K step): each row's four scales are
+  // gathered into the lane of column chunk 0 (sd_lane), which writes them as one dword
+  bool dword_mode, sd_lane;
+  bool sd_aligned;  // dword mode: the lane's eight scale dwords start 16-byte aligned
 };
 
 // MXFP8 row scales are grouped per 128-wide K step: the byte of row r, 32-block kb of an R-row
@@ -159,6 +163,12 @@ __device__ __forceinline__ RowDst row_dst(const QOut& q, int64_t w, int64_t srow
     d.spitch = 4;
     d.pad = kb == nkb - 1 ? (uint32_t)(nks * 4 - nkb) : 0u;
     d.sc_lane = ((lane >> 2) & 3) == 0;
+    // the workgroup's first column (chunk 0) starts a K step: always for a unary kind or the gate
+    // half, for the up half of a gated kind when its offset (the output width) is a multiple of 128
+    d.dword_mode = ((col - 8 * (lane >> 2)) & 127) == 0;
+    d.sd_lane = (lane >> 2) == 0;
+    const uint64_t sbyte = reinterpret_cast<uint64_t>(q.row_scales) + (uint64_t)(row0 * 4) + d.svo;
+    d.sd_aligned = (sbyte & 15) == 0;
   } else {
     d.data = view(q.row_data, row0 * w / 2, srows * w / 2);
     d.scales = view(q.row_scales, row0 * (w >> 4), srows * (w >> 4));
@@ -167,6 +177,9 @@ __device__ __forceinline__ RowDst row_dst(const QOut& q, int64_t w, int64_t srow
     d.svo = (uint32_t)lr0 * (uint32_t)(w >> 4) + (uint32_t)(col >> 4);
     d.spitch = (uint32_t)(w >> 4);
     d.pad = 0;
+    d.dword_mode = false;
+    d.sd_lane = false;
+    d.sd_aligned = false;
     d.sc_lane = ((lane >> 2) & 1) == 0;
   }
   return d;
@@ -210,19 +223,34 @@ __device__ __forceinline__ ColDst col_dst(const QOut& q, int64_t w, int64_t tota
 
 // ---------------------------------------------------------------------------------- tile emitters
 
-// Rowwise quantization of row i (8 values) of the lane's tile; rv: the row is real.
+// MXFP8 row scales of one 128-column K step: block kb's code sits in the lanes of 16-lane row kb
+// (column chunks 4 kb .. 4 kb + 3); two lane swaps gather the row's four codes, kb in byte kb, into
+// its chunk-0 lane (lane lr0 / 8).  `code` must be 0 for blocks past the tensor's width: their bytes
+// are the zero padding of the last K step.
+__device__ __forceinline__ uint32_t gather_scale_dword(uint32_t code) {
+  const U2 a = swap32(code, code);        // lanes 0..31: blocks (kb, kb + 2)
+  const uint32_t w = a.x | (a.y << 16);
+  const U2 b = swap16(w, w);              // lanes 0..15: (w of blocks 0, 2; w of blocks 1, 3)
+  return b.x | (b.y << 8);
+}
+
+// Rowwise quantization of row i (8 values) of the lane's tile; rv: the row is real, valid: the
+// lane's columns are.  MXFP8 in dword mode returns the row's scale dword (in the chunk-0 lanes) for
+// flush_row_scales; otherwise the lane stores its block's scale byte here.
 template <int FMT>
-__device__ __forceinline__ void quant_row(const float (&v)[8], const RowDst& d, int i, bool rv,
-                                          float s_enc) {
+__device__ __forceinline__ uint32_t quant_row(const float (&v)[8], const RowDst& d, int i, bool rv,
+                                              bool valid, float s_enc) {
   float m = absmax8(v);
   if constexpr (FMT == MGS_FMT_MXFP8) {
     m = row4_max(m);
     const Mx8 e = mx_encode8(v, m);
-    const bool sv = rv && d.sc_lane;
     bst8(e.q, d.data, rv ? d.dvo : MASKED, i * d.dpitch);
+    if (d.dword_mode) return gather_scale_dword(valid ? e.code : 0u);
+    const bool sv = rv && d.sc_lane;
     bst1(e.code, d.scales, sv ? d.svo : MASKED, i * d.spitch);
 #pragma unroll
     for (uint32_t t = 1; t <= 3; ++t) bst1(0, d.scales, sv && t <= d.pad ? d.svo + t : MASKED, i * d.spitch);
+    return 0u;
   } else {
     m = pair4_max(m);
     const NvBlock b = nv_block(m, s_enc);
@@ -231,6 +259,25 @@ __device__ __forceinline__ void quant_row(const float (&v)[8], const RowDst& d, 
     for (int j = 0; j < 8; ++j) e[j] = b.r != 0.0f ? v[j] * b.r : 0.0f;
     bst4(e2m1x8(e), d.data, rv ? d.dvo : MASKED, i * d.dpitch);
     bst1(b.code, d.scales, rv && d.sc_lane ? d.svo : MASKED, i * d.spitch);
+    return 0u;
+  }
+}
+
+// MXFP8: the scale dwords of the tile's eight rows (rows lr0 .. lr0 + 7 of the panel, real when
+// < nrows) from the chunk-0 lanes: two 16-byte stores when all eight are real and aligned, else one
+// dword per real row.
+template <int FMT>
+__device__ __forceinline__ void flush_row_scales(const RowDst& d, const uint32_t (&sdw)[8], int lr0,
+                                                 int nrows) {
+  if constexpr (FMT == MGS_FMT_MXFP8) {
+    if (!d.dword_mode || !d.sd_lane) return;
+    if (d.sd_aligned && lr0 + 8 <= nrows) {
+      bst16(make_uint4(sdw[0], sdw[1], sdw[2], sdw[3]), d.scales, d.svo, 0);
+      bst16(make_uint4(sdw[4], sdw[5], sdw[6], sdw[7]), d.scales, d.svo + 16u, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bst4(sdw[i], d.scales, lr0 + i < nrows ? d.svo + 4u * i : MASKED, 0);
+    }
   }
 }
 
@@ -260,8 +307,10 @@ __device__ __forceinline__ void quant_col(const float (&v)[8], const ColDst& d, 
 template <int FMT>
 __device__ __forceinline__ void emit_row(const float (&y)[8][8], const RowDst& d, int lr0, int nrows,
                                          bool valid, float s_enc) {
+  uint32_t sdw[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) quant_row<FMT>(y[i], d, i, valid && (lr0 + i) < nrows, s_enc);
+  for (int i = 0; i < 8; ++i) sdw[i] = quant_row<FMT>(y[i], d, i, valid && (lr0 + i) < nrows, valid, s_enc);
+  flush_row_scales<FMT>(d, sdw, lr0, nrows);
 }
 
 // Columnwise quantization of a whole 8 x 8 tile.
@@ -757,7 +806,30 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
   const Bf16View dxv = bf16_view(dx, width_in, pi.row0, gt.total_rows, lr0, col);
   const RowDst rd = row_dst<FMT>(dxq, width_in, gt.total_rows, pi.row0, lr0, col, bp.lane);
 
+  // recompute first: y = a * p -> columnwise codes of the activation, one column of the lane's tile
+  // at a time, so that the inputs (not 64 FP32 results) are what stays live into the dx phase; the
+  // inputs are laundered afterwards so that phase evaluates a(x) afresh instead of keeping these
+  if (actq.col_data) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (GATED) v[i] = act_gated<KIND>(bf16_at(xg[i], j), bf16_at(xu[GATED ? i : 0], j), aa) * p[i];
+        else v[i] = act_unary<KIND>(bf16_at(xg[i], j), aa) * p[i];
+      }
+      if (FMT == MGS_FMT_NVFP4 && actq.col_rht) rht16_col(v, actq.col_rht, bp.lane & 3);
+      stage_col<FMT>(v, st_act, bp, j, s_act);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      launder(xg[i]);
+      if constexpr (GATED) launder(xu[GATED ? i : 0]);
+    }
+  }
+
   float d[8][8], dpacc[8];
+  uint32_t sdw[8];
   // column sums over the lane's rows (in row order) of the BF16-rounded dx, the values the dense
   // output holds; taken from the finished tile so that no accumulators live through the row loop
   auto col_sums = [&](float* lds) {
@@ -787,8 +859,9 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
     }
     pin(dpacc[i]);
     if (dx) bst16(pack8_bf16(d[i]), dxv.r, rv ? dxv.vo : MASKED, i * dxv.ld2);
-    if (dxq.row_data) quant_row<FMT>(d[i], rd, i, rv, s_dx);
+    if (dxq.row_data) sdw[i] = quant_row<FMT>(d[i], rd, i, rv, valid, s_dx);
   }
+  if (dxq.row_data) flush_row_scales<FMT>(rd, sdw, lr0, pi.nrows);
   if (cs_part) col_sums(cs_lds);
   if (dxq.col_data) stage_tile<FMT>(d, st_dx, bp, s_dx_col, dxq.col_rht);
   // gated: the up half in the same registers
@@ -807,29 +880,11 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
       for (int j = 0; j < 8; ++j)
         d[i][j] = dx_up<KIND>(aa, bf16_at(xg[i], j), bf16_at(xu[GATED ? i : 0], j), bf16_at(dyt[i], j), p[i]);
       if (dx) bst16(pack8_bf16(d[i]), dxv.r, rv ? dxv.vo + up2 : MASKED, i * dxv.ld2);
-      if (dxq.row_data) quant_row<FMT>(d[i], ru, i, rv, s_dx);
+      if (dxq.row_data) sdw[i] = quant_row<FMT>(d[i], ru, i, rv, valid, s_dx);
     }
+    if (dxq.row_data) flush_row_scales<FMT>(ru, sdw, lr0, pi.nrows);
     if (cs_part) col_sums(cs_lds + 4 * BLOCK_COLS);
     if (dxq.col_data) stage_tile<FMT>(d, st_up, bp, s_dx_col, dxq.col_rht);
-  }
-  // recompute: y = a * p -> columnwise codes of the activation
-  if (actq.col_data) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      launder(xg[i]);
-      if constexpr (GATED) launder(xu[GATED ? i : 0]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (GATED) v[i] = act_gated<KIND>(bf16_at(xg[i], j), bf16_at(xu[GATED ? i : 0], j), aa) * p[i];
-        else v[i] = act_unary<KIND>(bf16_at(xg[i], j), aa) * p[i];
-      }
-      if (FMT == MGS_FMT_NVFP4 && actq.col_rht) rht16_col(v, actq.col_rht, bp.lane & 3);
-      stage_col<FMT>(v, st_act, bp, j, s_act);
-    }
   }
 
   if (dp_part) {
@@ -839,17 +894,28 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(ActArgs aa, GroupTable gt,
       float v = dpacc[i];
       v += dpp_f<DPP_ROW_ROR4>(v);
       v += dpp_f<DPP_ROW_ROR8>(v);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
+      // + the lane 16 apart, then + the lane 32 apart (lane swaps: a + b is the same either way round)
+      const U2 h = swap16(__float_as_uint(v), __float_as_uint(v));
+      v = __uint_as_float(h.x) + __uint_as_float(h.y);
+      const U2 w = swap32(__float_as_uint(v), __float_as_uint(v));
+      v = __uint_as_float(w.x) + __uint_as_float(w.y);
       dpacc[i] = v;
     }
     if (bp.lane < 4) {
-      const rsrc_t r = view(dp_part, ((int64_t)bp.ct * gt.total_rows + pi.row0) * 4,
-                            (int64_t)n_ct * gt.total_rows * 4);
+      const int64_t first = (int64_t)bp.ct * gt.total_rows + pi.row0;
+      const rsrc_t r = view(dp_part, first * 4, (int64_t)n_ct * gt.total_rows * 4);
+      // the lane's eight rows are contiguous: two 16-byte stores when all are real and aligned
+      if (((reinterpret_cast<uintptr_t>(dp_part) >> 2) + first + lr0) % 4 == 0 &&
+          (reinterpret_cast<uintptr_t>(dp_part) & 3) == 0 && lr0 + 8 <= pi.nrows) {
+        bst16(make_uint4(__float_as_uint(dpacc[0]), __float_as_uint(dpacc[1]), __float_as_uint(dpacc[2]),
+                         __float_as_uint(dpacc[3])), r, (uint32_t)lr0 * 4u, 0);
+        bst16(make_uint4(__float_as_uint(dpacc[4]), __float_as_uint(dpacc[5]), __float_as_uint(dpacc[6]),
+                         __float_as_uint(dpacc[7])), r, (uint32_t)lr0 * 4u + 16u, 0);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dpacc[i]), r,
-                                              (int)((lr0 + i) < pi.nrows ? (uint32_t)(lr0 + i) * 4u : MASKED), 0, 0);
+        for (int i = 0; i < 8; ++i)
+          bst4(__float_as_uint(dpacc[i]), r, (lr0 + i) < pi.nrows ? (uint32_t)(lr0 + i) * 4u : MASKED, 0);
+      }
     }
   }
 

@@ -181,18 +181,6 @@ __device__ __forceinline__ TileJob make_job(const GemmArgs& ga, const Table& tt,
   return j;
 }
 
-// Lane exchanges of gfx950 (VALU, no LDS).  swap16(a, b): lanes of even 16-lane rows get
-// (a[l], a[l + 16]), lanes of odd rows (b[l - 16], b[l]); swap32(a, b): lanes 0..31 get (a[l], a[l + 32]),
-// lanes 32..63 (b[l - 32], b[l]) (measured on the device).
-struct U2 { uint32_t x, y; };
-__device__ __forceinline__ U2 swap16(uint32_t a, uint32_t b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  return U2{r[0], r[1]};
-}
-__device__ __forceinline__ U2 swap32(uint32_t a, uint32_t b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  return U2{r[0], r[1]};
-}
 // max over the lanes l, l ^ 16, l ^ 32, l ^ 48 of a non-negative value (its bits order like
 // unsigned integers)
 __device__ __forceinline__ float max_over_rows(float m) {

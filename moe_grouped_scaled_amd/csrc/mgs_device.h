@@ -64,6 +64,19 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Lane exchanges of gfx950 (VALU, no LDS).  swap16(a, b): lanes of even 16-lane rows get
+// (a[l], a[l + 16]), lanes of odd rows (b[l - 16], b[l]); swap32(a, b): lanes 0..31 get (a[l], a[l + 32]),
+// lanes 32..63 (b[l - 32], b[l]) (measured on the device).
+struct U2 { uint32_t x, y; };
+__device__ __forceinline__ U2 swap16(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return U2{r[0], r[1]};
+}
+__device__ __forceinline__ U2 swap32(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return U2{r[0], r[1]};
+}
+
 // max over the 4 lanes of a quad (v >= 0)
 __device__ __forceinline__ float quad_max(float v) {
   uint32_t u = __float_as_uint(v);
