@@ -953,22 +953,27 @@ __device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_
   return s;
 }
 
-// dprobs[r] = sum over column tiles of the partials, in tile order.  `rows` is the row stride of the
-// partials; with device-resident split sizes (`dev` non-null) only the rows in use are written.
-__global__ __launch_bounds__(256) void dprobs_reduce_kernel(const float* __restrict__ part, int n_ct,
-                                                            int rows, const GroupTable* __restrict__ dev,
-                                                            float* __restrict__ dprobs) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= (dev ? dev->total_rows : rows)) return;
-  dprobs[r] = ordered_sum(part + r, rows, n_ct);
-}
-
-// out[g, c] = sum of the partial sums of group g's 128-token blocks, in block order.
+// The fixed-order sums of the partials, in one launch.  Workgroups [0, dp_blocks): dprobs[r] = the sum
+// over the column tiles of dp_part[ct * rows + r], in tile order (`rows` is the row stride; with
+// device-resident split sizes only the rows in use are written).  The rest, one per group and 256
+// columns (cs_bx per group): cs_out[g, c] = the sum of group g's 128-token block partials
+// cs_part[block * width + c], in block order.
 template <bool DEV>
-__global__ __launch_bounds__(256) void col_sum_reduce_kernel(const float* __restrict__ part, GroupTable gt,
-                                                             int64_t width, float* __restrict__ out) {
-  const int g = blockIdx.y;
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ dp_part, int n_ct, int rows,
+                                                     float* __restrict__ dprobs, int dp_blocks,
+                                                     const float* __restrict__ cs_part, GroupTable gt,
+                                                     int64_t width, float* __restrict__ cs_out, int cs_bx) {
+  const int b = blockIdx.x;
+  if (b < dp_blocks) {
+    const int r = b * 256 + threadIdx.x;
+    int used;
+    if constexpr (DEV) used = gt.dev->total_rows;
+    else used = rows;
+    if (r < used) dprobs[r] = ordered_sum(dp_part + r, rows, n_ct);
+    return;
+  }
+  const int k = b - dp_blocks, g = k / cs_bx;
+  const int64_t c = (int64_t)(k - g * cs_bx) * 256 + threadIdx.x;
   if (c >= width) return;
   int b0, b1;
   if constexpr (DEV) {
@@ -978,7 +983,7 @@ __global__ __launch_bounds__(256) void col_sum_reduce_kernel(const float* __rest
     b0 = gt.panel_off[g] >> 2;
     b1 = gt.panel_off[g + 1] >> 2;
   }
-  out[(int64_t)g * width + c] = ordered_sum(part + (int64_t)b0 * width + c, width, b1 - b0);
+  cs_out[(int64_t)g * width + c] = ordered_sum(cs_part + (int64_t)b0 * width + c, width, b1 - b0);
 }
 
 // Per-group column sums.  A workgroup owns one group x 128 columns; lane (rs = lane / 16,
@@ -1212,10 +1217,23 @@ void bwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, con
     hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
 }
 
+// dprobs from its partials (when dprobs is non-null) and the column sums from theirs (when cs_out is
+// non-null), in one launch of reduce_kernel.
+void launch_reduce(const GroupTable& gt, const float* dp_part, int n_ct, float* dprobs, const float* cs_part,
+                   int64_t width, float* cs_out, hipStream_t st) {
+  const int dp_blocks = dprobs ? (gt.total_rows + 255) / 256 : 0;
+  const int cs_bx = cs_out ? (int)((width + 255) / 256) : 0;
+  const int64_t grid = (int64_t)dp_blocks + (int64_t)cs_bx * gt.num_groups;
+  if (grid == 0) return;
+  if (gt.dev)
+    hipLaunchKernelGGL(reduce_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st, dp_part, n_ct, gt.total_rows,
+                       dprobs, dp_blocks, cs_part, gt, width, cs_out, cs_bx);
+  else
+    hipLaunchKernelGGL(reduce_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, dp_part, n_ct, gt.total_rows,
+                       dprobs, dp_blocks, cs_part, gt, width, cs_out, cs_bx);
+}
 void launch_col_sum_reduce(const GroupTable& gt, int64_t width, const float* part, float* out, hipStream_t st) {
-  const dim3 grid((unsigned)((width + 255) / 256), (unsigned)gt.num_groups);
-  if (gt.dev) hipLaunchKernelGGL(col_sum_reduce_kernel<true>, grid, dim3(256), 0, st, part, gt, width, out);
-  else hipLaunchKernelGGL(col_sum_reduce_kernel<false>, grid, dim3(256), 0, st, part, gt, width, out);
+  launch_reduce(gt, nullptr, 0, nullptr, part, width, out, st);
 }
 
 ActArgs to_args(const ActHost& a) { return ActArgs{a.kind, a.s, a.inv_s, a.limit, a.alpha, a.beta}; }
@@ -1302,10 +1320,7 @@ hipError_t launch_act_bwd(const ActHost& act, int fmt, const GroupTable& gt, int
     case MGS_ACT_GLU: bwd_dispatch_fmt<MGS_ACT_GLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
     default: bwd_dispatch_fmt<MGS_ACT_CLAMPED_SWIGLU>(fmt, grid, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, part, cs_part, actq, n_ct); break;
   }
-  if (dprobs && gt.total_rows > 0)
-    hipLaunchKernelGGL(dprobs_reduce_kernel, dim3((unsigned)((gt.total_rows + 255) / 256)), dim3(256), 0, st,
-                       part, n_ct, gt.total_rows, gt.dev, dprobs);
-  if (dx_col_sum) launch_col_sum_reduce(gt, width_in, cs_part, dx_col_sum, st);
+  launch_reduce(gt, part, n_ct, gt.total_rows > 0 ? dprobs : nullptr, cs_part, width_in, dx_col_sum, st);
   return hipGetLastError();
 }
 
