@@ -130,7 +130,8 @@ typedef struct {
  *   dev_table  DEVICE buffer of mgs_groups_table_bytes() bytes holding the offsets, written on the
  *              stream by mgs_groups_update (call it after every change of the split sizes; kernels of
  *              the calls enqueued after it read them).  Calls sharing a dev_table must not overlap.
- * MXFP8 only: NVFP4 tensors, the FP32-input forward and mgs_grouped_col_sum return MGS_ERR_UNSUPPORTED. */
+ * Every call takes device-resident split sizes, for both formats; NVFP4's per-group amax and S_dec
+ * are taken over the rows of each group as the device table holds them at the time of the call. */
 typedef struct {
   int32_t num_groups;         /* 1 .. MGS_MAX_GROUPS */
   const int64_t* split_sizes; /* host array [num_groups], each >= 0; NULL: device-resident (above) */

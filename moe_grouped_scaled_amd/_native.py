@@ -110,7 +110,7 @@ def abi_version():
 
 
 class DeviceGroups:
-    """Device-resident split sizes (graph-safe calls; MXFP8).  `splits` is a device int64 tensor the
+    """Device-resident split sizes (graph-safe calls).  `splits` is a device int64 tensor the
     caller fills (copy_ works under graph replay); update() enqueues the offsets computation on the
     stream, and every call given this object afterwards reads them.  Layouts are strided for the row
     capacity `max_rows`; `status` (device int32) turns 1 when the splits are invalid (negative, or

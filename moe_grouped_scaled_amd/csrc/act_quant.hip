@@ -992,6 +992,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ d
 constexpr int CS_COLS = 128;
 constexpr int CS_UNROLL = 8;
 
+template <bool DEV>
 __global__ __launch_bounds__(256) void col_sum_kernel(GroupTable gt, int64_t width,
                                                       const uint16_t* __restrict__ x,
                                                       float* __restrict__ out) {
@@ -1003,7 +1004,14 @@ __global__ __launch_bounds__(256) void col_sum_kernel(GroupTable gt, int64_t wid
   const int64_t col = (int64_t)blockIdx.x * CS_COLS + 8 * cc;
   const bool valid = col < width;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int r_begin = gt.row_off[g], r_end = gt.row_off[g + 1];
+  int r_begin, r_end;
+  if constexpr (DEV) {
+    r_begin = gt.dev->row_off[g];
+    r_end = gt.dev->row_off[g + 1];
+  } else {
+    r_begin = gt.row_off[g];
+    r_end = gt.row_off[g + 1];
+  }
   const uint32_t ld2 = (uint32_t)width * 2u;
   const uint32_t vo = (uint32_t)slot * ld2 + (uint32_t)col * 2u;
   for (int rb = r_begin; rb < r_end; rb += 16 * CS_UNROLL) {
@@ -1041,7 +1049,7 @@ __global__ __launch_bounds__(256) void col_sum_kernel(GroupTable gt, int64_t wid
 // per wave.  BWD: the value is dx = (da/dg * dy) * p (both halves for gated kinds); else y = a * p.
 // With `rht` (bit 16 set) the pass also takes the maximum of the Hadamard-transformed columns (the
 // columnwise copy's values) into amax[E + g].
-template <int KIND, bool BWD, bool XF32>
+template <int KIND, bool BWD, bool XF32, bool DEV>
 __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable gt,
                                                          const void* __restrict__ xp,
                                                          const uint16_t* __restrict__ dy,
@@ -1050,7 +1058,7 @@ __global__ __launch_bounds__(256) void group_amax_kernel(ActArgs aa, GroupTable 
                                                          int cpw, float* __restrict__ amax, uint32_t rht) {
   constexpr bool GATED = is_gated<KIND>();
   __shared__ float wmax[2][4];
-  const BlockPos bp = block_pos<false>(gt, (n_chunks + cpw - 1) / cpw);
+  const BlockPos bp = block_pos<DEV>(gt, (n_chunks + cpw - 1) / cpw);
   if (!bp.ok) return;
   const PanelInfo& pi = bp.pi;
   const int lr0 = bp.lr0;
@@ -1155,12 +1163,20 @@ void launch_group_amax(hipStream_t st, const ActArgs& aa, const GroupTable& gt, 
   const int n_chunks = (int)((wa + BLOCK_COLS - 1) / BLOCK_COLS);
   const int cpw = amax_cpw(gt, n_chunks);
   const dim3 grid((unsigned)((int64_t)(gt.num_panels / 4) * ((n_chunks + cpw - 1) / cpw)));
-  if (!BWD && x_f32)
-    hipLaunchKernelGGL((group_amax_kernel<KIND, false, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
+  if (gt.dev) {
+    if (!BWD && x_f32)
+      hipLaunchKernelGGL((group_amax_kernel<KIND, false, true, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
+                         width_in, wa, n_chunks, cpw, amax, rht);
+    else
+      hipLaunchKernelGGL((group_amax_kernel<KIND, BWD, false, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
+                         width_in, wa, n_chunks, cpw, amax, rht);
+  } else if (!BWD && x_f32) {
+    hipLaunchKernelGGL((group_amax_kernel<KIND, false, true, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
                        width_in, wa, n_chunks, cpw, amax, rht);
-  else
-    hipLaunchKernelGGL((group_amax_kernel<KIND, BWD, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
+  } else {
+    hipLaunchKernelGGL((group_amax_kernel<KIND, BWD, false, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs,
                        width_in, wa, n_chunks, cpw, amax, rht);
+  }
 }
 
 // Zeroes `amax` (E entries, 2E with rht) and takes the group maxima into it.
@@ -1186,9 +1202,11 @@ void fwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, con
                       const void* x, const float* probs, int64_t width_in, const QOut& out,
                       float* cs_part, int n_ct, uint16_t* x_copy) {
   if (gt.dev) {
-    // device-resident split sizes: MXFP8 from a BF16 input only (checked by the caller)
-    if constexpr (!XF32)
-      hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8, false, true>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+    // device-resident split sizes: the offsets come from the device table
+    if (fmt == MGS_FMT_MXFP8)
+      hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8, XF32, true>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
+    else
+      hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_NVFP4, XF32, true>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
   } else if (fmt == MGS_FMT_MXFP8) {
     hipLaunchKernelGGL((act_fwd_kernel<KIND, MGS_FMT_MXFP8, XF32, false>), grid, dim3(256), 0, st, aa, gt, x, probs, width_in, out, cs_part, n_ct, x_copy);
   } else {
@@ -1209,8 +1227,10 @@ void bwd_dispatch_fmt(int fmt, dim3 grid, hipStream_t st, const ActArgs& aa, con
                       const uint16_t* x, const uint16_t* dy, const float* probs, int64_t width_in,
                       int64_t wa, uint16_t* dx, const QOut& dxq, float* dp_part, float* cs_part,
                       const QOut& actq, int n_ct) {
-  if (gt.dev)  // device-resident split sizes: MXFP8 only (checked by the caller)
+  if (gt.dev && fmt == MGS_FMT_MXFP8)  // device-resident split sizes
     hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
+  else if (gt.dev)
+    hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_NVFP4, true>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
   else if (fmt == MGS_FMT_MXFP8)
     hipLaunchKernelGGL((act_bwd_kernel<KIND, MGS_FMT_MXFP8, false>), grid, dim3(256), 0, st, aa, gt, x, dy, probs, width_in, wa, dx, dxq, dp_part, cs_part, actq, n_ct);
   else
@@ -1390,7 +1410,8 @@ hipError_t launch_groups_update(int num_groups, const int64_t* splits, int64_t m
 hipError_t launch_col_sum(const GroupTable& gt, int64_t width, const uint16_t* x, float* out,
                           hipStream_t st) {
   const dim3 grid((unsigned)((width + CS_COLS - 1) / CS_COLS), (unsigned)gt.num_groups);
-  hipLaunchKernelGGL(col_sum_kernel, grid, dim3(256), 0, st, gt, width, x, out);
+  if (gt.dev) hipLaunchKernelGGL(col_sum_kernel<true>, grid, dim3(256), 0, st, gt, width, x, out);
+  else hipLaunchKernelGGL(col_sum_kernel<false>, grid, dim3(256), 0, st, gt, width, x, out);
   return hipGetLastError();
 }
 

@@ -822,8 +822,14 @@ void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NV_STAGE];
   __shared__ __attribute__((aligned(16))) uint2 bias_lds[BN2 / 4];
   int tile;
-  if (!schedule_tile(tt, blockIdx.x, &tile)) return;
-  const TileJob j = make_job<BM2, BN2>(ga, tt, tile);
+  TileJob j;
+  if (tt.dev) {
+    if (!schedule_tile(*tt.dev, blockIdx.x, &tile)) return;
+    j = make_job<BM2, BN2>(ga, *tt.dev, tile);
+  } else {
+    if (!schedule_tile(tt, blockIdx.x, &tile)) return;
+    j = make_job<BM2, BN2>(ga, tt, tile);
+  }
   if (j.k == 0) {
     write_zero_tile<BM2, BN2>(j, ga);
     return;
@@ -1162,6 +1168,8 @@ hipError_t launch_gemm(const GemmArgs& ga, const GroupTable& gt, hipStream_t st,
     const int64_t grid = capacity_grid(ga, gt, BM2, BN2);
     if (ga.fmt == MGS_FMT_MXFP8)
       hipLaunchKernelGGL(gemm_mxfp8_256_kernel, dim3((unsigned)grid), dim3(256), 0, st, ga, tt);
+    else
+      hipLaunchKernelGGL(gemm_nvfp4_256_kernel, dim3((unsigned)grid), dim3(256), 0, st, ga, tt);
     return hipGetLastError();
   }
   if (ga.fmt == MGS_FMT_MXFP8) {

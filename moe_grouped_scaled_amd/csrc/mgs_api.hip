@@ -170,9 +170,6 @@ mgs::GemmTable* dev_gemm_table(const mgs_groups* groups) {
                                                                  kDevGemmTableOffset);
 }
 
-int unsupported_with_device_splits(const char* what) {
-  return fail(MGS_ERR_UNSUPPORTED, "%s is not available with device-resident split sizes (MXFP8 only)", what);
-}
 
 int hip_status(hipError_t e) {
   if (e != hipSuccess) return fail(MGS_ERR_HIP, "HIP launch error: %s", hipGetErrorString(e));
@@ -218,7 +215,6 @@ int act_bwd_impl(const mgs_act_params* act, int32_t fmt, const mgs_groups* group
   mgs::GroupTable gt;
   int64_t rows = 0;
   if ((rc = build_groups(groups, &gt, &rows))) return rc;
-  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
@@ -319,7 +315,6 @@ int mgs_grouped_scaled_act_fwd(const mgs_act_params* act, int32_t fmt, const mgs
   mgs::GroupTable gt;
   int64_t rows = 0;
   if ((rc = build_groups(groups, &gt, &rows))) return rc;
-  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
@@ -347,7 +342,6 @@ int mgs_grouped_scaled_act_fwd_f32(const mgs_act_params* act, int32_t fmt, const
   mgs::GroupTable gt;
   int64_t rows = 0;
   if ((rc = build_groups(groups, &gt, &rows))) return rc;
-  if (device_splits(gt)) return unsupported_with_device_splits("the FP32-input forward");
   if (is_gated(ah.kind) && width_in % 2 != 0) return fail(MGS_ERR_SHAPE, "gated width_in must be even");
   const int64_t wa = is_gated(ah.kind) ? width_in / 2 : width_in;
   if ((rc = check_width(wa, is_gated(ah.kind) ? "width_in / 2" : "width_in"))) return rc;
@@ -414,7 +408,6 @@ int mgs_grouped_mx_quantize(int32_t fmt, const mgs_groups* groups, int64_t width
   int64_t rows = 0;
   int rc = build_groups(groups, &gt, &rows);
   if (rc) return rc;
-  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if ((rc = check_width(width, "width"))) return rc;
   if ((rc = check_extent(gt, width, "width"))) return rc;
   if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
@@ -465,7 +458,6 @@ int mgs_grouped_gemm_mx(int32_t mode, int32_t fmt, const mgs_groups* groups, int
   int64_t rows = 0;
   int rc = build_groups(groups, &gt, &rows);
   if (rc) return rc;
-  if (device_splits(gt) && fmt != MGS_FMT_MXFP8) return unsupported_with_device_splits("NVFP4");
   if (!a || !a->data || !a->scales) return fail(MGS_ERR_INVALID_ARG, "operand A (data, scales) is NULL");
   if (!b || !b->data || !b->scales) return fail(MGS_ERR_INVALID_ARG, "operand B (data, scales) is NULL");
   if (fmt == MGS_FMT_NVFP4 && (!a->group_scale || !b->group_scale))
@@ -558,7 +550,6 @@ int mgs_grouped_col_sum(const mgs_groups* groups, int64_t width, const void* x_b
   int64_t rows = 0;
   int rc = build_groups(groups, &gt, &rows);
   if (rc) return rc;
-  if (device_splits(gt)) return unsupported_with_device_splits("mgs_grouped_col_sum");
   if (width <= 0 || width % 8 != 0) return fail(MGS_ERR_SHAPE, "width must be a positive multiple of 8");
   if (!x_bf16 && rows > 0) return fail(MGS_ERR_INVALID_ARG, "x_bf16 is NULL");
   if (!out) return fail(MGS_ERR_INVALID_ARG, "out is NULL");

@@ -103,13 +103,12 @@ class ExpertMLP:
 
     # ------------------------------------------------------------------ forward
     def forward(self, x1, probs, splits):
-        """`splits`: host split sizes, or an N.DeviceGroups (device-resident split sizes, MXFP8): then
+        """`splits`: host split sizes, or an N.DeviceGroups (device-resident split sizes): then
         x1 and probs have the capacity's rows, only the first sum(splits) of which are used, and the
         step enqueues the offsets computation first, so that a captured graph of the step follows the
         split sizes held in the device tensor at each replay."""
         e, h, f, f_in = self.e, self.h, self.f, self.f_in
         if isinstance(splits, N.DeviceGroups):
-            assert self.fmt == "mxfp8" and not self.fc1_fp32_act, "device-resident split sizes: MXFP8, BF16 FC1 output"
             splits.update()
         m = x1.shape[0]
         fmt = self.fmt

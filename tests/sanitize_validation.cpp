@@ -159,8 +159,8 @@ int main(int argc, char** argv) {
   mgs_groups gbig = host_groups(big1);
   EXPECT(mgs_grouped_scaled_act_fwd(&srelu, MGS_FMT_MXFP8, &gbig, 32768, FAKE, F, &q, nullptr, nullptr, nullptr),
          MGS_ERR_SHAPE);
-  EXPECT(mgs_grouped_scaled_act_fwd(&srelu, MGS_FMT_NVFP4, &gd, 96, FAKE, F, &q, nullptr, F, nullptr),
-         MGS_ERR_UNSUPPORTED);
+  EXPECT(mgs_grouped_scaled_act_fwd(&srelu, MGS_FMT_NVFP4, &gd, 96, FAKE, F, &q, nullptr, nullptr, nullptr),
+         MGS_ERR_INVALID_ARG);
   mgs_qbuf rht_row{FAKE, FAKE, F, (1u << 16) | 0x1234u};
   EXPECT(mgs_grouped_scaled_act_fwd(&srelu, MGS_FMT_NVFP4, &g4, 64, FAKE, F, &rht_row, nullptr, F, nullptr),
          MGS_ERR_UNSUPPORTED);
@@ -170,9 +170,9 @@ int main(int argc, char** argv) {
   EXPECT(mgs_grouped_scaled_act_fwd_f32(&srelu, MGS_FMT_MXFP8, &g4, 64, F, F, nullptr, nullptr, nullptr, nullptr,
                                         nullptr),
          MGS_ERR_INVALID_ARG);
-  EXPECT(mgs_grouped_scaled_act_fwd_f32(&srelu, MGS_FMT_MXFP8, &gd, 96, F, F, &q, nullptr, nullptr, nullptr,
+  EXPECT(mgs_grouped_scaled_act_fwd_f32(&srelu, MGS_FMT_MXFP8, &gd, 48, F, F, &q, nullptr, nullptr, nullptr,
                                         nullptr),
-         MGS_ERR_UNSUPPORTED);
+         MGS_ERR_SHAPE);
 
   // ---- backward
   EXPECT(mgs_grouped_scaled_act_bwd(&srelu, MGS_FMT_MXFP8, &g4, 64, FAKE, nullptr, F, FAKE, nullptr, nullptr,
@@ -206,9 +206,9 @@ int main(int argc, char** argv) {
   EXPECT(mgs_grouped_scaled_act_bwd_noalloc(&srelu, MGS_FMT_MXFP8, &g4, 64, FAKE, nullptr, F, FAKE, nullptr,
                                             nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr),
          MGS_ERR_INVALID_ARG);
-  EXPECT(mgs_grouped_scaled_act_bwd(&srelu, MGS_FMT_NVFP4, &gd, 96, FAKE, FAKE, F, FAKE, nullptr, nullptr,
+  EXPECT(mgs_grouped_scaled_act_bwd(&srelu, MGS_FMT_NVFP4, &gd, 96, FAKE, FAKE, F, nullptr, &q, nullptr,
                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr),
-         MGS_ERR_UNSUPPORTED);
+         MGS_ERR_INVALID_ARG);
 
   // ---- quantize and column sums
   EXPECT(mgs_grouped_mx_quantize(MGS_FMT_MXFP8, &g4, 64, FAKE, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
@@ -225,7 +225,7 @@ int main(int argc, char** argv) {
   EXPECT(mgs_grouped_mx_quantize_workspace_bytes(&g4, 40), MGS_ERR_SHAPE);
   EXPECT(mgs_grouped_col_sum(&g4, 12, FAKE, F, nullptr), MGS_ERR_SHAPE);
   EXPECT(mgs_grouped_col_sum(&g4, 64, FAKE, nullptr, nullptr), MGS_ERR_INVALID_ARG);
-  EXPECT(mgs_grouped_col_sum(&gd, 64, FAKE, F, nullptr), MGS_ERR_UNSUPPORTED);
+  EXPECT(mgs_grouped_col_sum(&gd, 64, FAKE, nullptr, nullptr), MGS_ERR_INVALID_ARG);
 
   // ---- GEMMs
   float cbuf[1];
@@ -260,9 +260,9 @@ int main(int argc, char** argv) {
   EXPECT(mgs_grouped_gemm_mx(MGS_GEMM_FPROP, MGS_FMT_MXFP8, &gd, 299, 64, 64, &q, &q, cbuf, MGS_DTYPE_F32,
                              nullptr, 0, nullptr),
          MGS_ERR_SHAPE);
-  EXPECT(mgs_grouped_gemm_mx(MGS_GEMM_FPROP, MGS_FMT_NVFP4, &gd, 300, 64, 64, &q, &q, cbuf, MGS_DTYPE_F32,
+  EXPECT(mgs_grouped_gemm_mx(MGS_GEMM_FPROP, MGS_FMT_NVFP4, &gd, 300, 64, 64, &q_nogs, &q, cbuf, MGS_DTYPE_F32,
                              nullptr, 0, nullptr),
-         MGS_ERR_UNSUPPORTED);
+         MGS_ERR_INVALID_ARG);
   EXPECT(mgs_grouped_gemm_mx_fprop_act(&g4, 197, 64, 64, &q, &q, cbuf, nullptr, &swiglu, F, MGS_DTYPE_BF16, &q,
                                        nullptr),
          MGS_ERR_UNSUPPORTED);

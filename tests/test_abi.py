@@ -245,8 +245,8 @@ def _fake_device_groups(e, cap):
 def test_device_resident_splits_validation_and_capacity_layouts():
     """With device-resident split sizes the layouts are those of the row capacity: rowwise copies
     hold max_rows rows, columnwise ones the padded bound 128 (ceil(max_rows / 128) + E) rows; the
-    GEMMs take m (k for WGRAD) = max_rows; NVFP4, the FP32-input forward and the standalone column
-    sum are refused; the offsets update needs device split sizes and a device table."""
+    GEMMs take m (k for WGRAD) = max_rows; the calls validate their other arguments as with host
+    split sizes; the offsets update needs device split sizes and a device table."""
     from moe_grouped_scaled_amd import _native as N
     assert N.LIB.mgs_groups_table_bytes() >= 2 * (2 * 65 + 4) * 4
     e, cap, w = 4, 300, 96
@@ -258,12 +258,12 @@ def test_device_resident_splits_validation_and_capacity_layouts():
         N.act_bwd_workspace_bytes(N.act_params("srelu"), [cap - 3 * 64 - 1, 64, 64, 64], w)
     q = _FakeQ().q
     act = N.act_params("srelu")
-    _expect(-3, N.grouped_scaled_act_fwd, act, "nvfp4", dg, w, FAKE, FAKE, out_row=q, group_amax=FAKE,
-            stream=0, match="device-resident")
-    _expect(-3, N.grouped_scaled_act_fwd_f32, act, "mxfp8", dg, w, FAKE, FAKE, out_row=q, stream=0,
-            match="FP32-input")
-    _expect(-3, N.grouped_col_sum, dg, w, FAKE, FAKE, stream=0, match="device-resident")
-    _expect(-3, N.grouped_mx_quantize, "nvfp4", dg, w, FAKE, out_row=q, group_amax=FAKE, stream=0)
+    assert N.qtensor_nbytes("nvfp4", True, dg, w, "data") == 128 * (-(-cap // 128) + e) * w // 2
+    _expect(-1, N.grouped_scaled_act_fwd, act, "nvfp4", dg, w, FAKE, FAKE, out_row=q, stream=0,
+            match="group_amax")
+    _expect(-1, N.grouped_scaled_act_fwd_f32, act, "mxfp8", dg, w, FAKE, FAKE, stream=0, match="no output")
+    _expect(-2, N.grouped_col_sum, dg, 12, FAKE, FAKE, stream=0, match="multiple of 8")
+    _expect(-1, N.grouped_mx_quantize, "nvfp4", dg, w, FAKE, out_row=q, stream=0, match="group_amax")
     import torch
     c = torch.empty(1, dtype=torch.float32)
     _expect(-2, N.grouped_gemm_mx, "fprop", "mxfp8", dg, cap - 1, 64, 64, q, q, c, stream=0, match="split sum")

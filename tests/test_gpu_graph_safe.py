@@ -9,12 +9,15 @@ gradients) is replayed over different routings.
 
 Checks:
   * the step with device-resident split sizes equals the step with host split sizes bit for bit on
-    every output row in use (the same kernels and arithmetic; only strides and grids differ);
+    every output row in use (the same kernels and arithmetic; only strides and grids differ), for
+    both recipes, the FP32-output forward and Hadamard-transformed NVFP4 copies;
   * one graph captured once and replayed over alternating routings (with eager work and
     synchronizations between replays) gives, at every replay, the eager step's outputs bit for bit,
     and those agree with the oracle step at the same split sizes;
+  * the NVFP4 step captured once follows each replay's routing (its per-group amax included);
   * invalid split sizes (a sum above the capacity, a negative one) set the status word and the calls
-    write nothing.
+    write nothing;
+  * the standalone column sum reads the device offsets.
 """
 
 import numpy as np
@@ -40,17 +43,18 @@ def N():
 
 def _weights(kind, seed=3):
     rng = np.random.default_rng(seed)
-    f_in = 2 * F if kind == "swiglu" else F
+    f_in = 2 * F if kind in ("swiglu", "clamped_swiglu", "glu") else F
     return dict(w1=workloads.normal_bf16(rng, (E, f_in, H), 0.05), w2=workloads.normal_bf16(rng, (E, H, F), 0.05),
                 b1=workloads.normal_bf16(rng, (E, f_in), 0.05), b2=workloads.normal_bf16(rng, (E, H), 0.05),
                 x1=workloads.normal_bf16(rng, (CAP, H)), p=workloads.uniform_f32(rng, CAP),
                 dy2=workloads.normal_bf16(rng, (CAP, H)))
 
 
-def _mlp(kind, d):
+def _mlp(kind, d, fmt="mxfp8", fp32_act=False, rht=None):
     from moe_grouped_scaled_amd.expert_mlp import ExpertMLP
-    return ExpertMLP(kind, "mxfp8", to_dev_bf16(d["w1"]), to_dev_bf16(d["w2"]), to_dev_bf16(d["b1"]),
-                     to_dev_bf16(d["b2"]), recompute=True, delay_wgrad=True, fuse_fc1_act="auto")
+    return ExpertMLP(kind, fmt, to_dev_bf16(d["w1"]), to_dev_bf16(d["w2"]), to_dev_bf16(d["b1"]),
+                     to_dev_bf16(d["b2"]), recompute=True, delay_wgrad=True, fuse_fc1_act="auto",
+                     fc1_fp32_act=fp32_act, rht_signs=rht)
 
 
 def _step(mlp, x1, p, dy2, splits):
@@ -66,18 +70,25 @@ def _host(g, m):
             "dw1": f32(g["dw1"]), "dw2": f32(g["dw2"]), "db1": f32(g["db1"]), "db2": f32(g["db2"])}
 
 
-@pytest.mark.parametrize("kind", ["srelu", "swiglu"])
-def test_device_splits_step_equals_host_splits_step(N, kind):
+CASES = [("srelu", "mxfp8", False, None), ("swiglu", "mxfp8", False, None), ("srelu", "mxfp8", True, None),
+         ("srelu", "nvfp4", False, None), ("tanh_srelu", "nvfp4", True, None), ("glu", "nvfp4", False, 0x6B35)]
+
+
+@pytest.mark.parametrize("kind,fmt,fp32_act,rht", CASES)
+def test_device_splits_step_equals_host_splits_step(N, kind, fmt, fp32_act, rht):
+    """Both recipes, the FP32-output forward and the Hadamard-transformed NVFP4 copies: the step with
+    device-resident split sizes writes the host-split step's bits on every row in use."""
     import torch
     d = _weights(kind)
     x1, p, dy2 = to_dev_bf16(d["x1"]), to_dev(d["p"]), to_dev_bf16(d["dy2"])
     dg = N.DeviceGroups(E, CAP)
     for splits in ROUTINGS:
         m = int(sum(splits))
-        print("case:", kind, "splits", splits, flush=True)
-        ref = _host(_step(_mlp(kind, d), x1[:m].contiguous(), p[:m].contiguous(), dy2[:m].contiguous(), splits), m)
+        print("case:", kind, fmt, "fp32_act" if fp32_act else "", "rht" if rht else "", "splits", splits, flush=True)
+        ref = _host(_step(_mlp(kind, d, fmt, fp32_act, rht), x1[:m].contiguous(), p[:m].contiguous(),
+                          dy2[:m].contiguous(), splits), m)
         dg.splits.copy_(torch.tensor(splits, dtype=torch.int64))
-        got = _host(_step(_mlp(kind, d), x1, p, dy2, dg), m)
+        got = _host(_step(_mlp(kind, d, fmt, fp32_act, rht), x1, p, dy2, dg), m)
         torch.cuda.synchronize()
         assert int(dg.status.item()) == 0
         for k in ref:
@@ -165,16 +176,53 @@ def test_invalid_device_splits_write_nothing(N):
         assert bool((c == 3.0).all())
 
 
-def test_device_splits_reject_what_they_do_not_support(N):
+def test_nvfp4_graph_replayed_over_routings(N):
+    """The NVFP4 step (per-group amax and S_dec taken over each replay's rows) captured once and
+    replayed over routings A, B, A, C: every replay equals the eager host-split step bit for bit."""
     import torch
+    kind = "srelu"
+    d = _weights(kind)
+    x1, p, dy2 = to_dev_bf16(d["x1"]), to_dev(d["p"]), to_dev_bf16(d["dy2"])
     dg = N.DeviceGroups(E, CAP)
-    x = torch.zeros(CAP, H, device="cuda").to(torch.bfloat16)
-    q = N.QTensor("mxfp8", False, dg, H)
-    with pytest.raises(N.MgsError) as ei:
-        N.grouped_mx_quantize("nvfp4", dg, H, x, N.QTensor("nvfp4", False, dg, H),
-                              group_amax=torch.zeros(E, device="cuda"))
-    assert ei.value.code == -3
-    with pytest.raises(N.MgsError) as ei:
-        N.grouped_col_sum(dg, H, x, torch.zeros(E, H, device="cuda"))
-    assert ei.value.code == -3
-    del q
+    mlp = _mlp(kind, d, "nvfp4")
+    dg.splits.copy_(torch.tensor(ROUTINGS[0], dtype=torch.int64))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            _step(mlp, x1, p, dy2, dg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = _step(mlp, x1, p, dy2, dg)
+    for it, splits in enumerate([ROUTINGS[0], ROUTINGS[1], ROUTINGS[0], ROUTINGS[2]]):
+        m = int(sum(splits))
+        print("nvfp4 replay", it, "splits", splits, flush=True)
+        dg.splits.copy_(torch.tensor(splits, dtype=torch.int64))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _host(out, m)
+        assert int(dg.status.item()) == 0
+        ref = _host(_step(_mlp(kind, d, "nvfp4"), x1[:m].contiguous(), p[:m].contiguous(), dy2[:m].contiguous(),
+                          splits), m)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), (it, splits, k)
+
+
+def test_col_sum_with_device_splits(N):
+    """The standalone per-group column sum reads the device offsets: equal to the host-split call."""
+    import torch
+    x = (torch.randn(CAP, H, device="cuda")).to(torch.bfloat16)
+    dg = N.DeviceGroups(E, CAP)
+    for splits in ROUTINGS:
+        m = int(sum(splits))
+        dg.splits.copy_(torch.tensor(splits, dtype=torch.int64))
+        dg.update()
+        got = torch.full((E, H), 7.0, device="cuda")
+        N.grouped_col_sum(dg, H, x, got)
+        ref = torch.empty(E, H, device="cuda")
+        N.grouped_col_sum(splits, H, x[:m].contiguous(), ref)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), splits
