@@ -346,6 +346,10 @@ def main():
                          "(SReLU, sigmoid)")
     ap.add_argument("--rht", type=lambda v: int(v, 0), default=None,
                     help="NVFP4: Hadamard-transform the weight-gradient operands with this 16-bit sign mask")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph with device-resident split "
+                         "sizes and replayed (the uniform routing, then alternating it with a Zipf(1.2) "
+                         "routing of the same tokens); reported under \"graph_replay\"")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -504,9 +508,58 @@ def main():
         "kernels": kernels,
         "recompute_memory_drop_bytes": {"measured": held[False] - held[True], "closed_form": drop_closed},
     }
+    if args.graph:
+        line["graph_replay"] = graph_replay(args, N, ExpertMLP, (x1, w1, w2, b1, b2, dy2, p), splits, ms_per_step)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.act, args.fmt)
     print(json.dumps(line))
+
+
+def graph_replay(args, N, ExpertMLP, tensors, splits, eager_ms):
+    """The step captured once in a HIP graph with device-resident split sizes (capacity = the tokens of
+    the step), then replayed: `steps` replays of the uniform routing, and `steps` replays alternating
+    it with a Zipf(1.2) routing of the same tokens (the split tensor is rewritten between replays)."""
+    import torch
+    import workloads
+    x1, w1, w2, b1, b2, dy2, p = tensors
+    e, m = len(splits), int(sum(splits))
+    zipf = list(map(int, workloads.zipf_split(np.random.default_rng(7), m, e, 1.2, 0)))
+    dg = N.DeviceGroups(e, m)
+    mlp = ExpertMLP(args.act, args.fmt, w1, w2, b1, b2, recompute=True, delay_wgrad=True, s=2.0,
+                    fc1_fp32_act=args.fc1_fp32_act, fuse_fc1_act=FC1_ACT[args.fc1_act], rht_signs=args.rht)
+    uniform = torch.tensor(splits, dtype=torch.int64, device="cuda")
+    skewed = torch.tensor(zipf, dtype=torch.int64, device="cuda")
+
+    def step():
+        mlp.forward(x1, p, dg)
+        mlp.backward(dy2)
+        mlp.backward_dw()
+
+    dg.splits.copy_(uniform)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(args.warmup, 2)):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    out = {"capacity_rows": m, "zipf_splits": zipf}
+    for name, seq in (("uniform", [uniform] * args.steps), ("alternating", [uniform, skewed] * (args.steps // 2))):
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for sp in seq:
+            dg.splits.copy_(sp)
+            graph.replay()
+        torch.cuda.synchronize()
+        out["ms_per_step_" + name] = (time.perf_counter() - t0) / len(seq) * 1e3
+    assert int(dg.status.item()) == 0
+    out["eager_ms_per_step"] = eager_ms
+    return out
 
 
 if __name__ == "__main__":
