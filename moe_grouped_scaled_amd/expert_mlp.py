@@ -109,6 +109,9 @@ class ExpertMLP:
         split sizes held in the device tensor at each replay."""
         e, h, f, f_in = self.e, self.h, self.f, self.f_in
         if isinstance(splits, N.DeviceGroups):
+            if x1.shape[0] != splits.max_rows or probs.shape[0] != splits.max_rows:
+                raise ValueError("with device-resident split sizes x1 and probs have the capacity's %d rows "
+                                 "(got %d and %d)" % (splits.max_rows, x1.shape[0], probs.shape[0]))
             splits.update()
         m = x1.shape[0]
         fmt = self.fmt

@@ -277,3 +277,16 @@ def test_device_resident_splits_validation_and_capacity_layouts():
     assert "split_sizes_dev" in N.last_error()
     g.struct.dev_table = None
     assert N.LIB.mgs_groups_update(g.ref, FAKE, None, None) == -1
+
+
+def test_expert_mlp_device_splits_need_capacity_rows():
+    """ExpertMLP with device-resident split sizes takes inputs of the capacity's rows and says so
+    before any launch."""
+    import torch
+    from moe_grouped_scaled_amd.expert_mlp import ExpertMLP
+    e, h, f = 4, 64, 64
+    w1, w2 = torch.zeros(e, f, h, dtype=torch.bfloat16), torch.zeros(e, h, f, dtype=torch.bfloat16)
+    mlp = ExpertMLP("srelu", "mxfp8", w1, w2)
+    dg = _fake_device_groups(e, 256)
+    with pytest.raises(ValueError, match="capacity"):
+        mlp.forward(torch.zeros(200, h, dtype=torch.bfloat16), torch.zeros(200), dg)
