@@ -716,28 +716,18 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
 // ------------------------------------------------------------------------------------ NVFP4 path
 
 // eight E2M1 codes (a dword, element 2i in the low nibble of byte i) times an exact FP16 block
-// scale -> eight FP16 values.  The E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} are FP16 numbers whose
-// low byte is zero; their high bytes sit in a two-dword table indexed with V_PERM_B32 (byte selector
-// 0..3 -> second operand, 4..7 -> first operand, 12 -> 0x00).  The sign (bit 3 of the nibble) is
-// OR-ed into bit 7 of the high byte.  The product with the block scale is exact: at most 6
-// significant bits, magnitudes in [2^-10, 2688], all normal FP16 numbers.
+// scale -> eight FP16 values.  V_CVT_SCALEF32_PK_F16_FP4 converts the two codes of one byte (low
+// nibble first) to FP16, times the power of two of its FP32 scale operand (measured on the device:
+// exact for all 256 bytes and every byte select); with scale 1 the values are the E2M1 values.  The
+// product with the block scale is exact: at most 6 significant bits, magnitudes in [2^-10, 2688], all
+// normal FP16 numbers.
 __device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, v2h scale) {
-  constexpr uint32_t LUT_LO = 0x3E3C3800u;  // codes 0..3: 0, 0.5, 1, 1.5
-  constexpr uint32_t LUT_HI = 0x46444240u;  // codes 4..7: 2, 3, 4, 6
-  const uint32_t a = __builtin_amdgcn_perm(LUT_HI, LUT_LO, w & 0x07070707u) | ((w << 4) & 0x80808080u);
-  const uint32_t b = __builtin_amdgcn_perm(LUT_HI, LUT_LO, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
-  // element 2k = byte k of a, element 2k+1 = byte k of b, each as the high byte of an FP16
-  uint32_t h[4];
-  h[0] = __builtin_amdgcn_perm(b, a, 0x040C000Cu);
-  h[1] = __builtin_amdgcn_perm(b, a, 0x050C010Cu);
-  h[2] = __builtin_amdgcn_perm(b, a, 0x060C020Cu);
-  h[3] = __builtin_amdgcn_perm(b, a, 0x070C030Cu);
-  uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[0]) * scale);
-  r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[1]) * scale);
-  r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[2]) * scale);
-  r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[3]) * scale);
-  return r;
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * scale;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * scale;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * scale;
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * scale;
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
 // ------------------------------------------------------------------------------------ NVFP4, large tile
