@@ -319,8 +319,10 @@ __device__ __forceinline__ bool schedule_tile(const Table& tt, int b, int* tile)
 // Scaled FP8 MFMA with the accumulator pinned to AGPRs.  Written as inline assembly because the
 // register allocator otherwise keeps part of the 256 accumulators of a wave in VGPRs and spills the
 // fragments.  The compiler does not see these as MFMAs, so code around them supplies the wait states
-// it would insert: mfma_valu_gap() after VALU writes of fragments that feed an MFMA, and
-// mfma_drain() before VALU reads the accumulators.
+// it would insert: mfma_valu_gap() after VALU writes of operands (the masking of a partial K step;
+// the values are pinned ahead of it so the compiler cannot sink the masking past it), and
+// mfma_drain() before anything reads the accumulators.  tests/test_mfma_hazard.py checks the
+// built code for both kinds of hazard.
 __device__ __forceinline__ void mfma_scale_fp8(v4f& acc, const v8i& b, const v8i& a, int sb, int sa) {
   asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                : "+a"(acc)
@@ -665,9 +667,14 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
     }
 #pragma unroll
     for (int fm = 0; fm < 8; ++fm) {
-      const v8i afr = join(alo, ahi);
+      v8i afr = join(alo, ahi);
       const int csa = csn;
       if (tail) {
+        // the masked fragments are final before the wait states (the compiler would otherwise be
+        // free to sink some of the masking past them, right up to the MFMA)
+        asm volatile("" : "+v"(afr));
+        if (fm == 0)
+          for (int f = 0; f < 8; ++f) asm volatile("" : "+v"(bfr[f]));
         __builtin_amdgcn_sched_barrier(0);
         mfma_valu_gap();
         __builtin_amdgcn_sched_barrier(0);
@@ -688,6 +695,13 @@ void gemm_mxfp8_256_kernel(GemmArgs ga, GemmTable tt) {
           if (fn == 2) csn = psa[(fm + 1) * 64];
         }
       }
+    }
+    // the tile's last MFMAs are waited out here, on each path: the compiler may copy accumulators
+    // out where the full-step loop and the partial last step join, before the drain after it
+    if (next_st < 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_drain();
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -944,6 +958,10 @@ void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
     for (int f = 0; f < 4; ++f) {
       fa[0][f] = dq(ra[f], sa01[f], sa23[f], 0);
       fb[0][f] = dq(rb[f], sb01[f], sb23[f], 0);
+      // computed here, ahead of the first substep's wait states (left free, the compiler sank part
+      // of it to just before the fragment's first MFMA)
+      asm volatile("" : "+v"(fa[0][f].x), "+v"(fa[0][f].y), "+v"(fa[0][f].z), "+v"(fa[0][f].w));
+      asm volatile("" : "+v"(fb[0][f].x), "+v"(fb[0][f].y), "+v"(fb[0][f].z), "+v"(fb[0][f].w));
     }
 #pragma unroll
     for (int sub = 0; sub < BK / 16; ++sub) {
@@ -971,6 +989,12 @@ void gemm_nvfp4_256_kernel(GemmArgs ga, GemmTable tt) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    }
+    // the tile's last MFMAs are waited out on each path (accumulator copies may follow the join)
+    if (next_st < 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_drain();
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
