@@ -80,6 +80,49 @@ def test_integer_codes_unit_scales_exact(N):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("k", [32, 128, 160, 256, 384, 640])
+def test_integer_products_exact_for_every_step_count(N, fmt, k):
+    """Small-integer codes with unit scales give the integer matmul exactly for one to five K steps of
+    128, whole or with a partial last step: the K loop ends on different paths for odd and even step
+    counts and for a partial step, and the accumulators must be complete on each."""
+    import torch
+    rng = np.random.default_rng(k)
+    splits = [3, 0, 130, 61]
+    e, m, n = len(splits), sum(splits), 160
+    if fmt == "mxfp8":
+        vals = np.array([0, 1, 2, 3, 4])
+        enc = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48}           # E4M3 codes of 0..4
+    else:
+        vals = np.array([0, 1, 2, 3, 4, 6])
+        enc = {0: 0, 1: 2, 2: 4, 3: 5, 4: 6, 6: 7}                     # E2M1 codes of 0..6
+    sign = 0x80 if fmt == "mxfp8" else 0x8
+    a_int = rng.choice(vals, (m, k)) * rng.choice([-1, 1], (m, k))
+    b_int = rng.choice(vals, (e, n, k)) * rng.choice([-1, 1], (e, n, k))
+
+    def codes(v):
+        c = np.vectorize(lambda t: enc[abs(int(t))])(v).astype(np.uint8)
+        c = c | np.where(v < 0, sign, 0).astype(np.uint8)
+        return c if fmt == "mxfp8" else codecs.pack_e2m1(c)
+
+    def unit(rows, groups):
+        if fmt == "mxfp8":
+            return {"row_scales": Q.mx_scales_to_kstep(np.full((rows, k // 32), 127, np.uint8))}
+        return {"row_scales": np.full(rows * (k // 16), 0x38, np.uint8), "group_scale": np.ones(groups, np.float32)}
+
+    A = dev_q(N, fmt, False, splits, k, {"row_data": codes(a_int).reshape(-1), **unit(m, e)})
+    B = dev_q(N, fmt, False, [n] * e, k, {"row_data": codes(b_int).reshape(e * n, k).reshape(-1) if fmt == "mxfp8"
+                                          else codes(b_int.reshape(e * n, k)).reshape(-1), **unit(e * n, e)})
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    N.grouped_gemm_mx("fprop", fmt, splits, m, n, k, A, B, c)
+    torch.cuda.synchronize()
+    got = f32(c)
+    off = Q.group_offsets(splits)
+    for g in range(e):
+        want = (a_int[off[g]:off[g + 1]] @ b_int[g].T).astype(np.float64)
+        assert np.array_equal(got[off[g]:off[g + 1]], want), (fmt, k, g)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_fprop_dgrad(N, fmt, out_dtype):
     import torch
